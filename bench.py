@@ -1,0 +1,201 @@
+"""Benchmark of the MI355X MoE layer: one JSON line on stdout.
+
+A step is one moe_layer_forward (route, permute, grouped SwiGLU FFN of the routed and the
+shared experts, combine) over one batch of the workload, with inputs and weights resident
+in HBM. Default workload: the DeepSeek-R1-shaped decode layer (T=128 tokens, H=7168, 256
+routed experts, top-8, sigmoid scores with a selection-only bias, weights renormalised
+and scaled by 2.5, one shared expert, I=2048, bf16).
+
+Besides layer tokens/s the line carries:
+  roofline      the dominant kernel (grouped gate/up + SwiGLU) timed with HIP events
+                recorded by the library around it on the stream it runs on; its
+                algorithmic bytes (touched experts' gate/up weights + activation rows read
+                + h written) per launch over its average duration, against 8 TB/s HBM.
+  cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the same batch
+                (the first few tokens; routing covers all tokens), tokens/s.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE layer tokens/s + grouped-GEMM % of HBM/MFMA peak, 256e top-8 H=7168 bf16"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="r1_decode")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--cpu-tokens", type=int, default=4)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, host, n_tokens):
+    """The oracle, as is, on the first n_tokens tokens of the batch (routing of all T)."""
+    import numpy as np
+
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    tokens = list(range(min(n_tokens, cfg.T)))
+
+    class Cached:
+        """The sample's expert weights generated up front, so the timed region is oracle work."""
+
+        def __init__(self, bank, experts):
+            self.fmt = bank.fmt
+            self._13 = {e: bank.w13(e) for e in experts}
+            self._2 = {e: bank.w2(e) for e in experts}
+
+        def w13(self, e):
+            return self._13[e]
+
+        def w2(self, e):
+            return self._2[e]
+
+    if cfg.routed:
+        r = O.route(O.decode_act(cfg.act, host.x), O.decode_act(cfg.act, host.wr), host.bias, cfg.k,
+                    cfg.score, cfg.scale)
+        used = sorted(set(np.unique(r["topk_idx"][tokens]).tolist()))
+    else:
+        used = sorted(set(np.unique(host.topk_idx[tokens]).tolist()))
+    log(f"cpu baseline: generating {len(used)} experts for {len(tokens)} tokens")
+    host.routed = Cached(host.routed, used)
+    if host.shared is not None:
+        host.shared = Cached(host.shared, [0])
+    t0 = time.perf_counter()
+    res = O.layer_forward(host, tokens=tokens)
+    dt = time.perf_counter() - t0
+    assert res["out"].shape[0] == len(tokens)
+    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(tokens)} of {cfg.T} tokens of the same batch (routing of all {cfg.T} "
+                      f"tokens, {len(used)} routed experts + shared expert FFNs in float64), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU expert parallelism is not built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_04_amd as moe
+    from synth.configs import CONFIGS
+    from synth.problem import device_problem, host_problem
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from moe_cases import make_layer
+
+    cfg = CONFIGS[args.workload]
+    if not cfg.routed:
+        raise SystemExit("bench.py times routed workloads (pre-routed rows: see tests)")
+    log(f"workload {cfg.name}: generating inputs on the device")
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
+    layer = make_layer(cfg, dev)
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    odt = torch.float32 if cfg.out == "f32" else torch.bfloat16
+    out = torch.empty((T, H), dtype=odt, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    ev = moe.StageEvents()
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        layer.forward(dev.x, out, counts=counts)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # timed region: K plain layer steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        layer.forward(dev.x, out, counts=counts)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step")
+
+    # per-stage times of the same launches, from events the library records on its stream
+    stage = {s: [] for s in moe.STAGES}
+    for _ in range(args.steps):
+        moe.moe_layer_forward_timed(layer.desc, dev.x, out, layer.ws, ev, counts=counts)
+        torch.cuda.synchronize()
+        for s_, v in ev.elapsed_ms().items():
+            stage[s_].append(v)
+    stage_ms = {s_: float(np.mean(v)) for s_, v in stage.items()}
+    log("stage ms: " + ", ".join(f"{s_}={v:.4f}" for s_, v in stage_ms.items()))
+
+    cnt = counts.cpu().numpy()
+    touched = int((cnt > 0).sum())
+    rows = T * k + (T if cfg.shared_I else 0)
+    wb = 2 if cfg.wdt == "bf16" else 4
+    gu_bytes = (touched * 2 * cfg.I * H + (2 * cfg.shared_I * H if cfg.shared_I else 0)) * wb
+    gu_bytes += rows * H * wb + rows * cfg.I * wb
+    gu_s = stage_ms["gate_up"] / 1e3
+    achieved = gu_bytes / gu_s / 1e9
+    dn_bytes = (touched * cfg.I * H + (cfg.shared_I * H if cfg.shared_I else 0)) * wb
+    dn_bytes += rows * cfg.I * wb + rows * H * wb
+    layer_flops = (6.0 * H * cfg.I * T * k + (6.0 * H * cfg.shared_I * T if cfg.shared_I else 0)
+                   + 2.0 * T * E * H)
+    layer_bytes = gu_bytes + dn_bytes + E * H * wb + 2 * T * H * wb
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, host, args.cpu_tokens)
+        log(f"cpu baseline: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": T / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.wdt,
+        "data": "synthetic (seeded Philox inputs; N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} top-{k} I={cfg.I} {cfg.score}"
+                               f"{' + selection bias' if cfg.use_bias else ''} scale {cfg.scale}, "
+                               f"{'1 shared expert, ' if cfg.shared_I else ''}{cfg.wdt}",
+                   "tokens": T, "experts_touched": touched,
+                   "stage_ms": {s_: round(v, 5) for s_, v in stage_ms.items()},
+                   "layer_algorithmic_bytes": layer_bytes, "layer_flops": layer_flops,
+                   "layer_hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": "grouped gate/up + SwiGLU (k_gateup_stream)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": gu_bytes,
+                     "avg_launch_ms": stage_ms["gate_up"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

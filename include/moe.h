@@ -1,0 +1,206 @@
+/* moe.h -- C ABI of the sparse MoE feed-forward layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (moe_ffn in "Decoding Trillion-Parameter MoE LLMs: Sparse Architecture and
+ * Agentic Intelligence", section "Routing: Top-K Experts Plus a Shared Expert"):
+ *
+ *   logits = x Wr^T                                   router scores          (moe_route)
+ *   S_t    = top-k experts of score(logits_t) + bias   selection only
+ *   w_t    = scale * score_S / sum(score_S)            renormalised weights
+ *   rows   = tokens regrouped by expert                dispatch               (moe_permute)
+ *   y_r    = SwiGLU_e(x_r)                             grouped expert FFN     (moe_grouped_ffn)
+ *   out_t  = sum_j w_tj y_(t,j) + SwiGLU_shared(x_t)   weighted combine       (moe_combine)
+ *
+ * moe_layer_forward runs all of it. Every step runs in the library's own HIP kernels.
+ *
+ * Conventions (all entry points):
+ *  - Tensor arguments are DEVICE pointers (HBM), row-major, the last dimension
+ *    contiguous. Descriptor structs and scalars are passed from the host. The caller
+ *    allocates and owns every buffer, including the workspace; the library allocates
+ *    nothing and keeps no device state between calls.
+ *  - Calls are asynchronous: they only enqueue kernels on `stream` (a hipStream_t; NULL
+ *    is the default stream) and never synchronise or copy to the host, so they may be
+ *    captured into a HIP graph. Group sizes stay on the device.
+ *  - All arguments are validated on the host before anything is enqueued. On an error
+ *    nothing is launched and outputs are untouched. Launch failures return MOE_ERR_HIP
+ *    (text from moe_last_hip_error). Faults inside kernels surface at the caller's next
+ *    synchronisation. No C++ exception crosses this boundary; the library never prints.
+ *  - Shapes are int32; internal addressing is 64-bit.
+ *  - Tensor pointers must be 16-byte aligned; the workspace 256-byte aligned.
+ *  - Calls on different streams may run concurrently if their buffers do not overlap.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,     /* a size is out of range or not a multiple the format needs */
+  MOE_ERR_DTYPE = 3,     /* unsupported dtype or dtype combination */
+  MOE_ERR_ALIGN = 4,     /* a pointer is not aligned as required */
+  MOE_ERR_WORKSPACE = 5, /* ws_bytes is smaller than the *_workspace_size result */
+  MOE_ERR_HIP = 6        /* a HIP launch failed */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,      /* IEEE binary32 */
+  MOE_BF16 = 1,     /* bfloat16 */
+  MOE_FP8_E4M3 = 2, /* OCP E4M3FN codes, with fp32 block scales */
+  MOE_MXFP4 = 3     /* OCP MX E2M1 pairs per byte (element 2i in the low nibble),
+                       with E8M0 scales per 32 elements along the contiguous dimension */
+} moe_dtype;
+
+typedef enum {
+  MOE_SOFTMAX = 0, /* softmax over all E logits */
+  MOE_SIGMOID = 1  /* logistic sigmoid of each logit */
+} moe_score_fn;
+
+/* One bank of SwiGLU experts (E = 1 for a shared expert).
+ *   w13 [E, 2I, H]: rows [0, I) are the gate projection, rows [I, 2I) the up projection.
+ *   w2  [E, H, I] : the down projection.
+ * FP8_E4M3: codes as above; w13_scale f32 [E, 2I/128, H/128], w2_scale f32 [E, H/128, I/128]
+ *           (one scale per 128 x 128 block; value = code * scale). H, I multiples of 128.
+ * MXFP4:    w13 bytes [E, 2I, H/2], w2 bytes [E, H, I/2]; w13_scale u8 [E, 2I, H/32],
+ *           w2_scale u8 [E, H, I/32] (value = e2m1 * 2^(scale - 127)). H, I multiples of 32.
+ * F32/BF16: no scales (NULL). H, I multiples of 64.
+ * The fp8 and MXFP4 expert formats are the FP8/FP4 grouped GEMM inputs of "GC-MoE:
+ * Overlapping Expert-Parallel Token Dispatch with FP8/FP4 Grouped GEMM via CUDA Green
+ * Contexts" (key_changes, fourth item); block shapes are this library's choice. */
+typedef struct {
+  moe_dtype dtype;
+  const void* w13;
+  const void* w13_scale;
+  const void* w2;
+  const void* w2_scale;
+  int32_t E, H, I;
+} moe_experts;
+
+/* ---------------------------------------------------------------------------- routing */
+
+/* Bytes of workspace moe_route needs for these sizes (pure host function). */
+size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E);
+
+/* Router scores, selection and routing weights for T tokens (moe_ffn's gate and
+ * topk_softmax; bias routing from the roadmap of "Chapter 7: Serving Mega-MoE at Scale").
+ *   x        [T, H] activations, x_dt F32 or BF16.
+ *   w_router [E, H] router weights, same dtype as x.
+ *   bias     [E] f32 selection bias, or NULL for none.
+ *   logits   [T, E] f32 = fp32(sum_h x w_r), accumulated in fp64; optional (NULL).
+ *   score    sigmoid: 1/(1+e^-l); softmax over all E.  Computed in fp64 from the fp32 logit.
+ *   key      fp32(score) + bias[e] (fp32). The k largest keys win; equal keys go to the
+ *            lower expert id; NaN ranks lowest. Exactly k distinct experts per token.
+ *   topk_idx [T, k] int32 chosen expert ids in ascending order.
+ *   topk_w   [T, k] f32 = route_scale * score_e / sum over chosen score (unbiased scores).
+ * Limits: 1 <= k <= min(E, 16), E <= 1024, T >= 0, H >= 1 and H % 8 == 0. */
+moe_status moe_route(const void* x, moe_dtype x_dt, const void* w_router, const float* bias,
+                     int32_t T, int32_t H, int32_t E, int32_t k, moe_score_fn fn,
+                     float route_scale, int32_t* topk_idx, float* topk_w, float* logits,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------- dispatch */
+
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
+
+/* Regroups the T*k (token, slot) assignments into contiguous per-expert rows, ordered by
+ * expert id and, inside an expert, by token index (moe_ffn's dispatch, which is an
+ * all-to-all between GPUs in an expert-parallel deployment and a row gather on one GPU).
+ *   topk_idx [T, k] int32, each row k distinct ids in [0, E).
+ *   counts   [E] int32 rows per expert;  offsets [E+1] int32 exclusive prefix sum.
+ *   perm_src [T*k] int32: row r holds assignment perm_src[r] = t*k + j.
+ *   inv_perm [T*k] int32: assignment t*k + j sits in row inv_perm[t*k + j].
+ *   x        [T, H] (x_dt F32/BF16) or NULL for maps only; x_perm [T*k, H] receives
+ *            x_perm[r] = x[perm_src[r] / k] (NULL iff x is NULL).
+ * Limits: 1 <= k <= min(E,16), E <= 1024, T*k < 2^31. Ids outside [0, E) are undefined
+ * behaviour of the caller (they are not checked on the device). */
+moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, const void* x,
+                       moe_dtype x_dt, int32_t H, int32_t* counts, int32_t* offsets,
+                       int32_t* perm_src, int32_t* inv_perm, void* x_perm, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ grouped expert FFN */
+
+size_t moe_grouped_ffn_workspace_size(const moe_experts* w, moe_dtype act_dt, int32_t rows);
+
+/* SwiGLU FFN of each expert e on its rows [offsets[e], offsets[e+1]) of x_perm, as one
+ * grouped GEMM pair: h = SiLU(x Wg^T) * (x Wu^T), y = h W2^T (moe_ffn's e(x); SwiGLU and
+ * the fused epilogue follow GC-MoE's grouped GEMM with fused SwiGLU).
+ *   w        expert bank (see moe_experts), w->E groups.
+ *   x_perm   [rows, H] act_dt: F32 with F32 weights; BF16 with BF16 / FP8_E4M3 / MXFP4 weights.
+ *            With FP8_E4M3 weights, rows are quantised inside to E4M3 per 1 x 128 block
+ *            (scale = amax/448) and h is re-quantised the same way before the down GEMM.
+ *   offsets  [E+1] int32 device array, offsets[0] = 0, non-decreasing, offsets[E] = rows.
+ *   y_perm   [rows, H] y_dt (F32 or BF16).
+ * Limits: rows >= 0, rows < 2^31 / 8. */
+moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype act_dt,
+                           const int32_t* offsets, int32_t rows, void* y_perm, moe_dtype y_dt,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------ combine */
+
+/* out[t] = sum_j topk_w[t,j] * y_perm[inv_perm[t*k+j]] + shared_out[t]   (moe_ffn's
+ * weighted sum plus the always-active shared expert), summed in fp32 in slot order and
+ * rounded once to out_dt.
+ *   y_perm [T*k, H] y_dt; shared_out [T, H] y_dt or NULL; out [T, H] out_dt (F32 / BF16). */
+moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* inv_perm,
+                       const float* topk_w, int32_t T, int32_t k, int32_t H,
+                       const void* shared_out, void* out, moe_dtype out_dt, void* stream);
+
+/* -------------------------------------------------------------------------- whole layer */
+
+typedef struct {
+  int32_t T, H, E, k;
+  moe_score_fn score_fn;
+  float route_scale;
+  moe_dtype act_dtype; /* x: F32 or BF16 */
+  moe_dtype out_dtype; /* out: F32 or BF16 */
+  const void* w_router; /* [E, H], act_dtype */
+  const float* bias;    /* [E] selection bias, or NULL */
+  moe_experts routed;   /* E experts */
+  moe_experts shared;   /* shared.w13 == NULL: no shared expert; else E = 1, same dtype and H */
+} moe_layer_desc;
+
+/* Bytes of workspace moe_layer_forward needs for this descriptor (pure host function). */
+moe_status moe_layer_workspace_size(const moe_layer_desc* d, size_t* bytes);
+
+/* The whole layer: route, permute, grouped SwiGLU FFN of the routed experts and the
+ * shared expert (as one more group), weighted combine.
+ *   x [T, H] act_dtype; out [T, H] out_dtype.
+ *   Optional outputs (NULL to skip): topk_idx_out [T, k] int32, topk_w_out [T, k] f32,
+ *   counts_out [E] int32, logits_out [T, E] f32. */
+moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, void* out,
+                             int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                             float* logits_out, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward with stage timing: `events` points to MOE_STAGE_EVENTS hipEvent_t
+ * handles created by the caller (hipEventCreate); they are recorded on `stream` at the
+ * stage boundaries  [0] route [1] permute [2] gate/up+SwiGLU [3] down [4] combine [5],
+ * so hipEventElapsedTime(events[i], events[i+1]) is the time of stage i. The kernels and
+ * their launch configurations are exactly those of moe_layer_forward. */
+#define MOE_STAGE_EVENTS 6
+moe_status moe_layer_forward_timed(const moe_layer_desc* d, const void* x, void* out,
+                                   int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                                   float* logits_out, void* ws, size_t ws_bytes, void* stream,
+                                   void* const* events);
+
+/* Pre-routed rows (one GPU's share under expert parallelism, after the dispatch exchange):
+ * each of `rows` received rows carries one local expert id and one weight.
+ *   out[r] = row_w[r] * SwiGLU_{row_expert[r]}(x[r]).
+ * Runs permute (k = 1), the grouped FFN and combine.  x, out [rows, H] BF16 or F32. */
+size_t moe_rows_workspace_size(const moe_experts* w, moe_dtype act_dt, int32_t rows);
+moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_dt,
+                            const int32_t* row_expert, const float* row_w, int32_t rows,
+                            void* out, moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
+
+const char* moe_status_str(moe_status s);
+const char* moe_last_hip_error(void); /* thread-local text of the last MOE_ERR_HIP */
+
+#ifdef __cplusplus
+}
+#endif
+#endif

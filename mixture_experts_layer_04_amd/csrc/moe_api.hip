@@ -1,0 +1,468 @@
+// C ABI of the MoE layer library (include/moe.h): host-side argument validation,
+// workspace sizing and carving, and the launch sequence of each entry point. Nothing here
+// synchronises, copies to the host or allocates; every call only enqueues on `stream`.
+#include <stdio.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_last_hip[256] = "";
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  snprintf(g_last_hip, sizeof g_last_hip, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+  return MOE_ERR_HIP;
+}
+
+inline size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool al256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+size_t dt_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : 2; }
+
+// Sizes and formats a bank must satisfy.
+moe_status check_bank(const moe_experts* w, int32_t H, bool need_scales) {
+  if (!w->w13 || !w->w2) return MOE_ERR_NULL;
+  if (w->E < 1 || w->H != H || w->I < 1) return MOE_ERR_SHAPE;
+  switch (w->dtype) {
+    case MOE_F32:
+    case MOE_BF16:
+      if (H % 64 || w->I % 64) return MOE_ERR_SHAPE;
+      break;
+    case MOE_FP8_E4M3:
+      if (H % 128 || w->I % 128) return MOE_ERR_SHAPE;
+      if (need_scales && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_NULL;
+      break;
+    case MOE_MXFP4:
+      if (H % 64 || w->I % 64) return MOE_ERR_SHAPE;
+      if (need_scales && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_NULL;
+      break;
+    default:
+      return MOE_ERR_DTYPE;
+  }
+  if (!al16(w->w13) || !al16(w->w2)) return MOE_ERR_ALIGN;
+  if ((w->w13_scale && !al16(w->w13_scale)) || (w->w2_scale && !al16(w->w2_scale)))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+// Activation dtype that goes with a weight dtype.
+bool act_ok(moe_dtype act, moe_dtype wdt) {
+  if (wdt == MOE_F32) return act == MOE_F32;
+  if (wdt == MOE_BF16 || wdt == MOE_FP8_E4M3 || wdt == MOE_MXFP4) return act == MOE_BF16;
+  return false;
+}
+bool io_dt_ok(moe_dtype d) { return d == MOE_F32 || d == MOE_BF16; }
+
+// ------------------------------------------------------------------ layer plan
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += up256(bytes);
+    return o;
+  }
+};
+
+struct FfnPlan {
+  int32_t tile_m = 0, max_tiles = 0, rows_total = 0, I_max = 0;
+  size_t o_tiles = 0, o_ntiles = 0, o_scratch = 0, o_y = 0;
+  moe_dtype y_dt = MOE_BF16;
+};
+
+void plan_ffn(Carve& c, FfnPlan& p, moe_dtype wdt, moe_dtype act, int32_t H, int32_t I_max,
+              int32_t rows_routed, int32_t E, int32_t shared_rows, bool need_y) {
+  p.rows_total = rows_routed + shared_rows;
+  p.I_max = I_max;
+  p.tile_m = ffn_tile_m(wdt, rows_routed, E);
+  int64_t mt = max_tiles(rows_routed, E, p.tile_m);
+  if (shared_rows) mt += (shared_rows + p.tile_m - 1) / p.tile_m;
+  p.max_tiles = (int32_t)mt;
+  p.y_dt = act == MOE_F32 ? MOE_F32 : MOE_BF16;
+  p.o_tiles = c.take((size_t)mt * sizeof(Tile));
+  p.o_ntiles = c.take(sizeof(int32_t));
+  p.o_scratch = c.take(ffn_scratch_bytes(wdt, p.rows_total, H, I_max));
+  if (need_y) p.o_y = c.take((size_t)p.rows_total * H * dt_bytes(p.y_dt));
+}
+
+struct LayerPlan {
+  size_t o_route = 0, o_idx = 0, o_w = 0, o_counts = 0, o_offsets = 0, o_perm_src = 0,
+         o_inv_perm = 0, o_row_token = 0, o_perm_ws = 0, o_xq = 0, o_xqs = 0;
+  FfnPlan ffn;
+  size_t total = 0;
+};
+
+LayerPlan plan_layer(const moe_layer_desc* d) {
+  LayerPlan p;
+  Carve c;
+  const int32_t T = d->T, H = d->H, E = d->E, k = d->k;
+  const bool shared = d->shared.w13 != nullptr;
+  const int64_t rows = (int64_t)T * k;
+  p.o_route = c.take(route_ws_bytes(T, H, E));
+  p.o_idx = c.take(rows * sizeof(int32_t));
+  p.o_w = c.take(rows * sizeof(float));
+  p.o_counts = c.take(E * sizeof(int32_t));
+  p.o_offsets = c.take((E + 1) * sizeof(int32_t));
+  p.o_perm_src = c.take(rows * sizeof(int32_t));
+  p.o_inv_perm = c.take(rows * sizeof(int32_t));
+  p.o_row_token = c.take((rows + (shared ? T : 0)) * sizeof(int32_t));
+  p.o_perm_ws = c.take(permute_ws_bytes(T, E));
+  if (d->routed.dtype == MOE_FP8_E4M3) {
+    p.o_xq = c.take((size_t)T * H);
+    p.o_xqs = c.take((size_t)T * (H / 128) * sizeof(float));
+  }
+  int32_t I_max = d->routed.I;
+  if (shared && d->shared.I > I_max) I_max = d->shared.I;
+  plan_ffn(c, p.ffn, d->routed.dtype, d->act_dtype, H, I_max, (int32_t)rows, E, shared ? T : 0,
+           true);
+  p.total = c.off;
+  return p;
+}
+
+moe_status check_layer(const moe_layer_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (!d->w_router) return MOE_ERR_NULL;
+  const bool shared = d->shared.w13 != nullptr;
+  if (d->T < 0 || d->H < 1 || d->E < 1 || d->k < 1 || d->k > d->E || d->k > 16)
+    return MOE_ERR_SHAPE;
+  if (d->E + (shared ? 1 : 0) > 1024) return MOE_ERR_SHAPE;
+  if ((int64_t)d->T * (d->k + 1) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if (d->score_fn != MOE_SOFTMAX && d->score_fn != MOE_SIGMOID) return MOE_ERR_SHAPE;
+  if (!io_dt_ok(d->act_dtype) || !io_dt_ok(d->out_dtype)) return MOE_ERR_DTYPE;
+  if (!act_ok(d->act_dtype, d->routed.dtype)) return MOE_ERR_DTYPE;
+  if (d->routed.E != d->E) return MOE_ERR_SHAPE;
+  moe_status st = check_bank(&d->routed, d->H, true);
+  if (st != MOE_OK) return st;
+  if (shared) {
+    if (d->shared.dtype != d->routed.dtype) return MOE_ERR_DTYPE;
+    if (d->shared.E != 1) return MOE_ERR_SHAPE;
+    st = check_bank(&d->shared, d->H, true);
+    if (st != MOE_OK) return st;
+  }
+  if (!al16(d->w_router) || (d->bias && !al16(d->bias))) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+BankView view(const moe_experts& w) {
+  BankView v;
+  v.w13 = w.w13;
+  v.w13_scale = w.w13_scale;
+  v.w2 = w.w2;
+  v.w2_scale = w.w2_scale;
+  v.I = w.I;
+  return v;
+}
+
+FfnArgs ffn_args(const FfnPlan& p, char* ws, const moe_experts& routed, const moe_experts* shared,
+                 moe_dtype act, int32_t H, const void* a, const int32_t* rowmap, void* y) {
+  FfnArgs f;
+  memset(&f, 0, sizeof f);
+  f.wdt = routed.dtype;
+  f.act_dt = act;
+  f.y_dt = p.y_dt;
+  f.E = routed.E;
+  f.has_shared = shared != nullptr;
+  f.H = H;
+  f.I_max = p.I_max;
+  f.bank[0] = view(routed);
+  if (shared) f.bank[1] = view(*shared);
+  f.a = a;
+  f.a_rowmap = rowmap;
+  f.y = y;
+  f.tiles = reinterpret_cast<const Tile*>(ws + p.o_tiles);
+  f.ntiles = reinterpret_cast<const int32_t*>(ws + p.o_ntiles);
+  f.max_tiles = p.max_tiles;
+  f.tile_m = p.tile_m;
+  f.rows_total = p.rows_total;
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "required pointer is NULL";
+    case MOE_ERR_SHAPE: return "size out of range or not a supported multiple";
+    case MOE_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case MOE_ERR_ALIGN: return "pointer not aligned as required";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_hip_error(void) { return g_last_hip; }
+
+// ------------------------------------------------------------------------- route
+
+size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E) {
+  if (T < 0 || H < 1 || E < 1) return 0;
+  return route_ws_bytes(T, H, E);
+}
+
+moe_status moe_route(const void* x, moe_dtype x_dt, const void* w_router, const float* bias,
+                     int32_t T, int32_t H, int32_t E, int32_t k, moe_score_fn fn,
+                     float route_scale, int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (T < 0 || H < 1 || E < 1 || E > 1024 || k < 1 || k > E || k > 16 || H % 8)
+    return MOE_ERR_SHAPE;
+  if (fn != MOE_SOFTMAX && fn != MOE_SIGMOID) return MOE_ERR_SHAPE;
+  if (!io_dt_ok(x_dt)) return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_w || !ws) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(w_router) || (bias && !al16(bias)) || !al16(topk_idx) || !al16(topk_w) ||
+      (logits && !al16(logits)) || !al256(ws))
+    return MOE_ERR_ALIGN;
+  if (ws_bytes < route_ws_bytes(T, H, E)) return MOE_ERR_WORKSPACE;
+  hipError_t e = launch_route(x, x_dt, w_router, bias, T, H, E, k, fn, route_scale, topk_idx,
+                              topk_w, logits, ws, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
+}
+
+// ----------------------------------------------------------------------- permute
+
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
+  (void)k;
+  if (T < 0 || E < 1) return 0;
+  return permute_ws_bytes(T, E);
+}
+
+moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, const void* x,
+                       moe_dtype x_dt, int32_t H, int32_t* counts, int32_t* offsets,
+                       int32_t* perm_src, int32_t* inv_perm, void* x_perm, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 16) return MOE_ERR_SHAPE;
+  if ((int64_t)T * k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if (!counts || !offsets || !ws) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_idx || !perm_src || !inv_perm)) return MOE_ERR_NULL;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_NULL;
+  if (x) {
+    if (!io_dt_ok(x_dt)) return MOE_ERR_DTYPE;
+    if (H < 1 || (H * (int64_t)dt_bytes(x_dt)) % 16) return MOE_ERR_SHAPE;
+    if (!al16(x) || !al16(x_perm)) return MOE_ERR_ALIGN;
+  }
+  if (!al256(ws)) return MOE_ERR_ALIGN;
+  if (ws_bytes < permute_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_permute_maps(topk_idx, T, k, E, counts, offsets, perm_src, inv_perm,
+                                     nullptr, nullptr, nullptr, 1, 0, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute");
+  if (x) {
+    e = launch_gather_rows(x, (int32_t)dt_bytes(x_dt), H, perm_src, k, T * k, x_perm, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_permute gather");
+  }
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------- grouped FFN
+
+static bool plan_grouped(const moe_experts* w, moe_dtype act_dt, int32_t rows, FfnPlan* p,
+                         size_t* total) {
+  Carve c;
+  plan_ffn(c, *p, w->dtype, act_dt, w->H, w->I, rows, w->E, 0, false);
+  *total = c.off;
+  return true;
+}
+
+size_t moe_grouped_ffn_workspace_size(const moe_experts* w, moe_dtype act_dt, int32_t rows) {
+  if (!w || rows < 0 || w->E < 1 || w->H < 1 || w->I < 1) return 0;
+  FfnPlan p;
+  size_t total;
+  plan_grouped(w, act_dt, rows, &p, &total);
+  return total;
+}
+
+moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype act_dt,
+                           const int32_t* offsets, int32_t rows, void* y_perm, moe_dtype y_dt,
+                           void* ws, size_t ws_bytes, void* stream) {
+  if (!w) return MOE_ERR_NULL;
+  if (rows < 0 || (int64_t)rows * 8 >= ((int64_t)1 << 31) || w->E > 1024) return MOE_ERR_SHAPE;
+  moe_status st = check_bank(w, w->H, true);
+  if (st != MOE_OK) return st;
+  if (!act_ok(act_dt, w->dtype) || !io_dt_ok(y_dt)) return MOE_ERR_DTYPE;
+  if (y_dt != (act_dt == MOE_F32 ? MOE_F32 : MOE_BF16)) return MOE_ERR_DTYPE;
+  if (!offsets || !ws) return MOE_ERR_NULL;
+  if (rows > 0 && (!x_perm || !y_perm)) return MOE_ERR_NULL;
+  if ((x_perm && !al16(x_perm)) || (y_perm && !al16(y_perm)) || !al256(ws)) return MOE_ERR_ALIGN;
+  FfnPlan p;
+  size_t total;
+  plan_grouped(w, act_dt, rows, &p, &total);
+  if (ws_bytes < total) return MOE_ERR_WORKSPACE;
+  if (w->dtype == MOE_FP8_E4M3 || w->dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
+  char* base = reinterpret_cast<char*>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_tiles_from_offsets(offsets, w->E, reinterpret_cast<Tile*>(base + p.o_tiles),
+                                           reinterpret_cast<int32_t*>(base + p.o_ntiles), p.tile_m, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn tiles");
+  FfnArgs f = ffn_args(p, base, *w, nullptr, act_dt, w->H, x_perm, nullptr, y_perm);
+  e = launch_grouped_ffn(f, base + p.o_scratch, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_ffn");
+}
+
+// ----------------------------------------------------------------------- combine
+
+moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* inv_perm,
+                       const float* topk_w, int32_t T, int32_t k, int32_t H,
+                       const void* shared_out, void* out, moe_dtype out_dt, void* stream) {
+  if (T < 0 || k < 1 || H < 8 || H % 8 || (int64_t)T * k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if (!io_dt_ok(y_dt) || !io_dt_ok(out_dt)) return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !inv_perm || !topk_w || !out) return MOE_ERR_NULL;
+  if (!al16(y_perm) || !al16(out) || (shared_out && !al16(shared_out))) return MOE_ERR_ALIGN;
+  hipError_t e = launch_combine(y_perm, y_dt, inv_perm, topk_w, T, k, H, shared_out, out, out_dt,
+                                (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine");
+}
+
+// ------------------------------------------------------------------- whole layer
+
+moe_status moe_layer_workspace_size(const moe_layer_desc* d, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  moe_status st = check_layer(d);
+  if (st != MOE_OK) return st;
+  *bytes = plan_layer(d).total;
+  return MOE_OK;
+}
+
+static moe_status layer_forward(const moe_layer_desc* d, const void* x, void* out,
+                                int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                                float* logits_out, void* ws, size_t ws_bytes, void* stream,
+                                void* const* events) {
+  moe_status st = check_layer(d);
+  if (st != MOE_OK) return st;
+  if (d->routed.dtype == MOE_FP8_E4M3 || d->routed.dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
+  if (!ws || (d->T > 0 && (!x || !out))) return MOE_ERR_NULL;
+  if ((x && !al16(x)) || (out && !al16(out)) || !al256(ws)) return MOE_ERR_ALIGN;
+  if ((topk_idx_out && !al16(topk_idx_out)) || (topk_w_out && !al16(topk_w_out)) ||
+      (counts_out && !al16(counts_out)) || (logits_out && !al16(logits_out)))
+    return MOE_ERR_ALIGN;
+  const LayerPlan p = plan_layer(d);
+  if (ws_bytes < p.total) return MOE_ERR_WORKSPACE;
+  char* base = reinterpret_cast<char*>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t T = d->T, k = d->k, E = d->E, H = d->H;
+  const bool shared = d->shared.w13 != nullptr;
+  int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(base + p.o_idx);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + p.o_w);
+  int32_t* counts = counts_out ? counts_out : reinterpret_cast<int32_t*>(base + p.o_counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + p.o_offsets);
+  int32_t* perm_src = reinterpret_cast<int32_t*>(base + p.o_perm_src);
+  int32_t* inv_perm = reinterpret_cast<int32_t*>(base + p.o_inv_perm);
+  int32_t* row_token = reinterpret_cast<int32_t*>(base + p.o_row_token);
+  hipEvent_t ev[MOE_STAGE_EVENTS] = {};
+  if (events)
+    for (int i = 0; i < MOE_STAGE_EVENTS; ++i) ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
+  hipError_t e = hipSuccess;
+#define MOE_MARK(i)                                                                    \
+  if (events && (e = hipEventRecord(ev[i], s)) != hipSuccess)                         \
+    return hip_fail(e, "moe_layer_forward event");
+  MOE_MARK(0);
+  e = launch_route(x, d->act_dtype, d->w_router, d->bias, T, H, E, k, d->score_fn,
+                              d->route_scale, idx, w, logits_out, base + p.o_route, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward route");
+  MOE_MARK(1);
+  e = launch_permute_maps(idx, T, k, E, counts, offsets, perm_src, inv_perm, row_token,
+                          reinterpret_cast<Tile*>(base + p.ffn.o_tiles),
+                          reinterpret_cast<int32_t*>(base + p.ffn.o_ntiles), p.ffn.tile_m,
+                          shared ? 1 : 0, base + p.o_perm_ws, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward permute");
+  MOE_MARK(2);
+  void* y = base + p.ffn.o_y;
+  FfnArgs f = ffn_args(p.ffn, base, d->routed, shared ? &d->shared : nullptr, d->act_dtype, H, x,
+                       row_token, y);
+  e = launch_grouped_ffn(f, base + p.ffn.o_scratch, s, events ? ev[3] : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward grouped_ffn");
+  MOE_MARK(4);
+  const void* ysh = shared ? reinterpret_cast<const char*>(y) +
+                                 (size_t)T * k * H * dt_bytes(p.ffn.y_dt)
+                           : nullptr;
+  e = launch_combine(y, p.ffn.y_dt, inv_perm, w, T, k, H, ysh, out, d->out_dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward combine");
+  MOE_MARK(5);
+#undef MOE_MARK
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, void* out,
+                             int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                             float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+  return layer_forward(d, x, out, topk_idx_out, topk_w_out, counts_out, logits_out, ws, ws_bytes,
+                       stream, nullptr);
+}
+
+moe_status moe_layer_forward_timed(const moe_layer_desc* d, const void* x, void* out,
+                                   int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                                   float* logits_out, void* ws, size_t ws_bytes, void* stream,
+                                   void* const* events) {
+  if (!events) return MOE_ERR_NULL;
+  for (int i = 0; i < MOE_STAGE_EVENTS; ++i)
+    if (!events[i]) return MOE_ERR_NULL;
+  return layer_forward(d, x, out, topk_idx_out, topk_w_out, counts_out, logits_out, ws, ws_bytes,
+                       stream, events);
+}
+
+// ------------------------------------------------------------- pre-routed rows
+
+static size_t plan_rows(const moe_experts* w, moe_dtype act_dt, int32_t rows, size_t o[6],
+                        FfnPlan* fp) {
+  Carve c;
+  o[0] = c.take(w->E * sizeof(int32_t));             // counts
+  o[1] = c.take((w->E + 1) * sizeof(int32_t));       // offsets
+  o[2] = c.take((size_t)rows * sizeof(int32_t));     // perm_src
+  o[3] = c.take((size_t)rows * sizeof(int32_t));     // inv_perm
+  o[4] = c.take((size_t)rows * sizeof(int32_t));     // row_token
+  o[5] = c.take(permute_ws_bytes(rows, w->E));
+  plan_ffn(c, *fp, w->dtype, act_dt, w->H, w->I, rows, w->E, 0, true);
+  return c.off;
+}
+
+size_t moe_rows_workspace_size(const moe_experts* w, moe_dtype act_dt, int32_t rows) {
+  if (!w || rows < 0 || w->E < 1 || w->H < 1 || w->I < 1) return 0;
+  size_t o[6];
+  FfnPlan fp;
+  return plan_rows(w, act_dt, rows, o, &fp);
+}
+
+moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_dt,
+                            const int32_t* row_expert, const float* row_w, int32_t rows,
+                            void* out, moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
+  if (!w) return MOE_ERR_NULL;
+  if (rows < 0 || (int64_t)rows * 2 >= ((int64_t)1 << 31) || w->E > 1024) return MOE_ERR_SHAPE;
+  moe_status st = check_bank(w, w->H, true);
+  if (st != MOE_OK) return st;
+  if (!act_ok(act_dt, w->dtype) || !io_dt_ok(out_dt)) return MOE_ERR_DTYPE;
+  if (!ws) return MOE_ERR_NULL;
+  if (rows > 0 && (!x || !row_expert || !row_w || !out)) return MOE_ERR_NULL;
+  if ((x && !al16(x)) || (out && !al16(out)) || !al256(ws)) return MOE_ERR_ALIGN;
+  size_t o[6];
+  FfnPlan p;
+  size_t total = plan_rows(w, act_dt, rows, o, &p);
+  if (ws_bytes < total) return MOE_ERR_WORKSPACE;
+  if (w->dtype == MOE_FP8_E4M3 || w->dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
+  char* base = reinterpret_cast<char*>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* inv_perm = reinterpret_cast<int32_t*>(base + o[3]);
+  int32_t* row_token = reinterpret_cast<int32_t*>(base + o[4]);
+  hipError_t e = launch_permute_maps(row_expert, rows, 1, w->E, reinterpret_cast<int32_t*>(base + o[0]),
+                                     reinterpret_cast<int32_t*>(base + o[1]),
+                                     reinterpret_cast<int32_t*>(base + o[2]), inv_perm, row_token,
+                                     reinterpret_cast<Tile*>(base + p.o_tiles),
+                                     reinterpret_cast<int32_t*>(base + p.o_ntiles), p.tile_m, 0,
+                                     base + o[5], s);
+  if (e != hipSuccess) return hip_fail(e, "moe_rows_forward permute");
+  void* y = base + p.o_y;
+  FfnArgs f = ffn_args(p, base, *w, nullptr, act_dt, w->H, x, row_token, y);
+  e = launch_grouped_ffn(f, base + p.o_scratch, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_rows_forward grouped_ffn");
+  e = launch_combine(y, p.y_dt, inv_perm, row_w, rows, 1, w->H, nullptr, out, out_dt, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_rows_forward combine");
+}
+
+}  // extern "C"

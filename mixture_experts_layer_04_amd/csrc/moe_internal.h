@@ -1,0 +1,129 @@
+// Internal declarations of the MoE layer library: device helpers, the tile list
+// shared by the permute and grouped-GEMM kernels, and the launchers each .hip file
+// provides to the C-ABI layer (moe_api.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------ vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern <-> fp32 (bf16 is the upper half of an fp32).
+__device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(two << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(two & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------------------------- tile list
+// A row range of one group (expert): rows [row0, row0 + nrows) of the permuted row
+// space, all belonging to `group`. Groups 0..E-1 are routed experts; group E, when
+// present, is the shared expert. Built on the device by the permute scan kernel.
+struct Tile {
+  int32_t group;
+  int32_t row0;
+  int32_t nrows;
+  int32_t pad;
+};
+
+// Upper bound of the tile count for n_rows rows in n_groups groups with tiles of m rows.
+inline int64_t max_tiles(int64_t n_rows, int64_t n_groups, int64_t m) {
+  return n_rows / m + n_groups;
+}
+
+// ---------------------------------------------------------------------- expert banks
+// Device-side view of one bank of experts (routed: E experts; shared: 1).
+struct BankView {
+  const void* w13;
+  const void* w13_scale;
+  const void* w2;
+  const void* w2_scale;
+  int32_t I;
+};
+
+// Everything the grouped FFN kernels need for one call.
+struct FfnArgs {
+  moe_dtype wdt;          // weight format (both banks)
+  moe_dtype act_dt;       // F32 or BF16 activation rows
+  moe_dtype y_dt;         // F32 or BF16 output rows
+  int32_t E;              // routed groups; group E is the shared bank when has_shared
+  int32_t has_shared;
+  int32_t H;
+  int32_t I_max;          // row stride of h
+  BankView bank[2];
+  // activations: row r of the grouped row space reads a + map(r) * H, where
+  // map(r) = a_rowmap ? a_rowmap[r] : r
+  const void* a;
+  const int32_t* a_rowmap;
+  // fp8 path: activations pre-quantised to E4M3 (a_q, [*, H]) with fp32 scales [*, H/128]
+  const uint8_t* a_q;
+  const float* a_qscale;
+  void* h;                // [rows_total, I_max] intermediate (bf16, f32, or fp8 + scales)
+  float* h_scale;         // fp8 path: [rows_total, I_max/128]
+  void* y;                // [rows_total, H]
+  const Tile* tiles;      // tile list (row chunks of `tile_m` rows)
+  const int32_t* ntiles;  // device count of valid tiles
+  int32_t max_tiles;      // launch bound on tiles
+  int32_t tile_m;
+  int32_t rows_total;
+};
+
+// ------------------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error. All enqueue on `s`.
+
+// route.hip
+size_t route_ws_bytes(int32_t T, int32_t H, int32_t E);
+hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const float* bias,
+                        int32_t T, int32_t H, int32_t E, int32_t k, moe_score_fn fn,
+                        float scale, int32_t* topk_idx, float* topk_w, float* logits,
+                        void* ws, hipStream_t s);
+
+// permute.hip
+size_t permute_ws_bytes(int32_t T, int32_t E);
+// Counts, offsets, perm_src, inv_perm (and row_token[r] = token of row r, if non-NULL).
+// If tiles != NULL also writes the tile list for tile_m-row chunks, including a shared
+// group E of T rows starting at row T*k when with_shared.
+hipError_t launch_permute_maps(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                               int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                               int32_t* inv_perm, int32_t* row_token, Tile* tiles,
+                               int32_t* ntiles, int32_t tile_m, int32_t with_shared, void* ws,
+                               hipStream_t s);
+hipError_t launch_gather_rows(const void* x, int32_t elem_bytes, int32_t H,
+                              const int32_t* perm_src, int32_t k, int32_t rows, void* x_perm,
+                              hipStream_t s);
+// Tile list straight from a device offsets array (grouped FFN called on its own).
+hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* tiles,
+                                     int32_t* ntiles, int32_t tile_m, hipStream_t s);
+
+// grouped_ffn.hip
+int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups);
+size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_max);
+// Runs gate/up + SwiGLU and down for all tiles. `scratch` holds h (and fp8 staging).
+// If mid_event is non-NULL it is recorded between the gate/up and the down launches.
+hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s,
+                              hipEvent_t mid_event = nullptr);
+// fp8 path: per 1 x 128 block E4M3 quantisation of rows of a [n, H] bf16 matrix.
+hipError_t launch_quant_rows_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* qs,
+                                 hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const void* y, moe_dtype y_dt, const int32_t* inv_perm,
+                          const float* topk_w, int32_t T, int32_t k, int32_t H,
+                          const void* shared, void* out, moe_dtype out_dt, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,228 @@
+// Dispatch on one GPU: regroup the T*k (token, slot) assignments into contiguous
+// per-expert rows (moe_ffn's dispatch, "Decoding Trillion-Parameter MoE LLMs", section
+// "Routing: Top-K Experts Plus a Shared Expert"; across GPUs this is the all-to-all of
+// the WideEP claim card's "Context After" paragraph). Rows are ordered by expert id,
+// then by token, so the permutation is unique and the result deterministic.
+//
+// k_hist    one wavefront per block of 64 tokens: each lane ORs its bit into an LDS
+//           64-bit mask per expert (ds_or_b64; order-free, so deterministic). The masks
+//           and their popcounts (per-block counts) go to the workspace.
+// k_scan    one workgroup: per-expert totals, exclusive scan over experts (offsets), then
+//           each block's base row per expert; optionally the tile list for the grouped
+//           GEMM (row chunks of tile_m rows per expert, plus the shared group).
+// k_scatter one wavefront per block: row = base[block][e] + number of earlier tokens of
+//           the block that chose e (popcount of the mask below the lane).
+// k_gather  x_perm[r] = x[perm_src[r] / k], 16 B per lane.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kScanThreads = 1024;
+
+__global__ void __launch_bounds__(64) k_hist(const int32_t* __restrict__ topk_idx, int T, int k,
+                                             int E, uint64_t* __restrict__ masks,
+                                             int32_t* __restrict__ cnt) {
+  __shared__ uint64_t m[1024];
+  const int l = threadIdx.x;
+  const int b = blockIdx.x;
+  for (int e = l; e < E; e += 64) m[e] = 0ull;
+  __syncthreads();
+  const int t = b * 64 + l;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[(int64_t)t * k + j];
+      atomicOr(reinterpret_cast<unsigned long long*>(&m[e]), 1ull << l);
+    }
+  }
+  __syncthreads();
+  for (int e = l; e < E; e += 64) {
+    masks[(int64_t)b * E + e] = m[e];
+    cnt[(int64_t)b * E + e] = __popcll(m[e]);
+  }
+}
+
+// Exclusive scan of v over the workgroup (kScanThreads threads); returns the prefix,
+// total in *total.
+__device__ int block_exclusive_scan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    int add = tid >= o ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  int incl = sh[tid];
+  *total = sh[kScanThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ void __launch_bounds__(kScanThreads) k_scan(int32_t* __restrict__ cnt, int nb, int E,
+                                                       int T, int k, int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets,
+                                                       Tile* __restrict__ tiles,
+                                                       int32_t* __restrict__ ntiles, int tile_m,
+                                                       int with_shared) {
+  __shared__ int sh[kScanThreads];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E)
+    for (int b = 0; b < nb; ++b) tot += cnt[(int64_t)b * E + e];
+  int all;
+  const int off = block_exclusive_scan(e < E ? tot : 0, sh, &all);
+  if (e < E) {
+    counts[e] = tot;
+    offsets[e] = off;
+    int run = off;
+    for (int b = 0; b < nb; ++b) {
+      const int c = cnt[(int64_t)b * E + e];
+      cnt[(int64_t)b * E + e] = run;
+      run += c;
+    }
+  }
+  if (e == 0) offsets[E] = all;
+  if (tiles) {
+    // routed groups: ceil(count / tile_m) tiles each; the shared group E holds T rows
+    // starting at row T*k
+    int nt = 0, rows = 0, row0 = 0;
+    if (e < E) { rows = tot; row0 = off; }
+    else if (e == E && with_shared) { rows = T; row0 = T * k; }
+    nt = (rows + tile_m - 1) / tile_m;
+    int ntot;
+    const int toff = block_exclusive_scan(nt, sh, &ntot);
+    for (int i = 0; i < nt; ++i) {
+      Tile tl;
+      tl.group = e;
+      tl.row0 = row0 + i * tile_m;
+      tl.nrows = min(tile_m, rows - i * tile_m);
+      tl.pad = 0;
+      tiles[toff + i] = tl;
+    }
+    if (e == 0) *ntiles = ntot;
+  }
+}
+
+__global__ void __launch_bounds__(64) k_scatter(const int32_t* __restrict__ topk_idx, int T, int k,
+                                                int E, const uint64_t* __restrict__ masks,
+                                                const int32_t* __restrict__ base,
+                                                int32_t* __restrict__ perm_src,
+                                                int32_t* __restrict__ inv_perm,
+                                                int32_t* __restrict__ row_token) {
+  const int l = threadIdx.x;
+  const int b = blockIdx.x;
+  const int t = b * 64 + l;
+  if (t >= T) return;
+  const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = (int64_t)t * k + j;
+    const int e = topk_idx[a];
+    const uint64_t mk = masks[(int64_t)b * E + e];
+    const int r = base[(int64_t)b * E + e] + __popcll(mk & below);
+    perm_src[r] = (int32_t)a;
+    inv_perm[a] = r;
+    if (row_token) row_token[r] = t;
+  }
+}
+
+// Rows of T*k .. T*k+T-1 (the shared group) read token r - T*k.
+__global__ void k_shared_rows(int32_t* __restrict__ row_token, int T, int k) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < T) row_token[(int64_t)T * k + i] = i;
+}
+
+__global__ void __launch_bounds__(256) k_gather(const uint4* __restrict__ x, int vec_per_row,
+                                                const int32_t* __restrict__ perm_src, int k,
+                                                int rows, uint4* __restrict__ xp) {
+  const int r = blockIdx.x;
+  const int src = perm_src[r] / k;
+  for (int v = blockIdx.y * 256 + threadIdx.x; v < vec_per_row; v += gridDim.y * 256)
+    xp[(int64_t)r * vec_per_row + v] = x[(int64_t)src * vec_per_row + v];
+}
+
+__global__ void __launch_bounds__(kScanThreads) k_tiles_from_offsets(const int32_t* __restrict__ offsets,
+                                                                     int E, Tile* __restrict__ tiles,
+                                                                     int32_t* __restrict__ ntiles,
+                                                                     int tile_m) {
+  __shared__ int sh[kScanThreads];
+  const int e = threadIdx.x;
+  int rows = 0, row0 = 0;
+  if (e < E) {
+    row0 = offsets[e];
+    rows = offsets[e + 1] - row0;
+  }
+  const int nt = (rows + tile_m - 1) / tile_m;
+  int ntot;
+  const int toff = block_exclusive_scan(nt, sh, &ntot);
+  for (int i = 0; i < nt; ++i) {
+    Tile tl;
+    tl.group = e;
+    tl.row0 = row0 + i * tile_m;
+    tl.nrows = min(tile_m, rows - i * tile_m);
+    tl.pad = 0;
+    tiles[toff + i] = tl;
+  }
+  if (e == 0) *ntiles = ntot;
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int32_t T, int32_t E) {
+  const size_t nb = (size_t)(T + 63) / 64;
+  size_t masks = nb * E * sizeof(uint64_t);
+  size_t cnt = nb * E * sizeof(int32_t);
+  return (masks + 255) / 256 * 256 + (cnt + 255) / 256 * 256;
+}
+
+hipError_t launch_permute_maps(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                               int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                               int32_t* inv_perm, int32_t* row_token, Tile* tiles,
+                               int32_t* ntiles, int32_t tile_m, int32_t with_shared, void* ws,
+                               hipStream_t s) {
+  const int nb = (T + 63) / 64;
+  uint64_t* masks = reinterpret_cast<uint64_t*>(ws);
+  size_t mbytes = ((size_t)nb * E * sizeof(uint64_t) + 255) / 256 * 256;
+  int32_t* cnt = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + mbytes);
+  if (nb > 0) {
+    hipLaunchKernelGGL(k_hist, dim3(nb), dim3(64), 0, s, topk_idx, T, k, E, masks, cnt);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, cnt, nb, E, T, k, counts, offsets,
+                     tiles, ntiles, tile_m, with_shared);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (nb > 0) {
+    hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(64), 0, s, topk_idx, T, k, E, masks, cnt, perm_src,
+                       inv_perm, row_token);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (row_token && with_shared && T > 0) {
+    hipLaunchKernelGGL(k_shared_rows, dim3((T + 255) / 256), dim3(256), 0, s, row_token, T, k);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+hipError_t launch_gather_rows(const void* x, int32_t elem_bytes, int32_t H,
+                              const int32_t* perm_src, int32_t k, int32_t rows, void* x_perm,
+                              hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int vec = (int)((int64_t)H * elem_bytes / 16);
+  const int gx = (vec + 255) / 256;
+  hipLaunchKernelGGL(k_gather, dim3(rows, gx), dim3(256), 0, s, reinterpret_cast<const uint4*>(x),
+                     vec, perm_src, k, rows, reinterpret_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* tiles,
+                                     int32_t* ntiles, int32_t tile_m, hipStream_t s) {
+  hipLaunchKernelGGL(k_tiles_from_offsets, dim3(1), dim3(kScanThreads), 0, s, offsets, E, tiles,
+                     ntiles, tile_m);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -321,3 +321,13 @@ def rel_err(got: np.ndarray, want64: np.ndarray, rms: float | None = None) -> fl
     if rms is None:
         rms = float(np.sqrt(np.mean(want64 ** 2)))
     return float(np.max(np.abs(np.asarray(got, np.float64) - want64)) / rms)
+
+
+def combine(y64: np.ndarray, inv_perm: np.ndarray, topk_w64: np.ndarray, shared64=None):
+    """moe_ffn's accumulation: out[t] = sum_j w[t,j] * y[inv_perm[t*k+j]] (+ shared[t])."""
+    T, k = topk_w64.shape
+    rows = y64[np.asarray(inv_perm, np.int64).reshape(T, k)]          # [T, k, H]
+    out = np.einsum("tk,tkh->th", topk_w64, rows)
+    if shared64 is not None:
+        out = out + shared64
+    return out
