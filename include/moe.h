@@ -135,7 +135,8 @@ size_t moe_grouped_ffn_workspace_size(const moe_experts* w, moe_dtype act_dt, in
  *            With FP8_E4M3 weights, rows are quantised inside to E4M3 per 1 x 128 block
  *            (scale = amax/448) and h is re-quantised the same way before the down GEMM.
  *   offsets  [E+1] int32 device array, offsets[0] = 0, non-decreasing, offsets[E] = rows.
- *   y_perm   [rows, H] y_dt (F32 or BF16).
+ *   y_perm   [rows, H] y_dt (F32 or BF16; F32 keeps the expert outputs unrounded until the
+ *            combine, as moe_layer_forward does).
  * Limits: rows >= 0, rows < 2^31 / 8. */
 moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype act_dt,
                            const int32_t* offsets, int32_t rows, void* y_perm, moe_dtype y_dt,

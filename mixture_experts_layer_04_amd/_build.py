@@ -15,17 +15,17 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=None) -> str:
-    cmd = ["hipcc", *FLAGS, *(extra or []), *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB]
+def build(verbose: bool = False, extra=None, out: str = LIB) -> str:
+    cmd = ["hipcc", *FLAGS, *(extra or []), *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("libmoe build failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
     if verbose:
         print(" ".join(cmd))
-        out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
-        if out.strip():
-            print(out)
-    return LIB
+        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+        if msg.strip():
+            print(msg)
+    return out
 
 
 if __name__ == "__main__":

@@ -83,6 +83,37 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
   }
 }
 
+// Tuning constants of the streaming kernels (K steps per loop iteration, weight load
+// cache policy). Weights are read with ordinary cached loads: on MI355X they measured
+// faster than non-temporal ones for this many-rows-at-once access pattern.
+#ifndef MOE_STREAM_UNROLL_GU
+#define MOE_STREAM_UNROLL_GU 4
+#endif
+#ifndef MOE_STREAM_UNROLL_DN
+#define MOE_STREAM_UNROLL_DN 8
+#endif
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 0
+#endif
+
+__device__ __forceinline__ Frag32 load_w(const void* p) {
+  return MOE_STREAM_NT ? load_nt(p) : load_c(p);
+}
+// Activation fragment of a row; lanes of padding rows (beyond the tile's rows) load
+// nothing and contribute zeros to columns that are never stored.
+__device__ __forceinline__ Frag32 load_x(const void* p, bool valid) {
+  if (valid) return load_c(p);
+  Frag32 z;
+  z.lo = u32x4{0, 0, 0, 0};
+  z.hi = u32x4{0, 0, 0, 0};
+  return z;
+}
+
+template <bool kF32>
+__device__ __forceinline__ f32x4 mma(const Frag32& w, const Frag32& x, f32x4 acc) {
+  return kF32 ? mma_f32(w, x, acc) : mma_bf16(w, x, acc);
+}
+
 // Gate/up + SwiGLU. Workgroup = (tile, block of 64 h features); wavefront w computes
 // features [f0, f0+16) of h: gate rows f0.. and up rows I+f0.. of W13[e].
 template <bool kF32>
@@ -101,30 +132,40 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
   const int m = l & 15, kq = l >> 4;
   const int esz = kF32 ? 4 : 2;
   const char* w13 = reinterpret_cast<const char*>(a.bank[bank].w13) + ge * 2 * I * (int64_t)H * esz;
-  const char* wg = w13 + (int64_t)(f0 + m) * H * esz;
-  const char* wu = w13 + (int64_t)(I + f0 + m) * H * esz;
-  const int row = tl.row0 + (m < tl.nrows ? m : tl.nrows - 1);
+  const bool xv = m < tl.nrows;
+  const int row = tl.row0 + (xv ? m : 0);
   const int64_t src = a.a_rowmap ? a.a_rowmap[row] : row;
-  const char* xr = reinterpret_cast<const char*>(a.a) + src * H * esz;
-  constexpr int kStep = kF32 ? 32 : 64;          // K elements per step
+  constexpr int kStep = kF32 ? 32 : 64;          // K elements per MFMA step
   constexpr int kLane = kStep / 4;               // contiguous elements per lane per step
-  f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+  constexpr int U = MOE_STREAM_UNROLL_GU;
   const int64_t lane_off = (int64_t)kq * kLane * esz;
-#pragma unroll 4
-  for (int k0 = 0; k0 < H; k0 += kStep) {
-    const int64_t o = (int64_t)k0 * esz + lane_off;
-    Frag32 fg = load_nt(wg + o);
-    Frag32 fu = load_nt(wu + o);
-    Frag32 fx = load_c(xr + o);
-    if (kF32) {
-      accg = mma_f32(fg, fx, accg);
-      accu = mma_f32(fu, fx, accu);
-    } else {
-      accg = mma_bf16(fg, fx, accg);
-      accu = mma_bf16(fu, fx, accu);
+  const char* wg = w13 + (int64_t)(f0 + m) * H * esz + lane_off;
+  const char* wu = w13 + (int64_t)(I + f0 + m) * H * esz + lane_off;
+  const char* xr = reinterpret_cast<const char*>(a.a) + src * H * esz + lane_off;
+  f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+  const int kmain = H - H % (kStep * U);
+  for (int k0 = 0; k0 < kmain; k0 += kStep * U) {
+    Frag32 fg[U], fu[U], fx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t o = (int64_t)(k0 + u * kStep) * esz;
+      fg[u] = load_w(wg + o);
+      fu[u] = load_w(wu + o);
+      fx[u] = load_x(xr + o, xv);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      accg = mma<kF32>(fg[u], fx[u], accg);
+      accu = mma<kF32>(fu[u], fx[u], accu);
     }
   }
-  if (m < tl.nrows) {
+  for (int k0 = kmain; k0 < H; k0 += kStep) {
+    const int64_t o = (int64_t)k0 * esz;
+    Frag32 fg = load_w(wg + o), fu = load_w(wu + o), fx = load_x(xr + o, xv);
+    accg = mma<kF32>(fg, fx, accg);
+    accu = mma<kF32>(fu, fx, accu);
+  }
+  if (xv) {
     f32x4 hv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) hv[i] = silu_mul(accg[i], accu[i]);
@@ -148,30 +189,186 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
   if (f0 >= H) return;
   const int m = l & 15, kq = l >> 4;
   const int esz = kF32 ? 4 : 2;
-  const char* w2 = reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * esz;
-  const char* wr = w2 + (int64_t)(f0 + m) * I * esz;
-  const int row = tl.row0 + (m < tl.nrows ? m : tl.nrows - 1);
-  const char* hr = reinterpret_cast<const char*>(a.h) + (int64_t)row * a.I_max * esz;
   constexpr int kStep = kF32 ? 32 : 64;
   constexpr int kLane = kStep / 4;
-  f32x4 acc = {0, 0, 0, 0};
+  constexpr int U = MOE_STREAM_UNROLL_DN;
   const int64_t lane_off = (int64_t)kq * kLane * esz;
-#pragma unroll 4
-  for (int k0 = 0; k0 < I; k0 += kStep) {
-    const int64_t o = (int64_t)k0 * esz + lane_off;
-    Frag32 fw = load_nt(wr + o);
-    Frag32 fh = load_c(hr + o);
-    acc = kF32 ? mma_f32(fw, fh, acc) : mma_bf16(fw, fh, acc);
+  const bool xv = m < tl.nrows;
+  const char* w2 = reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * esz;
+  const char* wr = w2 + (int64_t)(f0 + m) * I * esz + lane_off;
+  const char* hr = reinterpret_cast<const char*>(a.h) +
+                   (int64_t)(tl.row0 + (xv ? m : 0)) * a.I_max * esz + lane_off;
+  f32x4 acc = {0, 0, 0, 0};
+  const int kmain = I - I % (kStep * U);
+  for (int k0 = 0; k0 < kmain; k0 += kStep * U) {
+    Frag32 fw[U], fh[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t o = (int64_t)(k0 + u * kStep) * esz;
+      fw[u] = load_w(wr + o);
+      fh[u] = load_x(hr + o, xv);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = mma<kF32>(fw[u], fh[u], acc);
   }
-  if (m < tl.nrows) store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + kq * 4, acc);
+  for (int k0 = kmain; k0 < I; k0 += kStep) {
+    const int64_t o = (int64_t)k0 * esz;
+    acc = mma<kF32>(load_w(wr + o), load_x(hr + o, xv), acc);
+  }
+  if (xv) store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + kq * 4, acc);
+}
+
+// ---------------------------------------------------------------------------------
+// Tiled kernels (many rows per expert, e.g. prefill): classic LDS-staged GEMM tiles of
+// 128 rows x 128 weight rows x 64 K per workgroup, 4 wavefronts of 64 x 64 each built
+// from v_mfma_f32_16x16x32_bf16. Global -> register prefetch of the next K block overlaps
+// the MFMAs on the current one (double-buffered LDS, one barrier per K block). LDS rows are
+// padded by 16 B so the 16-B fragment reads of 16 consecutive rows hit distinct banks.
+// For gate/up, the 128 weight rows of a tile are 64 gate and the matching 64 up rows,
+// interleaved in groups of 16 so that every lane holds gate and up of the same
+// (row, feature) and SwiGLU is applied in registers.
+constexpr int kTBM = 128, kTBN = 128, kTBK = 64;
+constexpr int kLdsRow = kTBK * 2 + 16;                    // bytes per LDS row
+constexpr int kLdsStage = (kTBM + kTBN) * kLdsRow;        // bytes per stage
+
+// Workgroup id remap so that consecutive logical ids run on the same XCD (ids are dealt
+// to the 8 XCDs round-robin), letting neighbours share their A tile in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+  if (grid % 8) return bid;
+  return (bid % 8) * (grid / 8) + bid / 8;
+}
+
+template <bool kGateUp, bool kYF32>
+__global__ void __launch_bounds__(256, 2) k_tiled_bf16(FfnArgs a, int nb_per_tile) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kLdsStage];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile_id = bid / nb_per_tile;
+  const int nb = bid - tile_id * nb_per_tile;
+  if (tile_id >= *a.ntiles) return;
+  const Tile tl = a.tiles[tile_id];
+  const int bank = tl.group < a.E ? 0 : 1;
+  const int64_t ge = tl.group < a.E ? tl.group : 0;
+  const int I = a.bank[bank].I;
+  const int H = a.H;
+  const int K = kGateUp ? H : I;
+  const int fpb = kGateUp ? kTBN / 2 : kTBN;              // output features per tile
+  const int f0 = nb * fpb;
+  if (f0 >= (kGateUp ? I : H)) return;
+  const char* wbase = kGateUp
+      ? reinterpret_cast<const char*>(a.bank[bank].w13) + ge * 2 * (int64_t)I * H * 2
+      : reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * 2;
+  // global -> LDS assignment: 16-B chunk c = tid + 256 i of a 128 x 128 B block
+  const char* ag[4];
+  const char* bg[4];
+  int lds_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3, col = (c & 7) * 16;
+    lds_off[i] = r * kLdsRow + col;
+    const int grow = tl.row0 + (r < tl.nrows ? r : tl.nrows - 1);
+    if (kGateUp) {
+      const int64_t src = a.a_rowmap ? a.a_rowmap[grow] : grow;
+      ag[i] = reinterpret_cast<const char*>(a.a) + src * (int64_t)H * 2 + col;
+      const int half = r >> 6, jj = r & 63, grp = jj >> 4, within = jj & 15;
+      const int feat = f0 + half * 32 + (grp >> 1) * 16 + within;
+      const int wrow = (grp & 1) ? I + feat : feat;
+      bg[i] = wbase + (int64_t)wrow * K * 2 + col;
+    } else {
+      ag[i] = reinterpret_cast<const char*>(a.h) + (int64_t)grow * a.I_max * 2 + col;
+      bg[i] = wbase + (int64_t)(f0 + r) * K * 2 + col;
+    }
+  }
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m16 = l & 15, g = l >> 4;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  u32x4 ra[4], rb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = *reinterpret_cast<const u32x4*>(ag[i]);
+    rb[i] = *reinterpret_cast<const u32x4*>(bg[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    *reinterpret_cast<u32x4*>(smem + lds_off[i]) = ra[i];
+    *reinterpret_cast<u32x4*>(smem + kTBM * kLdsRow + lds_off[i]) = rb[i];
+  }
+  __syncthreads();
+  const int KT = K / kTBK;
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* cur = smem + (kt & 1) * kLdsStage;
+    if (kt + 1 < KT) {
+      const int64_t o = (int64_t)(kt + 1) * kTBK * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ra[i] = *reinterpret_cast<const u32x4*>(ag[i] + o);
+        rb[i] = *reinterpret_cast<const u32x4*>(bg[i] + o);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[4], fb[4];
+      const int kb = g * 32 + ks * 16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fa[t] = *reinterpret_cast<const bf16x8*>(cur + (wm * 64 + t * 16 + m16) * kLdsRow + kb);
+        fb[t] = *reinterpret_cast<const bf16x8*>(cur + kTBM * kLdsRow +
+                                                 (wn * 64 + t * 16 + m16) * kLdsRow + kb);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) {
+      char* nxt = smem + ((kt + 1) & 1) * kLdsStage;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<u32x4*>(nxt + lds_off[i]) = ra[i];
+        *reinterpret_cast<u32x4*>(nxt + kTBM * kLdsRow + lds_off[i]) = rb[i];
+      }
+    }
+    __syncthreads();
+  }
+  // epilogue: lane holds D[row 4g+i][column m16] of each 16 x 16 sub-tile
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = wm * 64 + mt * 16 + 4 * g + i;
+      if (rl >= tl.nrows) continue;
+      const int64_t row = tl.row0 + rl;
+      if (kGateUp) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int feat = f0 + wn * 32 + p * 16 + m16;
+          const float hv = silu_mul(acc[mt][2 * p][i], acc[mt][2 * p + 1][i]);
+          reinterpret_cast<uint16_t*>(a.h)[row * a.I_max + feat] = f32_to_bf16(hv);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int64_t o = row * H + f0 + wn * 64 + nt * 16 + m16;
+          if (kYF32) reinterpret_cast<float*>(a.y)[o] = acc[mt][nt][i];
+          else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16(acc[mt][nt][i]);
+        }
+      }
+    }
+  }
 }
 
 }  // namespace
 
-int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups) {
-  (void)wdt;
-  (void)rows;
-  (void)groups;
+int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H) {
+  // Few rows per expert: stream the weights (each weight element read once per tile of
+  // <= 16 rows). Many rows: LDS-tiled GEMM with 128-row tiles.
+  if (wdt == MOE_BF16 && H % kTBN == 0 && (int64_t)rows > 32 * (int64_t)groups) return kTBM;
   return kStreamTileM;
 }
 
@@ -191,6 +388,18 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
   const bool f32 = a.wdt == MOE_F32;
   const bool yf32 = a.y_dt == MOE_F32;
   dim3 blk(256);
+  if (a.tile_m == kTBM) {
+    const int nb_gu = a.I_max / (kTBN / 2), nb_dn = a.H / kTBN;
+    hipLaunchKernelGGL((k_tiled_bf16<true, false>), dim3(a.max_tiles * nb_gu), blk, 0, s, a, nb_gu);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
+    if (yf32)
+      hipLaunchKernelGGL((k_tiled_bf16<false, true>), dim3(a.max_tiles * nb_dn), blk, 0, s, a, nb_dn);
+    else
+      hipLaunchKernelGGL((k_tiled_bf16<false, false>), dim3(a.max_tiles * nb_dn), blk, 0, s, a, nb_dn);
+    return hipGetLastError();
+  }
   if (f32)
     hipLaunchKernelGGL(k_gateup_stream<true>, dim3(a.max_tiles * fb_gu), blk, 0, s, a, fb_gu);
   else

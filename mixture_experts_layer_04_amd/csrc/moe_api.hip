@@ -78,11 +78,14 @@ void plan_ffn(Carve& c, FfnPlan& p, moe_dtype wdt, moe_dtype act, int32_t H, int
               int32_t rows_routed, int32_t E, int32_t shared_rows, bool need_y) {
   p.rows_total = rows_routed + shared_rows;
   p.I_max = I_max;
-  p.tile_m = ffn_tile_m(wdt, rows_routed, E);
+  p.tile_m = ffn_tile_m(wdt, rows_routed, E, H);
   int64_t mt = max_tiles(rows_routed, E, p.tile_m);
   if (shared_rows) mt += (shared_rows + p.tile_m - 1) / p.tile_m;
   p.max_tiles = (int32_t)mt;
-  p.y_dt = act == MOE_F32 ? MOE_F32 : MOE_BF16;
+  // Expert outputs stay fp32 until the combine rounds once: with bf16 rows here the
+  // heavy-tailed SwiGLU outputs of small layers measured up to 2.5e-2 of the output RMS.
+  (void)act;
+  p.y_dt = MOE_F32;
   p.o_tiles = c.take((size_t)mt * sizeof(Tile));
   p.o_ntiles = c.take(sizeof(int32_t));
   p.o_scratch = c.take(ffn_scratch_bytes(wdt, p.rows_total, H, I_max));
@@ -287,7 +290,6 @@ moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype a
   moe_status st = check_bank(w, w->H, true);
   if (st != MOE_OK) return st;
   if (!act_ok(act_dt, w->dtype) || !io_dt_ok(y_dt)) return MOE_ERR_DTYPE;
-  if (y_dt != (act_dt == MOE_F32 ? MOE_F32 : MOE_BF16)) return MOE_ERR_DTYPE;
   if (!offsets || !ws) return MOE_ERR_NULL;
   if (rows > 0 && (!x_perm || !y_perm)) return MOE_ERR_NULL;
   if ((x_perm && !al16(x_perm)) || (y_perm && !al16(y_perm)) || !al256(ws)) return MOE_ERR_ALIGN;
@@ -302,6 +304,7 @@ moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype a
                                            reinterpret_cast<int32_t*>(base + p.o_ntiles), p.tile_m, s);
   if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn tiles");
   FfnArgs f = ffn_args(p, base, *w, nullptr, act_dt, w->H, x_perm, nullptr, y_perm);
+  f.y_dt = y_dt;
   e = launch_grouped_ffn(f, base + p.o_scratch, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_ffn");
 }

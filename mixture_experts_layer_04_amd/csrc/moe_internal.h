@@ -111,7 +111,7 @@ hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* ti
                                      int32_t* ntiles, int32_t tile_m, hipStream_t s);
 
 // grouped_ffn.hip
-int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups);
+int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H);
 size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_max);
 // Runs gate/up + SwiGLU and down for all tiles. `scratch` holds h (and fp8 staging).
 // If mid_event is non-NULL it is recorded between the gate/up and the down launches.

@@ -33,6 +33,11 @@ SMALL = [
               weight_seed=15),
     MoEConfig("bf16_f32_out_k16", T=70, H=256, E=40, k=16, I=128, score="sigmoid", use_bias=True,
               scale=2.5, out="f32", seed=16, weight_seed=16),
+    # more than 32 rows per expert: the LDS-tiled grouped GEMM, with ragged 128-row tiles
+    MoEConfig("bf16_tiled_sigmoid_shared", T=600, H=256, E=12, k=3, I=192, score="sigmoid",
+              use_bias=True, scale=2.5, shared_I=128, seed=17, weight_seed=17),
+    MoEConfig("bf16_tiled_softmax_f32out", T=1000, H=384, E=6, k=2, I=128, score="softmax",
+              out="f32", seed=18, weight_seed=18),
 ]
 
 
@@ -154,4 +159,21 @@ def test_r1_decode_full_size():
     print("r1_decode sampled rel err", err, flush=True)
     assert err <= TOL["bf16"]
     # every token's output row is finite and of the oracle's scale
+    assert np.isfinite(got["out"]).all()
+
+
+def test_r1_prefill_full_size():
+    """DeepSeek-R1-shaped prefill layer with Zipf-skewed routing at its real size: routing of
+    all 8192 tokens bit-exact, outputs of sampled tokens against the oracle."""
+    cfg = CONFIGS["r1_prefill"]
+    print("case", describe(cfg), flush=True)
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
+    got = run_layer(cfg, dev)
+    tokens = [5, 4321, 8191]
+    want = O.layer_forward(host, tokens=tokens)
+    check_routing(got, want, cfg)
+    err = O.rel_err(got["out"][tokens], want["out"])
+    print("r1_prefill sampled rel err", err, flush=True)
+    assert err <= TOL["bf16"]
     assert np.isfinite(got["out"]).all()
