@@ -198,6 +198,14 @@ moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_d
                             const int32_t* row_expert, const float* row_w, int32_t rows,
                             void* out, moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
 
+/* Per 1 x 128 block fp8 quantisation of activation rows, as the fp8 expert path applies it
+ * to its inputs (the FP8 grouped GEMM inputs of GC-MoE, key_changes, fourth item):
+ * scale = fp32(amax / 448) per block of 128 consecutive elements of a row (1 for an
+ * all-zero block); code = E4M3FN(fp32(x / scale)), round to nearest even, saturating.
+ *   x [n, H] BF16; q [n, H] u8 codes; q_scale [n, H/128] f32. H a multiple of 128. */
+moe_status moe_quantize_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* q_scale,
+                            void* stream);
+
 const char* moe_status_str(moe_status s);
 const char* moe_last_hip_error(void); /* thread-local text of the last MOE_ERR_HIP */
 

@@ -54,7 +54,7 @@ EXPORTS = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size"
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
            "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_rows_workspace_size",
-           "moe_rows_forward", "moe_status_str", "moe_last_hip_error"]
+           "moe_rows_forward", "moe_quantize_fp8", "moe_status_str", "moe_last_hip_error"]
 
 
 def lib():
@@ -87,6 +87,8 @@ def lib():
     for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
               "moe_layer_forward", "moe_layer_forward_timed", "moe_rows_forward"):
         getattr(L, f).restype = ci
+    L.moe_quantize_fp8.argtypes = [vp, i32, i32, vp, vp, vp]
+    L.moe_quantize_fp8.restype = ci
     L.moe_status_str.argtypes = [ci]
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_last_hip_error.argtypes = []
@@ -259,6 +261,12 @@ def moe_layer_forward_timed(desc: moe_layer_desc, x, out, ws, events: StageEvent
                                        _ptr(topk_w), _ptr(counts), _ptr(logits), _ptr(ws), ws.numel(),
                                        _stream(stream), events.ev)
     _check(st, "moe_layer_forward_timed")
+
+
+def moe_quantize_fp8(x, q, q_scale, stream=None):
+    n, H = x.shape
+    st = lib().moe_quantize_fp8(_ptr(x), n, H, _ptr(q), _ptr(q_scale), _stream(stream))
+    _check(st, "moe_quantize_fp8")
 
 
 def moe_rows_workspace_size(experts: Experts, act_dtype, rows: int) -> int:

@@ -363,9 +363,258 @@ __global__ void __launch_bounds__(256, 2) k_tiled_bf16(FfnArgs a, int nb_per_til
   }
 }
 
+// ---------------------------------------------------------------------------------
+// fp8 path (E4M3 weights with fp32 128 x 128 block scales, activations E4M3 with fp32
+// 1 x 128 scales), the FP8 grouped GEMM with fused SwiGLU and re-quantisation of GC-MoE
+// (key_changes, fourth item) re-planned for gfx950:
+//  - v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales computes one 128-wide K block
+//    of a 16 x 16 tile exactly; the fp32 block scales (not powers of two, so not foldable
+//    into the MFMA's own scale operands) are applied per K block on the VALU:
+//    acc += partial * (s_w * s_x[token]).
+//  - weights are the MFMA A operand, read straight from HBM into registers (32 B/lane,
+//    one 128-B K block of 16 rows per wavefront and matrix, prefetched one block ahead);
+//    the tile's <= 128 activation rows and their scales are staged in LDS once per K
+//    block and shared by the 8 wavefronts of the workgroup (128 output features).
+//  - gate/up epilogue: h = SiLU(g) * u in fp32, per-token amax over the workgroup's 128
+//    features (wavefront shuffles, then LDS across wavefronts), scale = amax / 448,
+//    E4M3 codes of h / scale -- exactly one 1 x 128 quantisation block per workgroup.
+constexpr int kF8TileM = 128;
+constexpr int kF8Feat = 128;
+constexpr int kF8K = 128;
+constexpr int kF8LdsRow = kF8K + 16;
+
+// fp32 -> E4M3FN code, round to nearest even, saturating at +-448 (NaN -> 0x7F).
+// Written from the format: magnitudes below 2^-6 lie on the subnormal grid m * 2^-9;
+// above, a value 2^e * (1 + f) keeps 3 fraction bits.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (!(a == a)) return 0x7Fu;
+  if (a >= 464.0f) return sign | 0x7Eu;
+  const int ex = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;
+  if (ex < -6) return sign | (uint32_t)__builtin_rintf(a * 512.0f);      // 0..8
+  float m = __builtin_rintf(__uint_as_float((uint32_t)(127 + 3 - ex) << 23) * a);  // 8..16
+  int e = ex;
+  if (m == 16.0f) { m = 8.0f; ++e; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | ((uint32_t)m - 8u);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+__device__ __forceinline__ float wave_max16(float v) {  // max over lanes with equal l % 16
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// Quantise rows of a bf16 [n, H] matrix: one workgroup per row, 16 lanes per 1 x 128 block.
+__global__ void __launch_bounds__(256) k_quant_rows_fp8(const uint16_t* __restrict__ x, int H,
+                                                        uint8_t* __restrict__ q,
+                                                        float* __restrict__ qs) {
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int nblk = H / 128;
+  for (int b0 = 0; b0 < nblk; b0 += 16) {
+    const int b = b0 + (t >> 4);
+    const int j = t & 15;
+    float v[8];
+    float am = 0.0f;
+    if (b < nblk) {
+      uint4 w = *reinterpret_cast<const uint4*>(x + row * H + b * 128 + j * 8);
+      v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+      v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 16));
+    if (b < nblk) {
+      const float sc = am == 0.0f ? 1.0f : __fdiv_rn(am, 448.0f);
+      uint2 c;
+      c.x = e4m3_code(__fdiv_rn(v[0], sc)) | (e4m3_code(__fdiv_rn(v[1], sc)) << 8) |
+            (e4m3_code(__fdiv_rn(v[2], sc)) << 16) | (e4m3_code(__fdiv_rn(v[3], sc)) << 24);
+      c.y = e4m3_code(__fdiv_rn(v[4], sc)) | (e4m3_code(__fdiv_rn(v[5], sc)) << 8) |
+            (e4m3_code(__fdiv_rn(v[6], sc)) << 16) | (e4m3_code(__fdiv_rn(v[7], sc)) << 24);
+      *reinterpret_cast<uint2*>(q + row * H + b * 128 + j * 8) = c;
+      if (j == 0) qs[row * nblk + b] = sc;
+    }
+  }
+}
+
+__device__ __forceinline__ i32x8 ld32(const void* p) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  u32x4 a = q[0], b = q[1];
+  i32x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+template <bool kGateUp>
+__global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
+  __shared__ __attribute__((aligned(16))) uint8_t act[2][kF8TileM * kF8LdsRow];
+  __shared__ float ascale[2][kF8TileM];
+  __shared__ float red[8][kF8TileM];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int m16 = l & 15, g = l >> 4;
+  const int tile_id = blockIdx.x / fb_per_tile;
+  const int fb = blockIdx.x - tile_id * fb_per_tile;
+  if (tile_id >= *a.ntiles) return;
+  const Tile tl = a.tiles[tile_id];
+  const int bank = tl.group < a.E ? 0 : 1;
+  const int64_t ge = tl.group < a.E ? tl.group : 0;
+  const int I = a.bank[bank].I;
+  const int H = a.H;
+  const int K = kGateUp ? H : I;
+  const int f0 = fb * kF8Feat;
+  if (f0 >= (kGateUp ? I : H)) return;
+  const int KB = K / kF8K;
+  const int ntb = (tl.nrows + 15) >> 4;
+  // activation rows staged in LDS: 16-B chunk c = tid + 512 i of 128 rows x 128 B
+  const uint8_t* ap[2];
+  int aoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 512 * i;
+    const int r = c >> 3, col = (c & 7) * 16;
+    aoff[i] = r * kF8LdsRow + col;
+    const int grow = tl.row0 + (r < tl.nrows ? r : 0);
+    if (kGateUp) {
+      const int64_t src = a.a_rowmap ? a.a_rowmap[grow] : grow;
+      ap[i] = a.a_q + src * (int64_t)H + col;
+    } else {
+      ap[i] = reinterpret_cast<const uint8_t*>(a.h) + (int64_t)grow * a.I_max + col;
+    }
+  }
+  const float* sp = nullptr;  // this thread's row of activation scales (threads < 128)
+  const int kbs = K / kF8K;
+  if (tid < kF8TileM) {
+    const int grow = tl.row0 + (tid < tl.nrows ? tid : 0);
+    if (kGateUp) {
+      const int64_t src = a.a_rowmap ? a.a_rowmap[grow] : grow;
+      sp = a.a_qscale + src * kbs;
+    } else {
+      sp = a.h_scale + (int64_t)grow * (a.I_max / kF8K);
+    }
+  }
+  // weight rows of this wavefront: 16 features
+  const int fw = f0 + wave * 16;
+  const uint8_t* w0;
+  const uint8_t* w1 = nullptr;
+  const float* s0;
+  const float* s1 = nullptr;
+  if (kGateUp) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.bank[bank].w13) + ge * 2 * (int64_t)I * H;
+    const float* sb = reinterpret_cast<const float*>(a.bank[bank].w13_scale) + ge * (2 * I / 128) * (int64_t)(H / 128);
+    w0 = base + (int64_t)(fw + m16) * H + g * 32;
+    w1 = base + (int64_t)(I + fw + m16) * H + g * 32;
+    s0 = sb + (int64_t)(f0 / 128) * (H / 128);
+    s1 = sb + (int64_t)((I + f0) / 128) * (H / 128);
+  } else {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.bank[bank].w2) + ge * (int64_t)H * I;
+    const float* sb = reinterpret_cast<const float*>(a.bank[bank].w2_scale) + ge * (H / 128) * (int64_t)(I / 128);
+    w0 = base + (int64_t)(fw + m16) * I + g * 32;
+    s0 = sb + (int64_t)(f0 / 128) * (I / 128);
+  }
+  f32x4 acc0[8], acc1[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) { acc0[t] = f32x4{0, 0, 0, 0}; acc1[t] = f32x4{0, 0, 0, 0}; }
+  // prologue: K block 0
+  u32x4 ra[2];
+  float rs = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i]);
+  if (sp) rs = sp[0];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&act[0][aoff[i]]) = ra[i];
+  if (tid < kF8TileM) ascale[0][tid] = rs;
+  i32x8 wa = ld32(w0), wb = kGateUp ? ld32(w1) : wa;
+  __syncthreads();
+  for (int kb = 0; kb < KB; ++kb) {
+    const int buf = kb & 1;
+    i32x8 na = wa, nb = wb;
+    if (kb + 1 < KB) {
+      const int64_t o = (int64_t)(kb + 1) * kF8K;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + o);
+      if (sp) rs = sp[kb + 1];
+      na = ld32(w0 + o);
+      if (kGateUp) nb = ld32(w1 + o);
+    }
+    const float sw0 = s0[kb];
+    const float sw1 = kGateUp ? s1[kb] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t < ntb) {
+        const i32x8 xb = *reinterpret_cast<const i32x8*>(&act[buf][(t * 16 + m16) * kF8LdsRow + g * 32]);
+        const float sx = ascale[buf][t * 16 + m16];
+        const f32x4 z = {0, 0, 0, 0};
+        f32x4 p0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, z, 0, 0, 0, 127, 0, 127);
+        const float c0 = sw0 * sx;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc0[t][i] += p0[i] * c0;
+        if (kGateUp) {
+          f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb, xb, z, 0, 0, 0, 127, 0, 127);
+          const float c1 = sw1 * sx;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc1[t][i] += p1[i] * c1;
+        }
+      }
+    }
+    if (kb + 1 < KB) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&act[buf ^ 1][aoff[i]]) = ra[i];
+      if (tid < kF8TileM) ascale[buf ^ 1][tid] = rs;
+    }
+    wa = na;
+    wb = nb;
+    __syncthreads();
+  }
+  // lane holds D[feature fw + 4g + i][token t*16 + m16]
+  if (kGateUp) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc0[t][i] = silu_mul(acc0[t][i], acc1[t][i]);
+        am = fmaxf(am, fabsf(acc0[t][i]));
+      }
+      am = wave_max16(am);
+      if (g == 0) red[wave][t * 16 + m16] = am;
+    }
+    __syncthreads();
+    uint8_t* hq = reinterpret_cast<uint8_t*>(a.h);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int tok = t * 16 + m16;
+      if (tok >= tl.nrows) continue;
+      float am = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) am = fmaxf(am, red[w][tok]);
+      const float sc = am == 0.0f ? 1.0f : __fdiv_rn(am, 448.0f);
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c |= e4m3_code(__fdiv_rn(acc0[t][i], sc)) << (8 * i);
+      const int64_t row = tl.row0 + tok;
+      *reinterpret_cast<uint32_t*>(hq + row * a.I_max + fw + 4 * g) = c;
+      if (wave == 0 && g == 0) a.h_scale[row * (a.I_max / kF8K) + f0 / kF8K] = sc;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int tok = t * 16 + m16;
+      if (tok >= tl.nrows) continue;
+      const int64_t o = (int64_t)(tl.row0 + tok) * H + fw + 4 * g;
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + o) =
+          make_float4(acc0[t][0], acc0[t][1], acc0[t][2], acc0[t][3]);
+    }
+  }
+}
+
 }  // namespace
 
 int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H) {
+  if (wdt == MOE_FP8_E4M3) return kF8TileM;
   // Few rows per expert: stream the weights (each weight element read once per tile of
   // <= 16 rows). Many rows: LDS-tiled GEMM with 128-row tiles.
   if (wdt == MOE_BF16 && H % kTBN == 0 && (int64_t)rows > 32 * (int64_t)groups) return kTBM;
@@ -374,6 +623,10 @@ int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H) {
 
 size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_max) {
   (void)H;
+  if (wdt == MOE_FP8_E4M3) {
+    const size_t q = ((size_t)rows_total * I_max + 255) / 256 * 256;
+    return q + ((size_t)rows_total * (I_max / kF8K) * sizeof(float) + 255) / 256 * 256;
+  }
   const size_t hb = (wdt == MOE_F32) ? 4 : 2;
   return ((size_t)rows_total * I_max * hb + 255) / 256 * 256;
 }
@@ -383,6 +636,17 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
     return mid_event ? hipEventRecord(mid_event, s) : hipSuccess;
   }
   a.h = scratch;
+  if (a.wdt == MOE_FP8_E4M3) {
+    a.h_scale = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) +
+                                         ((size_t)a.rows_total * a.I_max + 255) / 256 * 256);
+    const int nb_gu = a.I_max / kF8Feat, nb_dn = a.H / kF8Feat;
+    hipLaunchKernelGGL(k_fp8<true>, dim3(a.max_tiles * nb_gu), dim3(512), 0, s, a, nb_gu);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_fp8<false>, dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
+    return hipGetLastError();
+  }
   const int fb_gu = (a.I_max + kFeatPerWG - 1) / kFeatPerWG;
   const int fb_dn = (a.H + kFeatPerWG - 1) / kFeatPerWG;
   const bool f32 = a.wdt == MOE_F32;
@@ -418,8 +682,12 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
   return hipGetLastError();
 }
 
-hipError_t launch_quant_rows_fp8(const void*, int32_t, int32_t, uint8_t*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_quant_rows_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* qs,
+                                 hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_rows_fp8, dim3(n), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(x), H, q, qs);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -266,9 +266,20 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
 
 // ------------------------------------------------------------------- grouped FFN
 
+// Staging of fp8 activations: E4M3 codes [rows, H] and fp32 scales [rows, H/128].
+struct QPlan {
+  size_t o_q = 0, o_qs = 0;
+};
+static void plan_quant(Carve& c, QPlan& q, moe_dtype wdt, int32_t rows, int32_t H) {
+  if (wdt != MOE_FP8_E4M3) return;
+  q.o_q = c.take((size_t)rows * H);
+  q.o_qs = c.take((size_t)rows * (H / 128) * sizeof(float));
+}
+
 static bool plan_grouped(const moe_experts* w, moe_dtype act_dt, int32_t rows, FfnPlan* p,
-                         size_t* total) {
+                         QPlan* q, size_t* total) {
   Carve c;
+  plan_quant(c, *q, w->dtype, rows, w->H);
   plan_ffn(c, *p, w->dtype, act_dt, w->H, w->I, rows, w->E, 0, false);
   *total = c.off;
   return true;
@@ -277,8 +288,9 @@ static bool plan_grouped(const moe_experts* w, moe_dtype act_dt, int32_t rows, F
 size_t moe_grouped_ffn_workspace_size(const moe_experts* w, moe_dtype act_dt, int32_t rows) {
   if (!w || rows < 0 || w->E < 1 || w->H < 1 || w->I < 1) return 0;
   FfnPlan p;
+  QPlan q;
   size_t total;
-  plan_grouped(w, act_dt, rows, &p, &total);
+  plan_grouped(w, act_dt, rows, &p, &q, &total);
   return total;
 }
 
@@ -294,10 +306,11 @@ moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype a
   if (rows > 0 && (!x_perm || !y_perm)) return MOE_ERR_NULL;
   if ((x_perm && !al16(x_perm)) || (y_perm && !al16(y_perm)) || !al256(ws)) return MOE_ERR_ALIGN;
   FfnPlan p;
+  QPlan q;
   size_t total;
-  plan_grouped(w, act_dt, rows, &p, &total);
+  plan_grouped(w, act_dt, rows, &p, &q, &total);
   if (ws_bytes < total) return MOE_ERR_WORKSPACE;
-  if (w->dtype == MOE_FP8_E4M3 || w->dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
+  if (w->dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
   char* base = reinterpret_cast<char*>(ws);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_tiles_from_offsets(offsets, w->E, reinterpret_cast<Tile*>(base + p.o_tiles),
@@ -305,6 +318,13 @@ moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype a
   if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn tiles");
   FfnArgs f = ffn_args(p, base, *w, nullptr, act_dt, w->H, x_perm, nullptr, y_perm);
   f.y_dt = y_dt;
+  if (w->dtype == MOE_FP8_E4M3) {
+    e = launch_quant_rows_fp8(x_perm, rows, w->H, reinterpret_cast<uint8_t*>(base + q.o_q),
+                              reinterpret_cast<float*>(base + q.o_qs), s);
+    if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn quantise");
+    f.a_q = reinterpret_cast<const uint8_t*>(base + q.o_q);
+    f.a_qscale = reinterpret_cast<const float*>(base + q.o_qs);
+  }
   e = launch_grouped_ffn(f, base + p.o_scratch, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_ffn");
 }
@@ -340,7 +360,7 @@ static moe_status layer_forward(const moe_layer_desc* d, const void* x, void* ou
                                 void* const* events) {
   moe_status st = check_layer(d);
   if (st != MOE_OK) return st;
-  if (d->routed.dtype == MOE_FP8_E4M3 || d->routed.dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
+  if (d->routed.dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
   if (!ws || (d->T > 0 && (!x || !out))) return MOE_ERR_NULL;
   if ((x && !al16(x)) || (out && !al16(out)) || !al256(ws)) return MOE_ERR_ALIGN;
   if ((topk_idx_out && !al16(topk_idx_out)) || (topk_w_out && !al16(topk_w_out)) ||
@@ -376,10 +396,20 @@ static moe_status layer_forward(const moe_layer_desc* d, const void* x, void* ou
                           reinterpret_cast<int32_t*>(base + p.ffn.o_ntiles), p.ffn.tile_m,
                           shared ? 1 : 0, base + p.o_perm_ws, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer_forward permute");
+  const bool fp8 = d->routed.dtype == MOE_FP8_E4M3;
+  if (fp8) {
+    e = launch_quant_rows_fp8(x, T, H, reinterpret_cast<uint8_t*>(base + p.o_xq),
+                              reinterpret_cast<float*>(base + p.o_xqs), s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward quantise");
+  }
   MOE_MARK(2);
   void* y = base + p.ffn.o_y;
   FfnArgs f = ffn_args(p.ffn, base, d->routed, shared ? &d->shared : nullptr, d->act_dtype, H, x,
                        row_token, y);
+  if (fp8) {
+    f.a_q = reinterpret_cast<const uint8_t*>(base + p.o_xq);
+    f.a_qscale = reinterpret_cast<const float*>(base + p.o_xqs);
+  }
   e = launch_grouped_ffn(f, base + p.ffn.o_scratch, s, events ? ev[3] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "moe_layer_forward grouped_ffn");
   MOE_MARK(4);
@@ -414,8 +444,9 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* d, const void* x, void*
 // ------------------------------------------------------------- pre-routed rows
 
 static size_t plan_rows(const moe_experts* w, moe_dtype act_dt, int32_t rows, size_t o[6],
-                        FfnPlan* fp) {
+                        FfnPlan* fp, QPlan* qp) {
   Carve c;
+  plan_quant(c, *qp, w->dtype, rows, w->H);
   o[0] = c.take(w->E * sizeof(int32_t));             // counts
   o[1] = c.take((w->E + 1) * sizeof(int32_t));       // offsets
   o[2] = c.take((size_t)rows * sizeof(int32_t));     // perm_src
@@ -430,7 +461,8 @@ size_t moe_rows_workspace_size(const moe_experts* w, moe_dtype act_dt, int32_t r
   if (!w || rows < 0 || w->E < 1 || w->H < 1 || w->I < 1) return 0;
   size_t o[6];
   FfnPlan fp;
-  return plan_rows(w, act_dt, rows, o, &fp);
+  QPlan qp;
+  return plan_rows(w, act_dt, rows, o, &fp, &qp);
 }
 
 moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_dt,
@@ -446,9 +478,10 @@ moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_d
   if ((x && !al16(x)) || (out && !al16(out)) || !al256(ws)) return MOE_ERR_ALIGN;
   size_t o[6];
   FfnPlan p;
-  size_t total = plan_rows(w, act_dt, rows, o, &p);
+  QPlan qp;
+  size_t total = plan_rows(w, act_dt, rows, o, &p, &qp);
   if (ws_bytes < total) return MOE_ERR_WORKSPACE;
-  if (w->dtype == MOE_FP8_E4M3 || w->dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
+  if (w->dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
   char* base = reinterpret_cast<char*>(ws);
   hipStream_t s = (hipStream_t)stream;
   int32_t* inv_perm = reinterpret_cast<int32_t*>(base + o[3]);
@@ -462,10 +495,29 @@ moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_d
   if (e != hipSuccess) return hip_fail(e, "moe_rows_forward permute");
   void* y = base + p.o_y;
   FfnArgs f = ffn_args(p, base, *w, nullptr, act_dt, w->H, x, row_token, y);
+  if (w->dtype == MOE_FP8_E4M3) {
+    e = launch_quant_rows_fp8(x, rows, w->H, reinterpret_cast<uint8_t*>(base + qp.o_q),
+                              reinterpret_cast<float*>(base + qp.o_qs), s);
+    if (e != hipSuccess) return hip_fail(e, "moe_rows_forward quantise");
+    f.a_q = reinterpret_cast<const uint8_t*>(base + qp.o_q);
+    f.a_qscale = reinterpret_cast<const float*>(base + qp.o_qs);
+  }
   e = launch_grouped_ffn(f, base + p.o_scratch, s);
   if (e != hipSuccess) return hip_fail(e, "moe_rows_forward grouped_ffn");
   e = launch_combine(y, p.y_dt, inv_perm, row_w, rows, 1, w->H, nullptr, out, out_dt, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_rows_forward combine");
+}
+
+// --------------------------------------------------------------- fp8 quantiser
+
+moe_status moe_quantize_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* q_scale,
+                            void* stream) {
+  if (n < 0 || H < 128 || H % 128) return MOE_ERR_SHAPE;
+  if (n == 0) return MOE_OK;
+  if (!x || !q || !q_scale) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(q) || !al16(q_scale)) return MOE_ERR_ALIGN;
+  hipError_t e = launch_quant_rows_fp8(x, n, H, q, q_scale, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_fp8");
 }
 
 }  // extern "C"

@@ -177,3 +177,64 @@ def test_r1_prefill_full_size():
     print("r1_prefill sampled rel err", err, flush=True)
     assert err <= TOL["bf16"]
     assert np.isfinite(got["out"]).all()
+
+
+FP8_SMALL = [
+    MoEConfig("fp8_softmax_shared", T=100, H=256, E=8, k=2, I=256, score="softmax", shared_I=128,
+              act="bf16", wdt="fp8", out="bf16", seed=31, weight_seed=31),
+    MoEConfig("fp8_sigmoid_bias_ragged", T=333, H=384, E=5, k=3, I=128, score="sigmoid",
+              use_bias=True, scale=2.5, shared_I=256, act="bf16", wdt="fp8", out="f32", seed=32,
+              weight_seed=32),
+    MoEConfig("fp8_single_token", T=1, H=128, E=4, k=2, I=128, score="softmax", act="bf16",
+              wdt="fp8", out="bf16", seed=33, weight_seed=33),
+]
+
+
+def test_quantize_fp8_matches_oracle_bit_exact():
+    """moe_quantize_fp8: E4M3 codes and fp32 scales equal the oracle's, decided in fp32 on both
+    sides from the same bf16 input (zeros, subnormal-range and wide-range blocks included)."""
+    rng = np.random.default_rng(40)
+    n, H = 37, 640
+    v = rng.normal(0, 1, (n, H)) * 10.0 ** rng.uniform(-6, 3, (n, 1))
+    v[3, :128] = 0.0                       # all-zero block
+    v[4, 128:256] *= 1e-30                 # far below the E4M3 range
+    v[5, :] = rng.choice([-1.0, 1.0], H) * 2.0 ** rng.integers(-12, 12, H)
+    xb = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+    bits = xb.view(torch.int16).numpy().view(np.uint16)
+    x = xb.cuda()
+    q = torch.empty((n, H), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((n, H // 128), dtype=torch.float32, device="cuda")
+    moe.moe_quantize_fp8(x, q, qs)
+    torch.cuda.synchronize()
+    codes, scales, _ = O.quantise_rows_e4m3(O.bf16_to_f64(bits).astype(np.float32))
+    assert np.array_equal(qs.cpu().numpy(), scales)
+    assert np.array_equal(q.cpu().numpy(), codes)
+
+
+@pytest.mark.parametrize("cfg", FP8_SMALL, ids=lambda c: c.name)
+def test_fp8_layer_matches_oracle(cfg):
+    print("case", describe(cfg), flush=True)
+    host, dev = problems(cfg)
+    got = run_layer(cfg, dev)
+    want = O.layer_forward(host)
+    check_routing(got, want, cfg)
+    err = O.rel_err(got["out"], want["out"])
+    print(cfg.name, "rel err", err, flush=True)
+    assert err <= TOL["fp8"], (describe(cfg), err)
+
+
+def test_e384_fp8_full_size():
+    """384 routed experts, top-8 + shared, fp8 block-scaled weights and activations, T=4096:
+    routing of all tokens bit-exact, outputs of sampled tokens against the oracle."""
+    cfg = CONFIGS["e384_fp8"]
+    print("case", describe(cfg), flush=True)
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
+    got = run_layer(cfg, dev)
+    tokens = [0, 2047, 4095]
+    want = O.layer_forward(host, tokens=tokens)
+    check_routing(got, want, cfg)
+    err = O.rel_err(got["out"][tokens], want["out"])
+    print("e384_fp8 sampled rel err", err, flush=True)
+    assert err <= TOL["fp8"]
+    assert np.isfinite(got["out"]).all()
