@@ -219,17 +219,28 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
 }
 
 // ---------------------------------------------------------------------------------
-// Tiled kernels (many rows per expert, e.g. prefill): classic LDS-staged GEMM tiles of
-// 128 rows x 128 weight rows x 64 K per workgroup, 4 wavefronts of 64 x 64 each built
-// from v_mfma_f32_16x16x32_bf16. Global -> register prefetch of the next K block overlaps
-// the MFMAs on the current one (double-buffered LDS, one barrier per K block). LDS rows are
-// padded by 16 B so the 16-B fragment reads of 16 consecutive rows hit distinct banks.
-// For gate/up, the 128 weight rows of a tile are 64 gate and the matching 64 up rows,
-// interleaved in groups of 16 so that every lane holds gate and up of the same
-// (row, feature) and SwiGLU is applied in registers.
-constexpr int kTBM = 128, kTBN = 128, kTBK = 64;
-constexpr int kLdsRow = kTBK * 2 + 16;                    // bytes per LDS row
-constexpr int kLdsStage = (kTBM + kTBN) * kLdsRow;        // bytes per stage
+// Tiled kernels (many rows per expert, e.g. prefill): LDS-staged GEMM tiles of
+// BM = 32*TM rows x BN = 32*TN weight rows x 64 K per workgroup, 4 wavefronts in a 2 x 2
+// grid, each computing (16*TM) x (16*TN) with v_mfma_f32_16x16x32_bf16. Global ->
+// register prefetch of the next K block overlaps the MFMAs on the current one
+// (double-buffered LDS, one barrier per K block). LDS rows are padded by 16 B so the 16-B
+// fragment reads of 16 consecutive rows hit distinct banks. A lane's fragment of a K block
+// is the 32 contiguous bytes at 32*(lane/16) (K index = 16*(lane/16) + 8*ks + j in both
+// operands). For gate/up, the BN weight rows of a tile are BN/2 gate rows and the matching
+// BN/2 up rows, interleaved in groups of 16, so that each lane holds gate and up of the
+// same (row, feature) and SwiGLU is applied in registers.
+// MXFP4 weights: each thread converts its 8 E2M1 values (4 bytes) with their E8M0 block
+// scale to bf16 on the way into LDS (v_cvt_scalef32_pk_bf16_fp4, exact), so the MFMA
+// loop is the bf16 one.
+#ifndef MOE_TILED_TM
+#define MOE_TILED_TM 4
+#endif
+#ifndef MOE_TILED_TN
+#define MOE_TILED_TN 4
+#endif
+constexpr int kTTM = MOE_TILED_TM, kTTN = MOE_TILED_TN;
+constexpr int kTBM = 32 * kTTM, kTBN = 32 * kTTN, kTBK = 64;
+constexpr int kLdsRow = kTBK * 2 + 16;  // bytes per LDS row
 
 // Workgroup id remap so that consecutive logical ids run on the same XCD (ids are dealt
 // to the 8 XCDs round-robin), letting neighbours share their A tile in that XCD's L2.
@@ -238,9 +249,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
   return (bid % 8) * (grid / 8) + bid / 8;
 }
 
-template <bool kGateUp, bool kYF32>
-__global__ void __launch_bounds__(256, 2) k_tiled_bf16(FfnArgs a, int nb_per_tile) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kLdsStage];
+__device__ __forceinline__ float e8m0_f32(uint32_t c) {
+  if (c == 0xFFu) return __uint_as_float(0x7FC00000u);
+  if (c == 0u) return __uint_as_float(0x00400000u);  // 2^-127
+  return __uint_as_float(c << 23);
+}
+
+template <int TM, int TN, bool kGateUp, bool kYF32, bool kMX>
+__global__ void __launch_bounds__(256, 1) k_tiled(FfnArgs a, int nb_per_tile) {
+  constexpr int BM = 32 * TM, BN = 32 * TN;
+  constexpr int STAGE = (BM + BN) * kLdsRow;
+  constexpr int CA = BM / 32, CB = BN / 32;  // 16-B chunks per thread per K block
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int tile_id = bid / nb_per_tile;
@@ -252,109 +272,156 @@ __global__ void __launch_bounds__(256, 2) k_tiled_bf16(FfnArgs a, int nb_per_til
   const int I = a.bank[bank].I;
   const int H = a.H;
   const int K = kGateUp ? H : I;
-  const int fpb = kGateUp ? kTBN / 2 : kTBN;              // output features per tile
+  const int fpb = kGateUp ? BN / 2 : BN;  // output features per tile
   const int f0 = nb * fpb;
   if (f0 >= (kGateUp ? I : H)) return;
-  const char* wbase = kGateUp
-      ? reinterpret_cast<const char*>(a.bank[bank].w13) + ge * 2 * (int64_t)I * H * 2
-      : reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * 2;
-  // global -> LDS assignment: 16-B chunk c = tid + 256 i of a 128 x 128 B block
-  const char* ag[4];
-  const char* bg[4];
-  int lds_off[4];
+  const int wrows = kGateUp ? 2 * I : H;  // rows of this expert's weight matrix
+  // weights: bf16 rows of K elements, or MXFP4 rows of K/2 bytes with K/32 scale bytes
+  const char* wbase;
+  const uint8_t* sbase = nullptr;
+  if (kMX) {
+    wbase = reinterpret_cast<const char*>(kGateUp ? a.bank[bank].w13 : a.bank[bank].w2) +
+            ge * (int64_t)wrows * (K / 2);
+    sbase = reinterpret_cast<const uint8_t*>(kGateUp ? a.bank[bank].w13_scale : a.bank[bank].w2_scale) +
+            ge * (int64_t)wrows * (K / 32);
+  } else {
+    wbase = reinterpret_cast<const char*>(kGateUp ? a.bank[bank].w13 : a.bank[bank].w2) +
+            ge * (int64_t)wrows * K * 2;
+  }
+  const char* ag[CA];
+  const char* bg[CB];
+  const uint8_t* bs[CB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < CA; ++i) {
     const int c = tid + 256 * i;
     const int r = c >> 3, col = (c & 7) * 16;
-    lds_off[i] = r * kLdsRow + col;
     const int grow = tl.row0 + (r < tl.nrows ? r : tl.nrows - 1);
     if (kGateUp) {
       const int64_t src = a.a_rowmap ? a.a_rowmap[grow] : grow;
       ag[i] = reinterpret_cast<const char*>(a.a) + src * (int64_t)H * 2 + col;
-      const int half = r >> 6, jj = r & 63, grp = jj >> 4, within = jj & 15;
-      const int feat = f0 + half * 32 + (grp >> 1) * 16 + within;
-      const int wrow = (grp & 1) ? I + feat : feat;
-      bg[i] = wbase + (int64_t)wrow * K * 2 + col;
     } else {
       ag[i] = reinterpret_cast<const char*>(a.h) + (int64_t)grow * a.I_max * 2 + col;
-      bg[i] = wbase + (int64_t)(f0 + r) * K * 2 + col;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3, colc = c & 7;
+    int wrow;
+    if (kGateUp) {
+      const int half = r / (BN / 2), jj = r % (BN / 2), nt = jj >> 4, within = jj & 15;
+      const int feat = f0 + half * (BN / 4) + (nt >> 1) * 16 + within;
+      wrow = (nt & 1) ? I + feat : feat;
+    } else {
+      wrow = f0 + r;
+    }
+    if (kMX) {
+      bg[i] = wbase + (int64_t)wrow * (K / 2) + colc * 4;
+      bs[i] = sbase + (int64_t)wrow * (K / 32) + (colc >> 2);
+    } else {
+      bg[i] = wbase + (int64_t)wrow * K * 2 + colc * 16;
+      bs[i] = nullptr;
     }
   }
   const int wm = wave & 1, wn = wave >> 1;
   const int m16 = l & 15, g = l >> 4;
-  f32x4 acc[4][4];
+  f32x4 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-  u32x4 ra[4], rb[4];
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  u32x4 ra[CA];
+  u32x4 rb[kMX ? 1 : CB];
+  uint32_t rq[kMX ? CB : 1], rsc[kMX ? CB : 1];
+  auto load_block = [&](int kt) {
+    const int64_t o = (int64_t)kt * kTBK * 2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *reinterpret_cast<const u32x4*>(ag[i]);
-    rb[i] = *reinterpret_cast<const u32x4*>(bg[i]);
-  }
+    for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ag[i] + o);
+    if (kMX) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<u32x4*>(smem + lds_off[i]) = ra[i];
-    *reinterpret_cast<u32x4*>(smem + kTBM * kLdsRow + lds_off[i]) = rb[i];
-  }
+      for (int i = 0; i < CB; ++i) {
+        rq[i] = *reinterpret_cast<const uint32_t*>(bg[i] + (int64_t)kt * (kTBK / 2));
+        rsc[i] = bs[i][kt * (kTBK / 32)];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CB; ++i) rb[kMX ? 0 : i] = *reinterpret_cast<const u32x4*>(bg[i] + o);
+    }
+  };
+  auto store_block = [&](char* st) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(st + (c >> 3) * kLdsRow + (c & 7) * 16) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + 256 * i;
+      char* dst = st + BM * kLdsRow + (c >> 3) * kLdsRow + (c & 7) * 16;
+      if (kMX) {
+        const float sc = e8m0_f32(rsc[i]);
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(rq[i], sc, 0);
+        bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(rq[i], sc, 1);
+        bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(rq[i], sc, 2);
+        bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(rq[i], sc, 3);
+        u32x4 v;
+        v[0] = __builtin_bit_cast(uint32_t, p0);
+        v[1] = __builtin_bit_cast(uint32_t, p1);
+        v[2] = __builtin_bit_cast(uint32_t, p2);
+        v[3] = __builtin_bit_cast(uint32_t, p3);
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = rb[kMX ? 0 : i];
+      }
+    }
+  };
+  load_block(0);
+  store_block(smem);
   __syncthreads();
   const int KT = K / kTBK;
   for (int kt = 0; kt < KT; ++kt) {
-    const char* cur = smem + (kt & 1) * kLdsStage;
-    if (kt + 1 < KT) {
-      const int64_t o = (int64_t)(kt + 1) * kTBK * 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4*>(ag[i] + o);
-        rb[i] = *reinterpret_cast<const u32x4*>(bg[i] + o);
-      }
-    }
+    const char* cur = smem + (kt & 1) * STAGE;
+    if (kt + 1 < KT) load_block(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 fa[4], fb[4];
+      bf16x8 fa[TM], fb[TN];
       const int kb = g * 32 + ks * 16;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        fa[t] = *reinterpret_cast<const bf16x8*>(cur + (wm * 64 + t * 16 + m16) * kLdsRow + kb);
-        fb[t] = *reinterpret_cast<const bf16x8*>(cur + kTBM * kLdsRow +
-                                                 (wn * 64 + t * 16 + m16) * kLdsRow + kb);
-      }
+      for (int t = 0; t < TM; ++t)
+        fa[t] = *reinterpret_cast<const bf16x8*>(cur + (wm * (BM / 2) + t * 16 + m16) * kLdsRow + kb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int t = 0; t < TN; ++t)
+        fb[t] = *reinterpret_cast<const bf16x8*>(cur + BM * kLdsRow +
+                                                 (wn * (BN / 2) + t * 16 + m16) * kLdsRow + kb);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) {
-      char* nxt = smem + ((kt + 1) & 1) * kLdsStage;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<u32x4*>(nxt + lds_off[i]) = ra[i];
-        *reinterpret_cast<u32x4*>(nxt + kTBM * kLdsRow + lds_off[i]) = rb[i];
-      }
-    }
+    if (kt + 1 < KT) store_block(smem + ((kt + 1) & 1) * STAGE);
     __syncthreads();
   }
   // epilogue: lane holds D[row 4g+i][column m16] of each 16 x 16 sub-tile
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < TM; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rl = wm * 64 + mt * 16 + 4 * g + i;
+      const int rl = wm * (BM / 2) + mt * 16 + 4 * g + i;
       if (rl >= tl.nrows) continue;
       const int64_t row = tl.row0 + rl;
       if (kGateUp) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int feat = f0 + wn * 32 + p * 16 + m16;
+        for (int p = 0; p < TN / 2; ++p) {
+          const int feat = f0 + wn * (BN / 4) + p * 16 + m16;
           const float hv = silu_mul(acc[mt][2 * p][i], acc[mt][2 * p + 1][i]);
           reinterpret_cast<uint16_t*>(a.h)[row * a.I_max + feat] = f32_to_bf16(hv);
         }
       } else {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int64_t o = row * H + f0 + wn * 64 + nt * 16 + m16;
+        for (int nt = 0; nt < TN; ++nt) {
+          const int64_t o = row * H + f0 + wn * (BN / 2) + nt * 16 + m16;
           if (kYF32) reinterpret_cast<float*>(a.y)[o] = acc[mt][nt][i];
           else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16(acc[mt][nt][i]);
         }
@@ -613,11 +680,24 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
 
 }  // namespace
 
-int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H) {
+bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I) {
+  switch (wdt) {
+    case MOE_F32:
+    case MOE_BF16: return H % 64 == 0 && I % 64 == 0;
+    case MOE_FP8_E4M3: return H % kF8Feat == 0 && I % kF8Feat == 0;
+    case MOE_MXFP4: return H % kTBN == 0 && I % (kTBN / 2) == 0 && H % kTBK == 0 && I % kTBK == 0;
+  }
+  return false;
+}
+
+int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32_t I_routed,
+                   int32_t I_shared) {
+  const bool tiled_ok = H % kTBN == 0 && I_routed % (kTBN / 2) == 0 && I_shared % (kTBN / 2) == 0;
   if (wdt == MOE_FP8_E4M3) return kF8TileM;
   // Few rows per expert: stream the weights (each weight element read once per tile of
   // <= 16 rows). Many rows: LDS-tiled GEMM with 128-row tiles.
-  if (wdt == MOE_BF16 && H % kTBN == 0 && (int64_t)rows > 32 * (int64_t)groups) return kTBM;
+  if (wdt == MOE_MXFP4) return kTBM;
+  if (wdt == MOE_BF16 && tiled_ok && (int64_t)rows > 32 * (int64_t)groups) return kTBM;
   return kStreamTileM;
 }
 
@@ -654,14 +734,22 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
   dim3 blk(256);
   if (a.tile_m == kTBM) {
     const int nb_gu = a.I_max / (kTBN / 2), nb_dn = a.H / kTBN;
-    hipLaunchKernelGGL((k_tiled_bf16<true, false>), dim3(a.max_tiles * nb_gu), blk, 0, s, a, nb_gu);
+    const bool mx = a.wdt == MOE_MXFP4;
+    if (mx)
+      hipLaunchKernelGGL((k_tiled<kTTM, kTTN, true, false, true>), dim3(a.max_tiles * nb_gu), blk, 0, s, a, nb_gu);
+    else
+      hipLaunchKernelGGL((k_tiled<kTTM, kTTN, true, false, false>), dim3(a.max_tiles * nb_gu), blk, 0, s, a, nb_gu);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
-    if (yf32)
-      hipLaunchKernelGGL((k_tiled_bf16<false, true>), dim3(a.max_tiles * nb_dn), blk, 0, s, a, nb_dn);
+    if (mx && yf32)
+      hipLaunchKernelGGL((k_tiled<kTTM, kTTN, false, true, true>), dim3(a.max_tiles * nb_dn), blk, 0, s, a, nb_dn);
+    else if (mx)
+      hipLaunchKernelGGL((k_tiled<kTTM, kTTN, false, false, true>), dim3(a.max_tiles * nb_dn), blk, 0, s, a, nb_dn);
+    else if (yf32)
+      hipLaunchKernelGGL((k_tiled<kTTM, kTTN, false, true, false>), dim3(a.max_tiles * nb_dn), blk, 0, s, a, nb_dn);
     else
-      hipLaunchKernelGGL((k_tiled_bf16<false, false>), dim3(a.max_tiles * nb_dn), blk, 0, s, a, nb_dn);
+      hipLaunchKernelGGL((k_tiled<kTTM, kTTN, false, false, false>), dim3(a.max_tiles * nb_dn), blk, 0, s, a, nb_dn);
     return hipGetLastError();
   }
   if (f32)

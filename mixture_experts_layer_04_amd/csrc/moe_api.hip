@@ -30,19 +30,15 @@ moe_status check_bank(const moe_experts* w, int32_t H, bool need_scales) {
   switch (w->dtype) {
     case MOE_F32:
     case MOE_BF16:
-      if (H % 64 || w->I % 64) return MOE_ERR_SHAPE;
       break;
     case MOE_FP8_E4M3:
-      if (H % 128 || w->I % 128) return MOE_ERR_SHAPE;
-      if (need_scales && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_NULL;
-      break;
     case MOE_MXFP4:
-      if (H % 64 || w->I % 64) return MOE_ERR_SHAPE;
       if (need_scales && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_NULL;
       break;
     default:
       return MOE_ERR_DTYPE;
   }
+  if (!ffn_shape_ok(w->dtype, H, w->I)) return MOE_ERR_SHAPE;
   if (!al16(w->w13) || !al16(w->w2)) return MOE_ERR_ALIGN;
   if ((w->w13_scale && !al16(w->w13_scale)) || (w->w2_scale && !al16(w->w2_scale)))
     return MOE_ERR_ALIGN;
@@ -74,11 +70,12 @@ struct FfnPlan {
   moe_dtype y_dt = MOE_BF16;
 };
 
-void plan_ffn(Carve& c, FfnPlan& p, moe_dtype wdt, moe_dtype act, int32_t H, int32_t I_max,
-              int32_t rows_routed, int32_t E, int32_t shared_rows, bool need_y) {
+void plan_ffn(Carve& c, FfnPlan& p, moe_dtype wdt, moe_dtype act, int32_t H, int32_t I_routed,
+              int32_t I_shared, int32_t rows_routed, int32_t E, int32_t shared_rows, bool need_y) {
+  const int32_t I_max = I_shared > I_routed ? I_shared : I_routed;
   p.rows_total = rows_routed + shared_rows;
   p.I_max = I_max;
-  p.tile_m = ffn_tile_m(wdt, rows_routed, E, H);
+  p.tile_m = ffn_tile_m(wdt, rows_routed, E, H, I_routed, I_shared);
   int64_t mt = max_tiles(rows_routed, E, p.tile_m);
   if (shared_rows) mt += (shared_rows + p.tile_m - 1) / p.tile_m;
   p.max_tiles = (int32_t)mt;
@@ -118,10 +115,8 @@ LayerPlan plan_layer(const moe_layer_desc* d) {
     p.o_xq = c.take((size_t)T * H);
     p.o_xqs = c.take((size_t)T * (H / 128) * sizeof(float));
   }
-  int32_t I_max = d->routed.I;
-  if (shared && d->shared.I > I_max) I_max = d->shared.I;
-  plan_ffn(c, p.ffn, d->routed.dtype, d->act_dtype, H, I_max, (int32_t)rows, E, shared ? T : 0,
-           true);
+  plan_ffn(c, p.ffn, d->routed.dtype, d->act_dtype, H, d->routed.I, shared ? d->shared.I : 0,
+           (int32_t)rows, E, shared ? T : 0, true);
   p.total = c.off;
   return p;
 }
@@ -280,7 +275,7 @@ static bool plan_grouped(const moe_experts* w, moe_dtype act_dt, int32_t rows, F
                          QPlan* q, size_t* total) {
   Carve c;
   plan_quant(c, *q, w->dtype, rows, w->H);
-  plan_ffn(c, *p, w->dtype, act_dt, w->H, w->I, rows, w->E, 0, false);
+  plan_ffn(c, *p, w->dtype, act_dt, w->H, w->I, 0, rows, w->E, 0, false);
   *total = c.off;
   return true;
 }
@@ -310,7 +305,6 @@ moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype a
   size_t total;
   plan_grouped(w, act_dt, rows, &p, &q, &total);
   if (ws_bytes < total) return MOE_ERR_WORKSPACE;
-  if (w->dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
   char* base = reinterpret_cast<char*>(ws);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_tiles_from_offsets(offsets, w->E, reinterpret_cast<Tile*>(base + p.o_tiles),
@@ -360,7 +354,6 @@ static moe_status layer_forward(const moe_layer_desc* d, const void* x, void* ou
                                 void* const* events) {
   moe_status st = check_layer(d);
   if (st != MOE_OK) return st;
-  if (d->routed.dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
   if (!ws || (d->T > 0 && (!x || !out))) return MOE_ERR_NULL;
   if ((x && !al16(x)) || (out && !al16(out)) || !al256(ws)) return MOE_ERR_ALIGN;
   if ((topk_idx_out && !al16(topk_idx_out)) || (topk_w_out && !al16(topk_w_out)) ||
@@ -453,7 +446,7 @@ static size_t plan_rows(const moe_experts* w, moe_dtype act_dt, int32_t rows, si
   o[3] = c.take((size_t)rows * sizeof(int32_t));     // inv_perm
   o[4] = c.take((size_t)rows * sizeof(int32_t));     // row_token
   o[5] = c.take(permute_ws_bytes(rows, w->E));
-  plan_ffn(c, *fp, w->dtype, act_dt, w->H, w->I, rows, w->E, 0, true);
+  plan_ffn(c, *fp, w->dtype, act_dt, w->H, w->I, 0, rows, w->E, 0, true);
   return c.off;
 }
 
@@ -481,7 +474,6 @@ moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_d
   QPlan qp;
   size_t total = plan_rows(w, act_dt, rows, o, &p, &qp);
   if (ws_bytes < total) return MOE_ERR_WORKSPACE;
-  if (w->dtype == MOE_MXFP4) return MOE_ERR_DTYPE;
   char* base = reinterpret_cast<char*>(ws);
   hipStream_t s = (hipStream_t)stream;
   int32_t* inv_perm = reinterpret_cast<int32_t*>(base + o[3]);

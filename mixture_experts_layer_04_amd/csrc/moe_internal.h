@@ -111,7 +111,11 @@ hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* ti
                                      int32_t* ntiles, int32_t tile_m, hipStream_t s);
 
 // grouped_ffn.hip
-int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H);
+// Whether the grouped FFN kernels support this format and shape.
+bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I);
+// Rows per tile for a call: streaming (16) or tiled; I_shared = 0 when there is none.
+int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32_t I_routed,
+                   int32_t I_shared);
 size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_max);
 // Runs gate/up + SwiGLU and down for all tiles. `scratch` holds h (and fp8 staging).
 // If mid_event is non-NULL it is recorded between the gate/up and the down launches.

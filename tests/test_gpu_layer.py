@@ -15,7 +15,7 @@ import synth
 from synth.configs import CONFIGS, MoEConfig
 from synth.problem import device_problem, host_problem
 
-from moe_cases import TOL, describe, experts, make_layer, problems, run_layer
+from moe_cases import TOL, describe, experts, make_layer, problems, run_layer, run_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -237,4 +237,50 @@ def test_e384_fp8_full_size():
     err = O.rel_err(got["out"][tokens], want["out"])
     print("e384_fp8 sampled rel err", err, flush=True)
     assert err <= TOL["fp8"]
+    assert np.isfinite(got["out"]).all()
+
+
+MX_ROWS = [
+    MoEConfig("mxfp4_rows_small", T=700, H=256, E=6, k=1, I=128, score="none", act="bf16",
+              wdt="mxfp4", out="bf16", seed=51, weight_seed=51, dirichlet_alpha=0.5),
+    MoEConfig("mxfp4_rows_f32out_ragged", T=257, H=384, E=9, k=1, I=192, score="none", act="bf16",
+              wdt="mxfp4", out="f32", seed=52, weight_seed=52, dirichlet_alpha=0.5),
+]
+
+
+@pytest.mark.parametrize("cfg", MX_ROWS, ids=lambda c: c.name)
+def test_mxfp4_rows_match_oracle(cfg):
+    print("case", describe(cfg), flush=True)
+    host, dev = problems(cfg)
+    got = run_rows(cfg, dev)
+    want = O.layer_forward(host)
+    err = O.rel_err(got["out"], want["out"])
+    print(cfg.name, "rel err", err, flush=True)
+    assert err <= TOL["mxfp4"], (describe(cfg), err)
+
+
+def test_mxfp4_routed_layer_matches_oracle():
+    cfg = MoEConfig("mxfp4_routed_shared", T=300, H=256, E=8, k=2, I=128, score="sigmoid",
+                    use_bias=True, scale=2.5, shared_I=128, act="bf16", wdt="mxfp4", out="bf16",
+                    seed=53, weight_seed=53)
+    host, dev = problems(cfg)
+    got = run_layer(cfg, dev)
+    want = O.layer_forward(host)
+    check_routing(got, want, cfg)
+    assert O.rel_err(got["out"], want["out"]) <= TOL["mxfp4"]
+
+
+def test_ep32_mxfp4_full_size():
+    """One GPU's expert-parallel share: 32 local MXFP4 experts, 16384 received rows with
+    Dirichlet(0.5)-multinomial loads; sampled rows against the oracle."""
+    cfg = CONFIGS["ep32_mxfp4"]
+    print("case", describe(cfg), flush=True)
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
+    got = run_rows(cfg, dev)
+    rows = [0, 8000, 16383]
+    want = O.layer_forward(host, tokens=rows)
+    err = O.rel_err(got["out"][rows], want["out"])
+    print("ep32_mxfp4 sampled rel err", err, flush=True)
+    assert err <= TOL["mxfp4"]
     assert np.isfinite(got["out"]).all()
