@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--workload", default="r1_decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run 3 plain device copies of this many MiB (a known-size "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -90,6 +93,26 @@ def cpu_baseline(cfg, host, n_tokens):
             "sample": f"{len(tokens)} of {cfg.T} tokens of the same batch (routing of all {cfg.T} "
                       f"tokens, {len(used)} routed experts + shared expert FFNs in float64), "
                       f"{dt:.1f} s"}
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE scaled by a plain
+    copy of known size), or None when absent or taken on kernel sources that have changed."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    return rec["traffic_bytes"]
 
 
 def main():
@@ -148,6 +171,16 @@ def main():
     stage_ms = {s_: float(np.mean(v)) for s_, v in stage.items()}
     log("stage ms: " + ", ".join(f"{s_}={v:.4f}" for s_, v in stage_ms.items()))
 
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: 3 x {args.copy_probe_mib} MiB device copies")
+
     cnt = counts.cpu().numpy()
     touched = int((cnt > 0).sum())
     rows = T * k + (T if cfg.shared_I else 0)
@@ -189,7 +222,7 @@ def main():
                    "layer_hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "kernel": "grouped gate/up + SwiGLU (k_gateup_stream)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(cfg.name),
                      "algorithmic_bytes_per_launch": gu_bytes,
                      "avg_launch_ms": stage_ms["gate_up"]},
         "cpu_baseline": cpu,
