@@ -223,8 +223,10 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
 // BM = 32*TM rows x BN = 32*TN weight rows x 64 K per workgroup, 4 wavefronts in a 2 x 2
 // grid, each computing (16*TM) x (16*TN) with v_mfma_f32_16x16x32_bf16. Global ->
 // register prefetch of the next K block overlaps the MFMAs on the current one
-// (double-buffered LDS, one barrier per K block). LDS rows are padded by 16 B so the 16-B
-// fragment reads of 16 consecutive rows hit distinct banks. A lane's fragment of a K block
+// (double-buffered LDS, one barrier per K block). The LDS layout is the row-interleaved,
+// XOR-swizzled one of lds_off(), which serves 16-row fragment reads at the full LDS rate.
+// This kernel carries the MXFP4 weights; bf16 weights use the DMA kernel k_tiled2 below.
+// A lane's fragment of a K block
 // is the 32 contiguous bytes at 32*(lane/16) (K index = 16*(lane/16) + 8*ks + j in both
 // operands). For gate/up, the BN weight rows of a tile are BN/2 gate rows and the matching
 // BN/2 up rows, interleaved in groups of 16, so that each lane holds gate and up of the
@@ -238,14 +240,19 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
 #ifndef MOE_TILED_TN
 #define MOE_TILED_TN 4
 #endif
+#ifndef MOE_TILED_EXPERT_ORDER
+#define MOE_TILED_EXPERT_ORDER 0
+#endif
 constexpr int kTTM = MOE_TILED_TM, kTTN = MOE_TILED_TN;
 constexpr int kTBM = 32 * kTTM, kTBN = 32 * kTTN, kTBK = 64;
-constexpr int kLdsRow = kTBK * 2 + 16;  // bytes per LDS row
 
 // Workgroup id remap so that consecutive logical ids run on the same XCD (ids are dealt
 // to the 8 XCDs round-robin), letting neighbours share their A tile in that XCD's L2.
+#ifndef MOE_XCD_REMAP
+#define MOE_XCD_REMAP 0
+#endif
 __device__ __forceinline__ int xcd_remap(int bid, int grid) {
-  if (grid % 8) return bid;
+  if (!MOE_XCD_REMAP || grid % 8) return bid;
   return (bid % 8) * (grid / 8) + bid / 8;
 }
 
@@ -255,17 +262,39 @@ __device__ __forceinline__ float e8m0_f32(uint32_t c) {
   return __uint_as_float(c << 23);
 }
 
+// LDS byte offset of logical 16-B chunk c of tile row r (each 16-row group takes
+// eight 256-B lines, row j and row 8 + j share line j, chunks XOR-swizzled by row & 7;
+// see the DMA kernel below).
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return (r >> 4) * 2048 + (r & 7) * 256 + ((r >> 3) & 1) * 128 + ((c ^ (r & 7)) << 4);
+}
+// Row and logical chunk that lane l of 1-KB DMA block q writes.
+__device__ __forceinline__ void dma_slot(int q, int l, int* r, int* c) {
+  const int half = (l >> 3) & 1;
+  *r = (q >> 1) * 16 + (q & 1) * 4 + (l >> 4) + 8 * half;
+  *c = (l & 7) ^ (*r & 7);
+}
+
 template <int TM, int TN, bool kGateUp, bool kYF32, bool kMX>
 __global__ void __launch_bounds__(256, 1) k_tiled(FfnArgs a, int nb_per_tile) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
-  constexpr int STAGE = (BM + BN) * kLdsRow;
+  constexpr int STAGE = (BM + BN) * 128;
   constexpr int CA = BM / 32, CB = BN / 32;  // 16-B chunks per thread per K block
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  // Logical order: expert-major; inside an expert, weight block nb major and row tile
+  // minor, so all row tiles of an expert stream each weight block together (one weight
+  // stream per expert in the XCD's L2) while their activation tiles stay resident.
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile_id = bid / nb_per_tile;
-  const int nb = bid - tile_id * nb_per_tile;
-  if (tile_id >= *a.ntiles) return;
+  const int t0 = bid / nb_per_tile;
+  if (t0 >= *a.ntiles) return;
+  const Tile head = a.tiles[t0];
+  int tile_id = t0, nb = bid - t0 * nb_per_tile;
+  if (MOE_TILED_EXPERT_ORDER) {
+    const int local = bid - head.first * nb_per_tile;
+    nb = local / head.ntile;
+    tile_id = head.first + (local - nb * head.ntile);
+  }
   const Tile tl = a.tiles[tile_id];
   const int bank = tl.group < a.E ? 0 : 1;
   const int64_t ge = tl.group < a.E ? tl.group : 0;
@@ -352,12 +381,12 @@ __global__ void __launch_bounds__(256, 1) k_tiled(FfnArgs a, int nb_per_tile) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(st + (c >> 3) * kLdsRow + (c & 7) * 16) = ra[i];
+      *reinterpret_cast<u32x4*>(st + lds_off(c >> 3, c & 7)) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int c = tid + 256 * i;
-      char* dst = st + BM * kLdsRow + (c >> 3) * kLdsRow + (c & 7) * 16;
+      char* dst = st + BM * 128 + lds_off(c >> 3, c & 7);
       if (kMX) {
         const float sc = e8m0_f32(rsc[i]);
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -389,11 +418,11 @@ __global__ void __launch_bounds__(256, 1) k_tiled(FfnArgs a, int nb_per_tile) {
       const int kb = g * 32 + ks * 16;
 #pragma unroll
       for (int t = 0; t < TM; ++t)
-        fa[t] = *reinterpret_cast<const bf16x8*>(cur + (wm * (BM / 2) + t * 16 + m16) * kLdsRow + kb);
+        fa[t] = *reinterpret_cast<const bf16x8*>(cur + lds_off(wm * (BM / 2) + t * 16 + m16, kb >> 4));
 #pragma unroll
       for (int t = 0; t < TN; ++t)
-        fb[t] = *reinterpret_cast<const bf16x8*>(cur + BM * kLdsRow +
-                                                 (wn * (BN / 2) + t * 16 + m16) * kLdsRow + kb);
+        fb[t] = *reinterpret_cast<const bf16x8*>(cur + BM * 128 +
+                                                 lds_off(wn * (BN / 2) + t * 16 + m16, kb >> 4));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -422,6 +451,199 @@ __global__ void __launch_bounds__(256, 1) k_tiled(FfnArgs a, int nb_per_tile) {
 #pragma unroll
         for (int nt = 0; nt < TN; ++nt) {
           const int64_t o = row * H + f0 + wn * (BN / 2) + nt * 16 + m16;
+          if (kYF32) reinterpret_cast<float*>(a.y)[o] = acc[mt][nt][i];
+          else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16(acc[mt][nt][i]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Tiled kernel, DMA version (bf16 weights): the same tile arithmetic as k_tiled, but the
+// K blocks go from global memory straight into LDS with global_load_lds_dwordx4 (no
+// register staging), through an S-stage ring so that each load has S-1 K blocks of MFMA
+// work to hide behind. LDS layout of a K block (128 B per row): each 16-row group takes
+// 2 KB = eight 256-B lines; line j holds row j in its low 128 B and row 8 + j in its high
+// 128 B, and the 16-B chunk c of row r sits at chunk c ^ (r & 7). Measured on MI355X, this
+// lets the fragment reads of 16 consecutive rows at one chunk run at the full LDS rate
+// (~250 B/clk/CU) where padded or plainly swizzled rows reach half of it. A wavefront's
+// DMA writes 1 KB contiguously (16 B per lane, lane order), i.e. 4 + 4 rows of a group,
+// and each lane's global address absorbs the layout.
+#ifndef MOE_T2_TM
+#define MOE_T2_TM 4
+#endif
+#ifndef MOE_T2_TN
+#define MOE_T2_TN 4
+#endif
+#ifndef MOE_T2_WGM
+#define MOE_T2_WGM 2
+#endif
+#ifndef MOE_T2_WGN
+#define MOE_T2_WGN 2
+#endif
+#ifndef MOE_T2_ORDER
+#define MOE_T2_ORDER 0
+#endif
+#ifndef MOE_T2_STAGES
+#define MOE_T2_STAGES 2
+#endif
+#ifndef MOE_T2_WAVES_PER_SIMD
+#define MOE_T2_WAVES_PER_SIMD 2
+#endif
+constexpr int kT2Threads = 64 * MOE_T2_WGM * MOE_T2_WGN;
+constexpr int kT2M = MOE_T2_WGM * 16 * MOE_T2_TM, kT2N = MOE_T2_WGN * 16 * MOE_T2_TN;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 B per lane from global memory into LDS at lds + 16 * lane (a device-only wrapper: the
+// target builtin must not appear in code the host pass instantiates).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup of WGM x WGN wavefronts; each wavefront computes (16 TM) x (16 TN).
+template <int TM, int TN, int WGM, int WGN, int S, bool kGateUp, bool kYF32>
+__global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled2(FfnArgs a, int nb_per_tile) {
+  constexpr int NW = WGM * WGN;
+  constexpr int BM = WGM * 16 * TM, BN = WGN * 16 * TN;
+  constexpr int STAGE = (BM + BN) * 128;
+  constexpr int RPI = NW * 8;                  // LDS rows filled per DMA instruction round
+  constexpr int CA = BM / RPI, CB = BN / RPI;  // DMA instructions per thread per K block
+  static_assert(BM % RPI == 0 && BN % RPI == 0 && BM % 16 == 0, "tile rows per DMA round");
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int t0 = bid / nb_per_tile;
+  if (t0 >= *a.ntiles) return;
+  const Tile head = a.tiles[t0];
+  int nb, tidx;
+  if (MOE_T2_ORDER) {
+    const int local = bid - head.first * nb_per_tile;
+    nb = local / head.ntile;
+    tidx = head.first + (local - nb * head.ntile);
+  } else {
+    nb = bid - t0 * nb_per_tile;
+    tidx = t0;
+  }
+  const Tile tl = a.tiles[tidx];
+  const int bank = tl.group < a.E ? 0 : 1;
+  const int64_t ge = tl.group < a.E ? tl.group : 0;
+  const int I = a.bank[bank].I;
+  const int H = a.H;
+  const int K = kGateUp ? H : I;
+  const int fpb = kGateUp ? BN / 2 : BN;
+  const int f0 = nb * fpb;
+  if (f0 >= (kGateUp ? I : H)) return;
+  const char* wbase = reinterpret_cast<const char*>(kGateUp ? a.bank[bank].w13 : a.bank[bank].w2) +
+                      ge * (int64_t)(kGateUp ? 2 * I : H) * K * 2;
+  // DMA instruction i of wavefront w fills 1-KB block q = NW i + w of the A (then B) tile
+  const char* ag[CA];
+  const char* bg[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    int r, cc;
+    dma_slot(NW * i + wave, l, &r, &cc);
+    const int col = cc * 16;
+    const int grow = tl.row0 + (r < tl.nrows ? r : tl.nrows - 1);
+    if (kGateUp) {
+      const int64_t src = a.a_rowmap ? a.a_rowmap[grow] : grow;
+      ag[i] = reinterpret_cast<const char*>(a.a) + src * (int64_t)H * 2 + col;
+    } else {
+      ag[i] = reinterpret_cast<const char*>(a.h) + (int64_t)grow * a.I_max * 2 + col;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    int r, cc;
+    dma_slot(NW * i + wave, l, &r, &cc);
+    const int col = cc * 16;
+    int wrow;
+    if (kGateUp) {
+      // N-wavefront block of 16 TN rows: gate and up rows of 8 TN features, by 16
+      const int blk = r / (16 * TN), jj = r % (16 * TN), nt = jj >> 4, within = jj & 15;
+      const int feat = f0 + blk * (8 * TN) + (nt >> 1) * 16 + within;
+      wrow = (nt & 1) ? I + feat : feat;
+    } else {
+      wrow = f0 + r;
+    }
+    bg[i] = wbase + (int64_t)wrow * K * 2 + col;
+  }
+  auto issue = [&](int kt, int stage) {
+    const int64_t o = (int64_t)kt * 128;
+    char* st = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) dma16(ag[i] + o, st + (NW * i + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) dma16(bg[i] + o, st + BM * 128 + (NW * i + wave) * 1024);
+  };
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int m16 = l & 15, g = l >> 4;
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  const int KT = K / kTBK;
+  int arow[TM], brow[TN];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) arow[t] = wm * (16 * TM) + t * 16 + m16;
+#pragma unroll
+  for (int t = 0; t < TN; ++t) brow[t] = wn * (16 * TN) + t * 16 + m16;
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < KT) issue(p, p);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * (CA + CB)>();
+    else wait_vmcnt<0>();
+    // A plain barrier, not __syncthreads(): its fence would wait for every outstanding
+    // DMA of the ring. The wait above already covers this thread's part of block kt.
+    __builtin_amdgcn_s_barrier();
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    const char* cur = smem + (kt % S) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[TM], fb[TN];
+      const int c = 2 * g + ks;  // logical 16-B chunk
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        fa[t] = *reinterpret_cast<const bf16x8*>(cur + lds_off(arow[t], c));
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        fb[t] = *reinterpret_cast<const bf16x8*>(cur + BM * 128 + lds_off(brow[t], c));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < TM; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = wm * (16 * TM) + mt * 16 + 4 * g + i;
+      if (rl >= tl.nrows) continue;
+      const int64_t row = tl.row0 + rl;
+      if (kGateUp) {
+#pragma unroll
+        for (int p = 0; p < TN / 2; ++p) {
+          const int feat = f0 + wn * (8 * TN) + p * 16 + m16;
+          const float hv = silu_mul(acc[mt][2 * p][i], acc[mt][2 * p + 1][i]);
+          reinterpret_cast<uint16_t*>(a.h)[row * a.I_max + feat] = f32_to_bf16(hv);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < TN; ++nt) {
+          const int64_t o = row * H + f0 + wn * (16 * TN) + nt * 16 + m16;
           if (kYF32) reinterpret_cast<float*>(a.y)[o] = acc[mt][nt][i];
           else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16(acc[mt][nt][i]);
         }
@@ -692,12 +914,12 @@ bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I) {
 
 int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32_t I_routed,
                    int32_t I_shared) {
-  const bool tiled_ok = H % kTBN == 0 && I_routed % (kTBN / 2) == 0 && I_shared % (kTBN / 2) == 0;
   if (wdt == MOE_FP8_E4M3) return kF8TileM;
   // Few rows per expert: stream the weights (each weight element read once per tile of
   // <= 16 rows). Many rows: LDS-tiled GEMM with 128-row tiles.
   if (wdt == MOE_MXFP4) return kTBM;
-  if (wdt == MOE_BF16 && tiled_ok && (int64_t)rows > 32 * (int64_t)groups) return kTBM;
+  const bool t2_ok = H % kT2N == 0 && I_routed % (kT2N / 2) == 0 && I_shared % (kT2N / 2) == 0;
+  if (wdt == MOE_BF16 && t2_ok && (int64_t)rows > 32 * (int64_t)groups) return kT2M;
   return kStreamTileM;
 }
 
@@ -732,6 +954,18 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
   const bool f32 = a.wdt == MOE_F32;
   const bool yf32 = a.y_dt == MOE_F32;
   dim3 blk(256);
+  if (a.tile_m == kT2M && a.wdt == MOE_BF16) {
+    const int nb_gu = a.I_max / (kT2N / 2), nb_dn = a.H / kT2N;
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, true, false>), dim3(a.max_tiles * nb_gu), dim3(kT2Threads), 0, s, a, nb_gu);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
+    if (yf32)
+      hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, true>), dim3(a.max_tiles * nb_dn), dim3(kT2Threads), 0, s, a, nb_dn);
+    else
+      hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, false>), dim3(a.max_tiles * nb_dn), dim3(kT2Threads), 0, s, a, nb_dn);
+    return hipGetLastError();
+  }
   if (a.tile_m == kTBM) {
     const int nb_gu = a.I_max / (kTBN / 2), nb_dn = a.H / kTBN;
     const bool mx = a.wdt == MOE_MXFP4;
