@@ -667,10 +667,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
 //  - gate/up epilogue: h = SiLU(g) * u in fp32, per-token amax over the workgroup's 128
 //    features (wavefront shuffles, then LDS across wavefronts), scale = amax / 448,
 //    E4M3 codes of h / scale -- exactly one 1 x 128 quantisation block per workgroup.
+#ifndef MOE_F8_STAGES_GU
+#define MOE_F8_STAGES_GU 3
+#endif
+#ifndef MOE_F8_STAGES_DN
+#define MOE_F8_STAGES_DN 4
+#endif
 constexpr int kF8TileM = 128;
 constexpr int kF8Feat = 128;
 constexpr int kF8K = 128;
-constexpr int kF8LdsRow = kF8K + 16;
 
 // fp32 -> E4M3FN code, round to nearest even, saturating at +-448 (NaN -> 0x7F).
 // Written from the format: magnitudes below 2^-6 lie on the subnormal grid m * 2^-9;
@@ -738,11 +743,30 @@ __device__ __forceinline__ i32x8 ld32(const void* p) {
   return r;
 }
 
+// 4 B per lane from global memory into LDS at lds + 4 * lane (device-only wrapper).
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+
 template <bool kGateUp>
 __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
-  __shared__ __attribute__((aligned(16))) uint8_t act[2][kF8TileM * kF8LdsRow];
-  __shared__ float ascale[2][kF8TileM];
-  __shared__ float red[8][kF8TileM];
+  // Each K block of the workgroup's operands -- its 128 (down) or 256 (gate/up) weight
+  // rows, the tile's 128 activation rows (both in the full-rate layout of lds_off) and the
+  // fp32 scales of both -- goes global -> LDS by DMA through an S-stage ring, requested
+  // S-1 blocks ahead. The K loop issues no other vector-memory load and reads no other LDS
+  // object, so its only vector-memory wait is the one for the oldest stage.
+  constexpr int S = kGateUp ? MOE_F8_STAGES_GU : MOE_F8_STAGES_DN;
+  constexpr int WR = kGateUp ? 2 * kF8Feat : kF8Feat;   // weight rows per stage
+  constexpr int WB = WR * 128;                           // weight bytes per stage
+  constexpr int ACT = kF8TileM * 128;
+  constexpr int SCL = 8 * 128;  // per wavefront: its 16 rows' scales, then the weight scales
+  constexpr int STG = WB + ACT + SCL;
+  constexpr int NWD = WR / 64;                           // weight DMA ops per thread
+  constexpr int A = NWD + 2 + 1;                         // DMA ops per thread per K block
+  // The ring is the kernel's only LDS object (the epilogue's amax table reuses it): with
+  // a second one the compiler tags LDS accesses with alias scopes and then makes every
+  // ring read wait for all outstanding DMA, not just for the oldest stage's.
+  __shared__ __attribute__((aligned(1024))) char ring[S * STG];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int m16 = l & 15, g = l >> 4;
   const int tile_id = blockIdx.x / fb_per_tile;
@@ -758,84 +782,101 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   if (f0 >= (kGateUp ? I : H)) return;
   const int KB = K / kF8K;
   const int ntb = (tl.nrows + 15) >> 4;
-  // activation rows staged in LDS: 16-B chunk c = tid + 512 i of 128 rows x 128 B
+  // weight DMA sources: block q = 8 i + wave of the weight area; tile rows r < 128 are the
+  // gate (or down) rows f0 + r, rows 128.. the up rows I + f0 + r - 128
+  const uint8_t* wbase = reinterpret_cast<const uint8_t*>(kGateUp ? a.bank[bank].w13 : a.bank[bank].w2) +
+                         ge * (int64_t)(kGateUp ? 2 * I : H) * K;
+  const uint8_t* wp[NWD];
+#pragma unroll
+  for (int i = 0; i < NWD; ++i) {
+    int r, c;
+    dma_slot(8 * i + wave, l, &r, &c);
+    const int wrow = r < kF8Feat ? f0 + r : I + f0 + (r - kF8Feat);
+    wp[i] = wbase + (int64_t)wrow * K + c * 16;
+  }
+  // activation DMA sources: block q = 8 i + wave of the activation area
   const uint8_t* ap[2];
-  int aoff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int c = tid + 512 * i;
-    const int r = c >> 3, col = (c & 7) * 16;
-    aoff[i] = r * kF8LdsRow + col;
+    int r, c;
+    dma_slot(8 * i + wave, l, &r, &c);
     const int grow = tl.row0 + (r < tl.nrows ? r : 0);
     if (kGateUp) {
       const int64_t src = a.a_rowmap ? a.a_rowmap[grow] : grow;
-      ap[i] = a.a_q + src * (int64_t)H + col;
+      ap[i] = a.a_q + src * (int64_t)H + c * 16;
     } else {
-      ap[i] = reinterpret_cast<const uint8_t*>(a.h) + (int64_t)grow * a.I_max + col;
+      ap[i] = reinterpret_cast<const uint8_t*>(a.h) + (int64_t)grow * a.I_max + c * 16;
     }
   }
-  const float* sp = nullptr;  // this thread's row of activation scales (threads < 128)
-  const int kbs = K / kF8K;
-  if (tid < kF8TileM) {
-    const int grow = tl.row0 + (tid < tl.nrows ? tid : 0);
+  // scales: lanes 0..15 of wavefront w fetch those of rows 16 w + lane, lanes 16 and 17
+  // the gate (or down) and up weight block scales, into the wavefront's 128-B slot
+  const float* sp;
+  if (l < 16) {
+    const int r = wave * 16 + m16;
+    const int grow = tl.row0 + (r < tl.nrows ? r : 0);
     if (kGateUp) {
       const int64_t src = a.a_rowmap ? a.a_rowmap[grow] : grow;
-      sp = a.a_qscale + src * kbs;
+      sp = a.a_qscale + src * (H / kF8K);
     } else {
       sp = a.h_scale + (int64_t)grow * (a.I_max / kF8K);
     }
-  }
-  // weight rows of this wavefront: 16 features
-  const int fw = f0 + wave * 16;
-  const uint8_t* w0;
-  const uint8_t* w1 = nullptr;
-  const float* s0;
-  const float* s1 = nullptr;
-  if (kGateUp) {
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.bank[bank].w13) + ge * 2 * (int64_t)I * H;
-    const float* sb = reinterpret_cast<const float*>(a.bank[bank].w13_scale) + ge * (2 * I / 128) * (int64_t)(H / 128);
-    w0 = base + (int64_t)(fw + m16) * H + g * 32;
-    w1 = base + (int64_t)(I + fw + m16) * H + g * 32;
-    s0 = sb + (int64_t)(f0 / 128) * (H / 128);
-    s1 = sb + (int64_t)((I + f0) / 128) * (H / 128);
+  } else if (kGateUp) {
+    const float* sb = reinterpret_cast<const float*>(a.bank[bank].w13_scale) + ge * (2 * I / 128) * (int64_t)KB;
+    sp = sb + (int64_t)((l == 16 ? f0 : I + f0) / 128) * KB;
   } else {
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.bank[bank].w2) + ge * (int64_t)H * I;
-    const float* sb = reinterpret_cast<const float*>(a.bank[bank].w2_scale) + ge * (H / 128) * (int64_t)(I / 128);
-    w0 = base + (int64_t)(fw + m16) * I + g * 32;
-    s0 = sb + (int64_t)(f0 / 128) * (I / 128);
+    const float* sb = reinterpret_cast<const float*>(a.bank[bank].w2_scale) + ge * (H / 128) * (int64_t)KB;
+    sp = sb + (int64_t)(f0 / 128) * KB;
   }
+  auto issue = [&](int kb) {
+    char* st = ring + (kb % S) * STG;
+    const int64_t o = (int64_t)kb * kF8K;
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) dma16(wp[i] + o, st + (8 * i + wave) * 1024);
+    dma16(ap[0] + o, st + WB + wave * 1024);
+    dma16(ap[1] + o, st + WB + (8 + wave) * 1024);
+    if (l < (kGateUp ? 18 : 17)) dma4(sp + kb, st + WB + ACT + wave * 128);
+  };
   f32x4 acc0[8], acc1[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) { acc0[t] = f32x4{0, 0, 0, 0}; acc1[t] = f32x4{0, 0, 0, 0}; }
-  // prologue: K block 0
-  u32x4 ra[2];
-  float rs = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i]);
-  if (sp) rs = sp[0];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&act[0][aoff[i]]) = ra[i];
-  if (tid < kF8TileM) ascale[0][tid] = rs;
-  i32x8 wa = ld32(w0), wb = kGateUp ? ld32(w1) : wa;
-  __syncthreads();
+  for (int p = 0; p < S - 1; ++p)
+    if (p < KB) issue(p);
+  const int wr0 = wave * 16 + m16;  // this lane's gate (or down) weight row in the tile
   for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    i32x8 na = wa, nb = wb;
-    if (kb + 1 < KB) {
-      const int64_t o = (int64_t)(kb + 1) * kF8K;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + o);
-      if (sp) rs = sp[kb + 1];
-      na = ld32(w0 + o);
-      if (kGateUp) nb = ld32(w1 + o);
+    // block kb has landed once at most (blocks issued after it) * A ops are outstanding
+    if (kb + S - 2 < KB) wait_vmcnt<(S - 2) * A>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kb + S - 1 < KB) issue(kb + S - 1);
+    const char* st = ring + (kb % S) * STG;
+    i32x8 wa, wb;
+    {
+      const u32x4 p0 = *reinterpret_cast<const u32x4*>(st + lds_off(wr0, 2 * g));
+      const u32x4 p1 = *reinterpret_cast<const u32x4*>(st + lds_off(wr0, 2 * g + 1));
+      wa[0] = p0[0]; wa[1] = p0[1]; wa[2] = p0[2]; wa[3] = p0[3];
+      wa[4] = p1[0]; wa[5] = p1[1]; wa[6] = p1[2]; wa[7] = p1[3];
+      if (kGateUp) {
+        const u32x4 q0 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g));
+        const u32x4 q1 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g + 1));
+        wb[0] = q0[0]; wb[1] = q0[1]; wb[2] = q0[2]; wb[3] = q0[3];
+        wb[4] = q1[0]; wb[5] = q1[1]; wb[6] = q1[2]; wb[7] = q1[3];
+      } else {
+        wb = wa;
+      }
     }
-    const float sw0 = s0[kb];
-    const float sw1 = kGateUp ? s1[kb] : 0.0f;
+    const float sw0 = *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 64);
+    const float sw1 = kGateUp ? *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 68) : 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       if (t < ntb) {
-        const i32x8 xb = *reinterpret_cast<const i32x8*>(&act[buf][(t * 16 + m16) * kF8LdsRow + g * 32]);
-        const float sx = ascale[buf][t * 16 + m16];
+        const int r = t * 16 + m16;
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g));
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g + 1));
+        i32x8 xb;
+        xb[0] = x0[0]; xb[1] = x0[1]; xb[2] = x0[2]; xb[3] = x0[3];
+        xb[4] = x1[0]; xb[5] = x1[1]; xb[6] = x1[2]; xb[7] = x1[3];
+        const float sx = *reinterpret_cast<const float*>(st + WB + ACT + t * 128 + m16 * 4);
         const f32x4 z = {0, 0, 0, 0};
         f32x4 p0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, z, 0, 0, 0, 127, 0, 127);
         const float c0 = sw0 * sx;
@@ -849,15 +890,10 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
         }
       }
     }
-    if (kb + 1 < KB) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&act[buf ^ 1][aoff[i]]) = ra[i];
-      if (tid < kF8TileM) ascale[buf ^ 1][tid] = rs;
-    }
-    wa = na;
-    wb = nb;
-    __syncthreads();
   }
+  __syncthreads();
+  float(*red)[kF8TileM] = reinterpret_cast<float(*)[kF8TileM]>(ring);  // [8][128] amax table
+  const int fw = f0 + wave * 16;
   // lane holds D[feature fw + 4g + i][token t*16 + m16]
   if (kGateUp) {
 #pragma unroll
