@@ -95,6 +95,57 @@ def cpu_baseline(cfg, host, n_tokens):
                       f"{dt:.1f} s"}
 
 
+# bytes per stored element (block scales included) of each storage format
+ELEM_BYTES = {"f32": 4.0, "bf16": 2.0, "fp8": 1.0 + 4.0 / (128 * 128), "mxfp4": 0.5 + 1.0 / 32}
+# dense MFMA peak (TFLOP/s) of the product each weight format is computed with: MXFP4 weights
+# are decoded to bf16 in registers and multiplied on the bf16 MFMA
+MFMA_PEAK = {"f32": 157.3, "bf16": BF16_PEAK_TFLOPS, "fp8": 5000.0, "mxfp4": BF16_PEAK_TFLOPS}
+
+
+def ffn_accounting(cfg, touched):
+    """Algorithmic HBM bytes and flops of the grouped gate/up (+SwiGLU) and down launches:
+    every touched expert's weights read once, every routed/shared row's input read once and
+    its output written once; which of HBM or MFMA bounds each launch; the kernel the library
+    picks for it (fp8: k_fp8; MXFP4: k_tiled; bf16 with more than 32 routed rows per expert on
+    average: k_tiled2; otherwise the streaming kernels)."""
+    T, H, I, Is, k = cfg.T, cfg.H, cfg.I, cfg.shared_I, cfg.k
+    rows_r = T * k if cfg.routed else T
+    rows = rows_r + (T if Is else 0)
+    wb = ELEM_BYTES[cfg.wdt]
+    q8 = 1.0 + 4.0 / 128          # an E4M3 code plus its share of a 1 x 128 fp32 scale
+    xb = q8 if cfg.wdt == "fp8" else ELEM_BYTES[cfg.act]
+    hb = q8 if cfg.wdt == "fp8" else (4.0 if cfg.wdt == "f32" else 2.0)
+    h_elems = rows_r * I + (T * Is if Is else 0)
+    w13 = (touched * 2 * I * H + (2 * Is * H if Is else 0)) * wb
+    w2 = (touched * I * H + (Is * H if Is else 0)) * wb
+    fl_gu = 2.0 * (rows_r * H * 2 * I + (T * H * 2 * Is if Is else 0))
+    fl_dn = 2.0 * (rows_r * I * H + (T * Is * H if Is else 0))
+    if cfg.wdt == "fp8":
+        kgu, kdn = "k_fp8<gate/up>", "k_fp8<down>"
+    elif cfg.wdt == "mxfp4":
+        kgu, kdn = "k_tiled<gate/up, MXFP4>", "k_tiled<down, MXFP4>"
+    elif cfg.wdt == "bf16" and rows_r > 32 * cfg.E:
+        kgu, kdn = "k_tiled2<gate/up>", "k_tiled2<down>"
+    else:
+        kgu, kdn = "k_gateup_stream", "k_down_stream"
+    peak = MFMA_PEAK[cfg.wdt]
+
+    def launch(nbytes, flops, kernel):
+        bound = "mfma" if flops / (peak * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"
+        frac_fn = ((lambda t: nbytes / t / 1e9 / HBM_PEAK_GBS) if bound == "hbm"
+                   else (lambda t: flops / t / 1e12 / peak))
+        return {"bytes": nbytes, "flops": flops, "bound": bound, "kernel": kernel,
+                "mfma_peak": peak, "frac_fn": frac_fn}
+
+    return {
+        "gate_up": launch(w13 + rows * H * xb + h_elems * hb, fl_gu, kgu),
+        "down": launch(w2 + h_elems * hb + rows * H * 4.0, fl_dn, kdn),
+        # router weights + x read by the router, output written by the combine
+        "other_bytes": cfg.E * H * ELEM_BYTES[cfg.act] + 2 * T * H * ELEM_BYTES[cfg.act],
+        "router_flops": 2.0 * T * cfg.E * H if cfg.routed else 0.0,
+    }
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
     summary (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE scaled by a plain
@@ -183,17 +234,15 @@ def main():
 
     cnt = counts.cpu().numpy()
     touched = int((cnt > 0).sum())
-    rows = T * k + (T if cfg.shared_I else 0)
-    wb = 2 if cfg.wdt == "bf16" else 4
-    gu_bytes = (touched * 2 * cfg.I * H + (2 * cfg.shared_I * H if cfg.shared_I else 0)) * wb
-    gu_bytes += rows * H * wb + rows * cfg.I * wb
+    acct = ffn_accounting(cfg, touched)
+    g = acct["gate_up"]
     gu_s = stage_ms["gate_up"] / 1e3
-    achieved = gu_bytes / gu_s / 1e9
-    dn_bytes = (touched * cfg.I * H + (cfg.shared_I * H if cfg.shared_I else 0)) * wb
-    dn_bytes += rows * cfg.I * wb + rows * H * wb
-    layer_flops = (6.0 * H * cfg.I * T * k + (6.0 * H * cfg.shared_I * T if cfg.shared_I else 0)
-                   + 2.0 * T * E * H)
-    layer_bytes = gu_bytes + dn_bytes + E * H * wb + 2 * T * H * wb
+    if g["bound"] == "hbm":
+        achieved, peak, unit = g["bytes"] / gu_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = g["flops"] / gu_s / 1e12, g["mfma_peak"], "TFLOP/s"
+    layer_bytes = acct["gate_up"]["bytes"] + acct["down"]["bytes"] + acct["other_bytes"]
+    layer_flops = acct["gate_up"]["flops"] + acct["down"]["flops"] + acct["router_flops"]
 
     cpu = None
     if not args.no_cpu:
@@ -219,11 +268,13 @@ def main():
                    "tokens": T, "experts_touched": touched,
                    "stage_ms": {s_: round(v, 5) for s_, v in stage_ms.items()},
                    "layer_algorithmic_bytes": layer_bytes, "layer_flops": layer_flops,
-                   "layer_hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": "grouped gate/up + SwiGLU (k_gateup_stream)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(cfg.name),
-                     "algorithmic_bytes_per_launch": gu_bytes,
+                   "layer_hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                   "down_frac": acct["down"]["frac_fn"](stage_ms["down"] / 1e3)},
+        "roofline": {"bound": g["bound"], "kernel": f"grouped gate/up + SwiGLU ({g['kernel']})",
+                     "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+                     "traffic": measured_traffic(cfg.name),
+                     "algorithmic_bytes_per_launch": g["bytes"],
+                     "algorithmic_flops_per_launch": g["flops"],
                      "avg_launch_ms": stage_ms["gate_up"]},
         "cpu_baseline": cpu,
     }

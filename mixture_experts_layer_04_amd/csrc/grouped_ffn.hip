@@ -240,21 +240,8 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
 #ifndef MOE_TILED_TN
 #define MOE_TILED_TN 4
 #endif
-#ifndef MOE_TILED_EXPERT_ORDER
-#define MOE_TILED_EXPERT_ORDER 0
-#endif
 constexpr int kTTM = MOE_TILED_TM, kTTN = MOE_TILED_TN;
 constexpr int kTBM = 32 * kTTM, kTBN = 32 * kTTN, kTBK = 64;
-
-// Workgroup id remap so that consecutive logical ids run on the same XCD (ids are dealt
-// to the 8 XCDs round-robin), letting neighbours share their A tile in that XCD's L2.
-#ifndef MOE_XCD_REMAP
-#define MOE_XCD_REMAP 0
-#endif
-__device__ __forceinline__ int xcd_remap(int bid, int grid) {
-  if (!MOE_XCD_REMAP || grid % 8) return bid;
-  return (bid % 8) * (grid / 8) + bid / 8;
-}
 
 __device__ __forceinline__ float e8m0_f32(uint32_t c) {
   if (c == 0xFFu) return __uint_as_float(0x7FC00000u);
@@ -282,19 +269,11 @@ __global__ void __launch_bounds__(256, 1) k_tiled(FfnArgs a, int nb_per_tile) {
   constexpr int CA = BM / 32, CB = BN / 32;  // 16-B chunks per thread per K block
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  // Logical order: expert-major; inside an expert, weight block nb major and row tile
-  // minor, so all row tiles of an expert stream each weight block together (one weight
-  // stream per expert in the XCD's L2) while their activation tiles stay resident.
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int t0 = bid / nb_per_tile;
-  if (t0 >= *a.ntiles) return;
-  const Tile head = a.tiles[t0];
-  int tile_id = t0, nb = bid - t0 * nb_per_tile;
-  if (MOE_TILED_EXPERT_ORDER) {
-    const int local = bid - head.first * nb_per_tile;
-    nb = local / head.ntile;
-    tile_id = head.first + (local - nb * head.ntile);
-  }
+  // Tile-major order: the nb_per_tile weight blocks of a row tile are consecutive
+  // workgroups, so they read the tile's activation rows at about the same time.
+  const int tile_id = blockIdx.x / nb_per_tile;
+  if (tile_id >= *a.ntiles) return;
+  const int nb = blockIdx.x - tile_id * nb_per_tile;
   const Tile tl = a.tiles[tile_id];
   const int bank = tl.group < a.E ? 0 : 1;
   const int64_t ge = tl.group < a.E ? tl.group : 0;
@@ -482,17 +461,18 @@ __global__ void __launch_bounds__(256, 1) k_tiled(FfnArgs a, int nb_per_tile) {
 #ifndef MOE_T2_WGN
 #define MOE_T2_WGN 2
 #endif
-#ifndef MOE_T2_ORDER
-#define MOE_T2_ORDER 0
-#endif
 #ifndef MOE_T2_STAGES
 #define MOE_T2_STAGES 2
+#endif
+#ifndef MOE_T2_MX_STAGES
+#define MOE_T2_MX_STAGES 3
 #endif
 #ifndef MOE_T2_WAVES_PER_SIMD
 #define MOE_T2_WAVES_PER_SIMD 2
 #endif
 constexpr int kT2Threads = 64 * MOE_T2_WGM * MOE_T2_WGN;
 constexpr int kT2M = MOE_T2_WGM * 16 * MOE_T2_TM, kT2N = MOE_T2_WGN * 16 * MOE_T2_TN;
+static_assert(kT2M == kTBM, "the MXFP4 tile list serves both tiled kernels");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -500,6 +480,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 // target builtin must not appear in code the host pass instantiates).
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+// 4 B per lane from global memory into LDS at lds + 4 * lane (device-only wrapper).
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+
+// Eight E2M1 values (one 32-bit word, low nibble first) times their E8M0 block scale, as
+// the bf16 fragment of one MFMA k-step (v_cvt_scalef32_pk_bf16_fp4 is exact: every
+// E2M1 value times a power of two in range is a bf16).
+__device__ __forceinline__ bf16x8 e2m1x8_bf16(uint32_t w, float scale) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
@@ -511,29 +507,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Workgroup of WGM x WGN wavefronts; each wavefront computes (16 TM) x (16 TN).
-template <int TM, int TN, int WGM, int WGN, int S, bool kGateUp, bool kYF32>
+// kMX: MXFP4 weights. A K block of a weight row is then 32 B of E2M1 codes plus 2 E8M0
+// scale bytes; the ring stages the codes (32 B a row: the 8-B quarter u of row r at
+// quarter u ^ 2 ((r >> 3) & 1), which spreads the 64-bit fragment reads of 16 rows over
+// all banks) and 4 scale bytes a row (those of K blocks kt & ~1 and (kt & ~1) + 1, one
+// aligned dword), and fragments are decoded to bf16 in registers as they are read.
+template <int TM, int TN, int WGM, int WGN, int S, bool kGateUp, bool kYF32, bool kMX>
 __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled2(FfnArgs a, int nb_per_tile) {
   constexpr int NW = WGM * WGN;
   constexpr int BM = WGM * 16 * TM, BN = WGN * 16 * TN;
-  constexpr int STAGE = (BM + BN) * 128;
+  constexpr int BSTAGE = kMX ? BN * 32 + BN * 4 : BN * 128;  // weight bytes of a stage
+  constexpr int STAGE = BM * 128 + BSTAGE;
   constexpr int RPI = NW * 8;                  // LDS rows filled per DMA instruction round
-  constexpr int CA = BM / RPI, CB = BN / RPI;  // DMA instructions per thread per K block
+  constexpr int CA = BM / RPI;                 // DMA instructions per thread per K block: A,
+  constexpr int CB = kMX ? BN * 32 / (1024 * NW) : BN / RPI;  // B,
+  constexpr int CS = kMX ? 1 : 0;                              // MXFP4 scales
+  constexpr int OPS = CA + CB + CS;
   static_assert(BM % RPI == 0 && BN % RPI == 0 && BM % 16 == 0, "tile rows per DMA round");
+  static_assert(!kMX || (BN * 32 % (1024 * NW) == 0 && BN == 32 * NW), "MXFP4 DMA rounds");
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int t0 = bid / nb_per_tile;
-  if (t0 >= *a.ntiles) return;
-  const Tile head = a.tiles[t0];
-  int nb, tidx;
-  if (MOE_T2_ORDER) {
-    const int local = bid - head.first * nb_per_tile;
-    nb = local / head.ntile;
-    tidx = head.first + (local - nb * head.ntile);
-  } else {
-    nb = bid - t0 * nb_per_tile;
-    tidx = t0;
-  }
+  // tile-major order, as in k_tiled
+  const int tidx = blockIdx.x / nb_per_tile;
+  if (tidx >= *a.ntiles) return;
+  const int nb = blockIdx.x - tidx * nb_per_tile;
   const Tile tl = a.tiles[tidx];
   const int bank = tl.group < a.E ? 0 : 1;
   const int64_t ge = tl.group < a.E ? tl.group : 0;
@@ -543,11 +540,24 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
   const int fpb = kGateUp ? BN / 2 : BN;
   const int f0 = nb * fpb;
   if (f0 >= (kGateUp ? I : H)) return;
+  const int64_t wrows = kGateUp ? 2 * I : H;  // rows of this expert's weight matrix
+  const int64_t wrow_bytes = kMX ? K / 2 : K * 2;
   const char* wbase = reinterpret_cast<const char*>(kGateUp ? a.bank[bank].w13 : a.bank[bank].w2) +
-                      ge * (int64_t)(kGateUp ? 2 * I : H) * K * 2;
+                      ge * wrows * wrow_bytes;
+  // weight row of B-tile row r (gate/up: each N-wavefront block of 16 TN rows holds the
+  // gate and up rows of 8 TN features, alternating by 16)
+  auto weight_row = [&](int r) {
+    if (kGateUp) {
+      const int blk = r / (16 * TN), jj = r % (16 * TN), nt = jj >> 4, within = jj & 15;
+      const int feat = f0 + blk * (8 * TN) + (nt >> 1) * 16 + within;
+      return (nt & 1) ? I + feat : feat;
+    }
+    return f0 + r;
+  };
   // DMA instruction i of wavefront w fills 1-KB block q = NW i + w of the A (then B) tile
   const char* ag[CA];
   const char* bg[CB];
+  const uint8_t* sg = nullptr;
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
     int r, cc;
@@ -563,27 +573,37 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
   }
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
-    int r, cc;
-    dma_slot(NW * i + wave, l, &r, &cc);
-    const int col = cc * 16;
-    int wrow;
-    if (kGateUp) {
-      // N-wavefront block of 16 TN rows: gate and up rows of 8 TN features, by 16
-      const int blk = r / (16 * TN), jj = r % (16 * TN), nt = jj >> 4, within = jj & 15;
-      const int feat = f0 + blk * (8 * TN) + (nt >> 1) * 16 + within;
-      wrow = (nt & 1) ? I + feat : feat;
+    if (kMX) {
+      // lane l: row 32 q + l / 2, physical 16-B half l % 2 of its 32-B slice
+      const int r = 32 * (NW * i + wave) + (l >> 1);
+      const int lh = (l & 1) ^ ((r >> 3) & 1);
+      bg[i] = wbase + weight_row(r) * wrow_bytes + lh * 16;
     } else {
-      wrow = f0 + r;
+      int r, cc;
+      dma_slot(NW * i + wave, l, &r, &cc);
+      bg[i] = wbase + weight_row(r) * wrow_bytes + cc * 16;
     }
-    bg[i] = wbase + (int64_t)wrow * K * 2 + col;
+  }
+  if (kMX) {
+    // lanes 0..31 of wavefront w fetch the scale dword of B-tile row 32 w + lane
+    const uint8_t* sbase = reinterpret_cast<const uint8_t*>(kGateUp ? a.bank[bank].w13_scale
+                                                                    : a.bank[bank].w2_scale) +
+                           ge * wrows * (K / 32);
+    sg = sbase + weight_row(32 * wave + (l & 31)) * (int64_t)(K / 32);
   }
   auto issue = [&](int kt, int stage) {
     const int64_t o = (int64_t)kt * 128;
     char* st = smem + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < CA; ++i) dma16(ag[i] + o, st + (NW * i + wave) * 1024);
+    if (kMX) {
 #pragma unroll
-    for (int i = 0; i < CB; ++i) dma16(bg[i] + o, st + BM * 128 + (NW * i + wave) * 1024);
+      for (int i = 0; i < CB; ++i) dma16(bg[i] + (int64_t)kt * 32, st + BM * 128 + (NW * i + wave) * 1024);
+      if (l < 32) dma4(sg + (kt & ~1) * 2, st + BM * 128 + BN * 32 + wave * 128);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CB; ++i) dma16(bg[i] + o, st + BM * 128 + (NW * i + wave) * 1024);
+    }
   };
   const int wm = wave % WGM, wn = wave / WGM;
   const int m16 = l & 15, g = l >> 4;
@@ -602,13 +622,28 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
   for (int p = 0; p < S - 1; ++p)
     if (p < KT) issue(p, p);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * (CA + CB)>();
+    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * OPS>();
     else wait_vmcnt<0>();
     // A plain barrier, not __syncthreads(): its fence would wait for every outstanding
     // DMA of the ring. The wait above already covers this thread's part of block kt.
     __builtin_amdgcn_s_barrier();
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     const char* cur = smem + (kt % S) * STAGE;
+    // MXFP4: this lane's 16 codes (elements 16 g .. 16 g + 15 of the K block) and scale
+    uint2 wq[kMX ? TN : 1];
+    float wsc[kMX ? TN : 1];
+    if (kMX) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const char* rb = cur + BM * 128 + brow[t] * 32;
+        // two 32-bit reads: with one 64-bit read the compiler makes it wait for all DMA
+        const char* q = rb + 8 * (g ^ (((brow[t] >> 3) & 1) << 1));
+        wq[t].x = *reinterpret_cast<const uint32_t*>(q);
+        wq[t].y = *reinterpret_cast<const uint32_t*>(q + 4);
+        wsc[t] = e8m0_f32(*reinterpret_cast<const uint8_t*>(cur + BM * 128 + BN * 32 + 4 * brow[t] +
+                                                             (kt & 1) * 2 + (g >> 1)));
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 fa[TM], fb[TN];
@@ -617,8 +652,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
       for (int t = 0; t < TM; ++t)
         fa[t] = *reinterpret_cast<const bf16x8*>(cur + lds_off(arow[t], c));
 #pragma unroll
-      for (int t = 0; t < TN; ++t)
-        fb[t] = *reinterpret_cast<const bf16x8*>(cur + BM * 128 + lds_off(brow[t], c));
+      for (int t = 0; t < TN; ++t) {
+        if (kMX) fb[t] = e2m1x8_bf16(ks ? wq[t].y : wq[t].x, wsc[t]);
+        else fb[t] = *reinterpret_cast<const bf16x8*>(cur + BM * 128 + lds_off(brow[t], c));
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -741,11 +778,6 @@ __device__ __forceinline__ i32x8 ld32(const void* p) {
   r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
   r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
   return r;
-}
-
-// 4 B per lane from global memory into LDS at lds + 4 * lane (device-only wrapper).
-__device__ __forceinline__ void dma4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
 template <bool kGateUp>
@@ -992,14 +1024,29 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
   dim3 blk(256);
   if (a.tile_m == kT2M && a.wdt == MOE_BF16) {
     const int nb_gu = a.I_max / (kT2N / 2), nb_dn = a.H / kT2N;
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, true, false>), dim3(a.max_tiles * nb_gu), dim3(kT2Threads), 0, s, a, nb_gu);
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, true, false, false>), dim3(a.max_tiles * nb_gu), dim3(kT2Threads), 0, s, a, nb_gu);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
     if (yf32)
-      hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, true>), dim3(a.max_tiles * nb_dn), dim3(kT2Threads), 0, s, a, nb_dn);
+      hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, true, false>), dim3(a.max_tiles * nb_dn), dim3(kT2Threads), 0, s, a, nb_dn);
     else
-      hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, false>), dim3(a.max_tiles * nb_dn), dim3(kT2Threads), 0, s, a, nb_dn);
+      hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, false, false>), dim3(a.max_tiles * nb_dn), dim3(kT2Threads), 0, s, a, nb_dn);
+    return hipGetLastError();
+  }
+  // MXFP4 through the DMA kernel when every weight row's scale bytes are dword aligned
+  // (K % 128 for both products)
+  if (a.tile_m == kT2M && a.wdt == MOE_MXFP4 && a.H % kT2N == 0 && a.bank[0].I % 128 == 0 &&
+      (!a.has_shared || a.bank[1].I % 128 == 0)) {
+    const int nb_gu = a.I_max / (kT2N / 2), nb_dn = a.H / kT2N;
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES, true, false, true>), dim3(a.max_tiles * nb_gu), dim3(kT2Threads), 0, s, a, nb_gu);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
+    if (yf32)
+      hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES, false, true, true>), dim3(a.max_tiles * nb_dn), dim3(kT2Threads), 0, s, a, nb_dn);
+    else
+      hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES, false, false, true>), dim3(a.max_tiles * nb_dn), dim3(kT2Threads), 0, s, a, nb_dn);
     return hipGetLastError();
   }
   if (a.tile_m == kTBM) {

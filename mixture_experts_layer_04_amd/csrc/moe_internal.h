@@ -38,9 +38,7 @@ struct Tile {
   int32_t group;
   int32_t row0;
   int32_t nrows;
-  int32_t first;   // index of the group's first tile in the list
-  int32_t ntile;   // number of tiles of the group
-  int32_t pad[3];
+  int32_t pad[5];  // 32-byte entries
 };
 
 // Upper bound of the tile count for n_rows rows in n_groups groups with tiles of m rows.

@@ -98,9 +98,7 @@ __global__ void __launch_bounds__(kScanThreads) k_scan(int32_t* __restrict__ cnt
       tl.group = e;
       tl.row0 = row0 + i * tile_m;
       tl.nrows = min(tile_m, rows - i * tile_m);
-      tl.first = toff;
-      tl.ntile = nt;
-      tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
+      tl.pad[0] = tl.pad[1] = tl.pad[2] = tl.pad[3] = tl.pad[4] = 0;
       tiles[toff + i] = tl;
     }
     if (e == 0) *ntiles = ntot;
@@ -163,9 +161,7 @@ __global__ void __launch_bounds__(kScanThreads) k_tiles_from_offsets(const int32
     tl.group = e;
     tl.row0 = row0 + i * tile_m;
     tl.nrows = min(tile_m, rows - i * tile_m);
-    tl.first = toff;
-    tl.ntile = nt;
-    tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
+    tl.pad[0] = tl.pad[1] = tl.pad[2] = tl.pad[3] = tl.pad[4] = 0;
     tiles[toff + i] = tl;
   }
   if (e == 0) *ntiles = ntot;

@@ -33,7 +33,12 @@ SMALL = [
               weight_seed=15),
     MoEConfig("bf16_f32_out_k16", T=70, H=256, E=40, k=16, I=128, score="sigmoid", use_bias=True,
               scale=2.5, out="f32", seed=16, weight_seed=16),
-    # more than 32 rows per expert: the LDS-tiled grouped GEMM, with ragged 128-row tiles
+    # more than 32 rows per expert: the LDS-tiled grouped GEMMs, with ragged 128-row tiles;
+    # H % 256 and I % 128 select the 128 x 256 kernel, other shapes the 128 x 128 one
+    MoEConfig("bf16_t3_sigmoid_shared", T=900, H=512, E=10, k=3, I=256, score="sigmoid",
+              use_bias=True, scale=2.5, shared_I=128, seed=19, weight_seed=19),
+    MoEConfig("bf16_t3_softmax_f32out", T=1200, H=768, E=5, k=2, I=384, score="softmax",
+              out="f32", seed=20, weight_seed=20),
     MoEConfig("bf16_tiled_sigmoid_shared", T=600, H=256, E=12, k=3, I=192, score="sigmoid",
               use_bias=True, scale=2.5, shared_I=128, seed=17, weight_seed=17),
     MoEConfig("bf16_tiled_softmax_f32out", T=1000, H=384, E=6, k=2, I=128, score="softmax",
@@ -245,6 +250,9 @@ MX_ROWS = [
               wdt="mxfp4", out="bf16", seed=51, weight_seed=51, dirichlet_alpha=0.5),
     MoEConfig("mxfp4_rows_f32out_ragged", T=257, H=384, E=9, k=1, I=192, score="none", act="bf16",
               wdt="mxfp4", out="f32", seed=52, weight_seed=52, dirichlet_alpha=0.5),
+    # H % 128 and I % 128: the DMA kernel that stages the E2M1 codes and decodes in registers
+    MoEConfig("mxfp4_rows_dma_ragged", T=1500, H=512, E=5, k=1, I=256, score="none", act="bf16",
+              wdt="mxfp4", out="f32", seed=54, weight_seed=54, dirichlet_alpha=0.5),
 ]
 
 
