@@ -106,7 +106,7 @@ def ffn_accounting(cfg, touched):
     """Algorithmic HBM bytes and flops of the grouped gate/up (+SwiGLU) and down launches:
     every touched expert's weights read once, every routed/shared row's input read once and
     its output written once; which of HBM or MFMA bounds each launch; the kernel the library
-    picks for it (fp8: k_fp8; MXFP4: k_tiled; bf16 with more than 32 routed rows per expert on
+    picks for it (fp8: k_fp8; MXFP4, and bf16 with more than 32 routed rows per expert on
     average: k_tiled2; otherwise the streaming kernels)."""
     T, H, I, Is, k = cfg.T, cfg.H, cfg.I, cfg.shared_I, cfg.k
     rows_r = T * k if cfg.routed else T
@@ -123,7 +123,7 @@ def ffn_accounting(cfg, touched):
     if cfg.wdt == "fp8":
         kgu, kdn = "k_fp8<gate/up>", "k_fp8<down>"
     elif cfg.wdt == "mxfp4":
-        kgu, kdn = "k_tiled<gate/up, MXFP4>", "k_tiled<down, MXFP4>"
+        kgu, kdn = "k_tiled2<gate/up, MXFP4>", "k_tiled2<down, MXFP4>"
     elif cfg.wdt == "bf16" and rows_r > 32 * cfg.E:
         kgu, kdn = "k_tiled2<gate/up>", "k_tiled2<down>"
     else:

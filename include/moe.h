@@ -67,7 +67,7 @@ typedef enum {
  * FP8_E4M3: codes as above; w13_scale f32 [E, 2I/128, H/128], w2_scale f32 [E, H/128, I/128]
  *           (one scale per 128 x 128 block; value = code * scale). H, I multiples of 128.
  * MXFP4:    w13 bytes [E, 2I, H/2], w2 bytes [E, H, I/2]; w13_scale u8 [E, 2I, H/32],
- *           w2_scale u8 [E, H, I/32] (value = e2m1 * 2^(scale - 127)). H, I multiples of 32.
+ *           w2_scale u8 [E, H, I/32] (value = e2m1 * 2^(scale - 127)). H, I multiples of 128.
  * F32/BF16: no scales (NULL). H, I multiples of 64.
  * The fp8 and MXFP4 expert formats are the FP8/FP4 grouped GEMM inputs of "GC-MoE:
  * Overlapping Expert-Parallel Token Dispatch with FP8/FP4 Grouped GEMM via CUDA Green

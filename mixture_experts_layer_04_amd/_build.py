@@ -6,7 +6,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "ffn_stream.hip",
+           "ffn_tiled.hip", "ffn_fp8.hip", "combine.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,0 +1,60 @@
+// Device helpers and constants shared by the grouped-FFN kernel files (ffn_stream.hip,
+// ffn_tiled.hip, ffn_fp8.hip), and the launcher each of them gives grouped_ffn.hip.
+// Internal; not part of the ABI.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Rows per tile of each kernel family; the tile list of a call is built for one of them.
+constexpr int kStreamTileM = 16;   // streaming kernels (few rows per expert)
+constexpr int kTiledM = 128;       // LDS-tiled bf16 / MXFP4 kernel
+constexpr int kTiledN = 128;       // its weight rows per workgroup (gate/up: 64 features)
+constexpr int kF8TileM = 128;      // fp8 kernel
+constexpr int kF8Feat = 128;       // fp8 output features per workgroup = one scale block
+constexpr int kF8K = 128;          // fp8 K block = one scale block
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// LDS byte offset of logical 16-B chunk c of tile row r (each 16-row group takes
+// eight 256-B lines, row j and row 8 + j share line j, chunks XOR-swizzled by row & 7;
+// ffn_tiled.hip describes it).
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return (r >> 4) * 2048 + (r & 7) * 256 + ((r >> 3) & 1) * 128 + ((c ^ (r & 7)) << 4);
+}
+// Row and logical chunk that lane l of 1-KB DMA block q writes.
+__device__ __forceinline__ void dma_slot(int q, int l, int* r, int* c) {
+  const int half = (l >> 3) & 1;
+  *r = (q >> 1) * 16 + (q & 1) * 4 + (l >> 4) + 8 * half;
+  *c = (l & 7) ^ (*r & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 B per lane from global memory into LDS at lds + 16 * lane (a device-only wrapper: the
+// target builtin must not appear in code the host pass instantiates).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+// 4 B per lane from global memory into LDS at lds + 4 * lane (device-only wrapper).
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Launchers of the kernel families (FfnArgs as set up by launch_grouped_ffn; mid_event,
+// if not null, is recorded between the gate/up and the down launches).
+hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);
+hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);
+hipError_t launch_ffn_fp8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);
+
+}  // namespace moe

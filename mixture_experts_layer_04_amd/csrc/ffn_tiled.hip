@@ -1,0 +1,277 @@
+// LDS-tiled grouped-FFN kernel (many rows per expert, e.g. prefill), for bf16 and MXFP4
+// weights: the grouped GEMM with fused SwiGLU of "GC-MoE: Overlapping Expert-Parallel
+// Token Dispatch with FP8/FP4 Grouped GEMM via CUDA Green Contexts" (key_changes, fourth
+// item), planned for gfx950.
+//
+// A workgroup computes a tile of 128 rows x 128 weight rows (gate/up: the gate and up rows
+// of 64 features, alternating by 16, so that each lane holds gate and up of the same
+// (row, feature) and SwiGLU is applied in registers) with 4 wavefronts in a 2 x 2 grid,
+// each (16 TM) x (16 TN) with v_mfma_f32_16x16x32_bf16. The K blocks (64 elements) go
+// from global memory straight into LDS with global_load_lds (no register staging),
+// through an S-stage ring, so that each block has S-1 blocks of MFMA work to hide
+// behind. A lane's fragment of a K block is the 32 contiguous bytes at 32 (lane / 16)
+// in both operands (K index 16 (lane / 16) + 8 ks + j for k-step ks).
+//
+// LDS layout of a K block (128 B per row): each 16-row group takes 2 KB = eight 256-B
+// lines; line j holds row j in its low 128 B and row 8 + j in its high 128 B, and the
+// 16-B chunk c of row r sits at chunk c ^ (r & 7). Measured on MI355X, this lets the
+// fragment reads of 16 consecutive rows at one chunk run at the full LDS rate
+// (~250 B/clk/CU) where padded or plainly swizzled rows reach half of it. A wavefront's
+// DMA writes 1 KB contiguously (16 B per lane, lane order), i.e. 4 + 4 rows of a group,
+// and each lane's global address absorbs the layout.
+#include "ffn_common.h"
+
+namespace moe {
+namespace {
+
+#ifndef MOE_T2_TM
+#define MOE_T2_TM 4
+#endif
+#ifndef MOE_T2_TN
+#define MOE_T2_TN 4
+#endif
+#ifndef MOE_T2_WGM
+#define MOE_T2_WGM 2
+#endif
+#ifndef MOE_T2_WGN
+#define MOE_T2_WGN 2
+#endif
+#ifndef MOE_T2_STAGES
+#define MOE_T2_STAGES 2
+#endif
+#ifndef MOE_T2_MX_STAGES
+#define MOE_T2_MX_STAGES 3
+#endif
+#ifndef MOE_T2_WAVES_PER_SIMD
+#define MOE_T2_WAVES_PER_SIMD 2
+#endif
+constexpr int kT2Threads = 64 * MOE_T2_WGM * MOE_T2_WGN;
+constexpr int kT2M = MOE_T2_WGM * 16 * MOE_T2_TM, kT2N = MOE_T2_WGN * 16 * MOE_T2_TN;
+static_assert(kT2M == kTiledM && kT2N == kTiledN, "tile shape of the tile list");
+
+__device__ __forceinline__ float e8m0_f32(uint32_t c) {
+  if (c == 0xFFu) return __uint_as_float(0x7FC00000u);
+  if (c == 0u) return __uint_as_float(0x00400000u);  // 2^-127
+  return __uint_as_float(c << 23);
+}
+
+// Eight E2M1 values (one 32-bit word, low nibble first) times their E8M0 block scale, as
+// the bf16 fragment of one MFMA k-step (v_cvt_scalef32_pk_bf16_fp4 is exact: every
+// E2M1 value times a power of two in range is a bf16).
+__device__ __forceinline__ bf16x8 e2m1x8_bf16(uint32_t w, float scale) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Workgroup of WGM x WGN wavefronts; each wavefront computes (16 TM) x (16 TN).
+// kMX: MXFP4 weights. A K block of a weight row is then 32 B of E2M1 codes plus 2 E8M0
+// scale bytes; the ring stages the codes (32 B a row: the 8-B quarter u of row r at
+// quarter u ^ 2 ((r >> 3) & 1), which spreads the 64-bit fragment reads of 16 rows over
+// all banks) and 4 scale bytes a row (those of K blocks kt & ~1 and (kt & ~1) + 1, one
+// aligned dword), and fragments are decoded to bf16 in registers as they are read.
+template <int TM, int TN, int WGM, int WGN, int S, bool kGateUp, bool kYF32, bool kMX>
+__global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled2(FfnArgs a, int nb_per_tile) {
+  constexpr int NW = WGM * WGN;
+  constexpr int BM = WGM * 16 * TM, BN = WGN * 16 * TN;
+  constexpr int BSTAGE = kMX ? BN * 32 + BN * 4 : BN * 128;  // weight bytes of a stage
+  constexpr int STAGE = BM * 128 + BSTAGE;
+  constexpr int RPI = NW * 8;                  // LDS rows filled per DMA instruction round
+  constexpr int CA = BM / RPI;                 // DMA instructions per thread per K block: A,
+  constexpr int CB = kMX ? BN * 32 / (1024 * NW) : BN / RPI;  // B,
+  constexpr int CS = kMX ? 1 : 0;                              // MXFP4 scales
+  constexpr int OPS = CA + CB + CS;
+  static_assert(BM % RPI == 0 && BN % RPI == 0 && BM % 16 == 0, "tile rows per DMA round");
+  static_assert(!kMX || (BN * 32 % (1024 * NW) == 0 && BN == 32 * NW), "MXFP4 DMA rounds");
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  // tile-major order, as in k_tiled
+  const int tidx = blockIdx.x / nb_per_tile;
+  if (tidx >= *a.ntiles) return;
+  const int nb = blockIdx.x - tidx * nb_per_tile;
+  const Tile tl = a.tiles[tidx];
+  const int bank = tl.group < a.E ? 0 : 1;
+  const int64_t ge = tl.group < a.E ? tl.group : 0;
+  const int I = a.bank[bank].I;
+  const int H = a.H;
+  const int K = kGateUp ? H : I;
+  const int fpb = kGateUp ? BN / 2 : BN;
+  const int f0 = nb * fpb;
+  if (f0 >= (kGateUp ? I : H)) return;
+  const int64_t wrows = kGateUp ? 2 * I : H;  // rows of this expert's weight matrix
+  const int64_t wrow_bytes = kMX ? K / 2 : K * 2;
+  const char* wbase = reinterpret_cast<const char*>(kGateUp ? a.bank[bank].w13 : a.bank[bank].w2) +
+                      ge * wrows * wrow_bytes;
+  // weight row of B-tile row r (gate/up: each N-wavefront block of 16 TN rows holds the
+  // gate and up rows of 8 TN features, alternating by 16)
+  auto weight_row = [&](int r) {
+    if (kGateUp) {
+      const int blk = r / (16 * TN), jj = r % (16 * TN), nt = jj >> 4, within = jj & 15;
+      const int feat = f0 + blk * (8 * TN) + (nt >> 1) * 16 + within;
+      return (nt & 1) ? I + feat : feat;
+    }
+    return f0 + r;
+  };
+  // DMA instruction i of wavefront w fills 1-KB block q = NW i + w of the A (then B) tile
+  const char* ag[CA];
+  const char* bg[CB];
+  const uint8_t* sg = nullptr;
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    int r, cc;
+    dma_slot(NW * i + wave, l, &r, &cc);
+    const int col = cc * 16;
+    const int grow = tl.row0 + (r < tl.nrows ? r : tl.nrows - 1);
+    if (kGateUp) {
+      const int64_t src = a.a_rowmap ? a.a_rowmap[grow] : grow;
+      ag[i] = reinterpret_cast<const char*>(a.a) + src * (int64_t)H * 2 + col;
+    } else {
+      ag[i] = reinterpret_cast<const char*>(a.h) + (int64_t)grow * a.I_max * 2 + col;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    if (kMX) {
+      // lane l: row 32 q + l / 2, physical 16-B half l % 2 of its 32-B slice
+      const int r = 32 * (NW * i + wave) + (l >> 1);
+      const int lh = (l & 1) ^ ((r >> 3) & 1);
+      bg[i] = wbase + weight_row(r) * wrow_bytes + lh * 16;
+    } else {
+      int r, cc;
+      dma_slot(NW * i + wave, l, &r, &cc);
+      bg[i] = wbase + weight_row(r) * wrow_bytes + cc * 16;
+    }
+  }
+  if (kMX) {
+    // lanes 0..31 of wavefront w fetch the scale dword of B-tile row 32 w + lane
+    const uint8_t* sbase = reinterpret_cast<const uint8_t*>(kGateUp ? a.bank[bank].w13_scale
+                                                                    : a.bank[bank].w2_scale) +
+                           ge * wrows * (K / 32);
+    sg = sbase + weight_row(32 * wave + (l & 31)) * (int64_t)(K / 32);
+  }
+  auto issue = [&](int kt, int stage) {
+    const int64_t o = (int64_t)kt * 128;
+    char* st = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) dma16(ag[i] + o, st + (NW * i + wave) * 1024);
+    if (kMX) {
+#pragma unroll
+      for (int i = 0; i < CB; ++i) dma16(bg[i] + (int64_t)kt * 32, st + BM * 128 + (NW * i + wave) * 1024);
+      if (l < 32) dma4(sg + (kt & ~1) * 2, st + BM * 128 + BN * 32 + wave * 128);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CB; ++i) dma16(bg[i] + o, st + BM * 128 + (NW * i + wave) * 1024);
+    }
+  };
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int m16 = l & 15, g = l >> 4;
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  const int KT = K / 64;  // 64-element K blocks (128 B of bf16 a row)
+  int arow[TM], brow[TN];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) arow[t] = wm * (16 * TM) + t * 16 + m16;
+#pragma unroll
+  for (int t = 0; t < TN; ++t) brow[t] = wn * (16 * TN) + t * 16 + m16;
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < KT) issue(p, p);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * OPS>();
+    else wait_vmcnt<0>();
+    // A plain barrier, not __syncthreads(): its fence would wait for every outstanding
+    // DMA of the ring. The wait above already covers this thread's part of block kt.
+    __builtin_amdgcn_s_barrier();
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    const char* cur = smem + (kt % S) * STAGE;
+    // MXFP4: this lane's 16 codes (elements 16 g .. 16 g + 15 of the K block) and scale
+    uint2 wq[kMX ? TN : 1];
+    float wsc[kMX ? TN : 1];
+    if (kMX) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const char* rb = cur + BM * 128 + brow[t] * 32;
+        // two 32-bit reads: with one 64-bit read the compiler makes it wait for all DMA
+        const char* q = rb + 8 * (g ^ (((brow[t] >> 3) & 1) << 1));
+        wq[t].x = *reinterpret_cast<const uint32_t*>(q);
+        wq[t].y = *reinterpret_cast<const uint32_t*>(q + 4);
+        wsc[t] = e8m0_f32(*reinterpret_cast<const uint8_t*>(cur + BM * 128 + BN * 32 + 4 * brow[t] +
+                                                             (kt & 1) * 2 + (g >> 1)));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[TM], fb[TN];
+      const int c = 2 * g + ks;  // logical 16-B chunk
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        fa[t] = *reinterpret_cast<const bf16x8*>(cur + lds_off(arow[t], c));
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        if (kMX) fb[t] = e2m1x8_bf16(ks ? wq[t].y : wq[t].x, wsc[t]);
+        else fb[t] = *reinterpret_cast<const bf16x8*>(cur + BM * 128 + lds_off(brow[t], c));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < TM; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = wm * (16 * TM) + mt * 16 + 4 * g + i;
+      if (rl >= tl.nrows) continue;
+      const int64_t row = tl.row0 + rl;
+      if (kGateUp) {
+#pragma unroll
+        for (int p = 0; p < TN / 2; ++p) {
+          const int feat = f0 + wn * (8 * TN) + p * 16 + m16;
+          const float hv = silu_mul(acc[mt][2 * p][i], acc[mt][2 * p + 1][i]);
+          reinterpret_cast<uint16_t*>(a.h)[row * a.I_max + feat] = f32_to_bf16(hv);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < TN; ++nt) {
+          const int64_t o = row * H + f0 + wn * (16 * TN) + nt * 16 + m16;
+          if (kYF32) reinterpret_cast<float*>(a.y)[o] = acc[mt][nt][i];
+          else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16(acc[mt][nt][i]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
+  const int nb_gu = a.I_max / (kT2N / 2), nb_dn = a.H / kT2N;
+  const dim3 gu(a.max_tiles * nb_gu), dn(a.max_tiles * nb_dn), blk(kT2Threads);
+  const bool yf32 = a.y_dt == MOE_F32;
+  if (a.wdt == MOE_MXFP4)
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES, true, false, true>), gu, blk, 0, s, a, nb_gu);
+  else
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, true, false, false>), gu, blk, 0, s, a, nb_gu);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
+  if (a.wdt == MOE_MXFP4 && yf32)
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES, false, true, true>), dn, blk, 0, s, a, nb_dn);
+  else if (a.wdt == MOE_MXFP4)
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES, false, false, true>), dn, blk, 0, s, a, nb_dn);
+  else if (yf32)
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, true, false>), dn, blk, 0, s, a, nb_dn);
+  else
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, false, false>), dn, blk, 0, s, a, nb_dn);
+  return hipGetLastError();
+}
+
+}  // namespace moe

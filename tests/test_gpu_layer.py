@@ -248,9 +248,8 @@ def test_e384_fp8_full_size():
 MX_ROWS = [
     MoEConfig("mxfp4_rows_small", T=700, H=256, E=6, k=1, I=128, score="none", act="bf16",
               wdt="mxfp4", out="bf16", seed=51, weight_seed=51, dirichlet_alpha=0.5),
-    MoEConfig("mxfp4_rows_f32out_ragged", T=257, H=384, E=9, k=1, I=192, score="none", act="bf16",
+    MoEConfig("mxfp4_rows_f32out_ragged", T=257, H=384, E=9, k=1, I=384, score="none", act="bf16",
               wdt="mxfp4", out="f32", seed=52, weight_seed=52, dirichlet_alpha=0.5),
-    # H % 128 and I % 128: the DMA kernel that stages the E2M1 codes and decodes in registers
     MoEConfig("mxfp4_rows_dma_ragged", T=1500, H=512, E=5, k=1, I=256, score="none", act="bf16",
               wdt="mxfp4", out="f32", seed=54, weight_seed=54, dirichlet_alpha=0.5),
 ]
