@@ -2,7 +2,8 @@
 
 A step is one moe_layer_forward (route, permute, grouped SwiGLU FFN of the routed and the
 shared experts, combine) over one batch of the workload, with inputs and weights resident
-in HBM. Default workload: the DeepSeek-R1-shaped decode layer (T=128 tokens, H=7168, 256
+in HBM; for the pre-routed workload (ep32_mxfp4: one GPU's share of received rows) it is
+one moe_rows_forward (permute, grouped FFN, combine). Default workload: the DeepSeek-R1-shaped decode layer (T=128 tokens, H=7168, 256
 routed experts, top-8, sigmoid scores with a selection-only bias, weights renormalised
 and scaled by 2.5, one shared expert, I=2048, bf16).
 
@@ -140,8 +141,9 @@ def ffn_accounting(cfg, touched):
     return {
         "gate_up": launch(w13 + rows * H * xb + h_elems * hb, fl_gu, kgu),
         "down": launch(w2 + h_elems * hb + rows * H * 4.0, fl_dn, kdn),
-        # router weights + x read by the router, output written by the combine
-        "other_bytes": cfg.E * H * ELEM_BYTES[cfg.act] + 2 * T * H * ELEM_BYTES[cfg.act],
+        # router weights + x read by the router (routed layers), output written by the combine
+        "other_bytes": ((cfg.E * H + T * H) * ELEM_BYTES[cfg.act] if cfg.routed else 0)
+        + T * H * ELEM_BYTES[cfg.out],
         "router_flops": 2.0 * T * cfg.E * H if cfg.routed else 0.0,
     }
 
@@ -180,33 +182,51 @@ def main():
     from synth.problem import device_problem, host_problem
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from moe_cases import make_layer
+    from moe_cases import experts, make_layer
 
     cfg = CONFIGS[args.workload]
-    if not cfg.routed:
-        raise SystemExit("bench.py times routed workloads (pre-routed rows: see tests)")
     log(f"workload {cfg.name}: generating inputs on the device")
     host = host_problem(cfg)
     dev = device_problem(cfg, host=host)
-    layer = make_layer(cfg, dev)
     T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
     odt = torch.float32 if cfg.out == "f32" else torch.bfloat16
     out = torch.empty((T, H), dtype=odt, device="cuda")
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     ev = moe.StageEvents()
     stream = torch.cuda.current_stream()
+    if cfg.routed:
+        # a step: the whole layer (route, permute, grouped FFN incl. shared expert, combine)
+        layer = make_layer(cfg, dev)
+
+        def step():
+            layer.forward(dev.x, out, counts=counts)
+
+        def timed_step():
+            moe.moe_layer_forward_timed(layer.desc, dev.x, out, layer.ws, ev, counts=counts)
+    else:
+        # pre-routed rows (one GPU's expert-parallel share): permute, grouped FFN, combine
+        bank = experts(dev.routed)
+        ws = moe.workspace(moe.moe_rows_workspace_size(bank, moe.DTYPES[cfg.act], T))
+        row_e, row_w = dev.topk_idx.view(-1), dev.topk_w.view(-1)
+        counts.copy_(torch.bincount(row_e.long(), minlength=E).int())
+
+        def step():
+            moe.moe_rows_forward(bank, dev.x, row_e, row_w, out, ws)
+
+        def timed_step():
+            moe.moe_rows_forward_timed(bank, dev.x, row_e, row_w, out, ws, ev)
 
     for _ in range(args.warmup):
-        layer.forward(dev.x, out, counts=counts)
+        step()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    # timed region: K plain layer steps
+    # timed region: K plain steps
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
-        layer.forward(dev.x, out, counts=counts)
+        step()
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
@@ -215,7 +235,7 @@ def main():
     # per-stage times of the same launches, from events the library records on its stream
     stage = {s: [] for s in moe.STAGES}
     for _ in range(args.steps):
-        moe.moe_layer_forward_timed(layer.desc, dev.x, out, layer.ws, ev, counts=counts)
+        timed_step()
         torch.cuda.synchronize()
         for s_, v in ev.elapsed_ms().items():
             stage[s_].append(v)

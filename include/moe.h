@@ -198,6 +198,15 @@ moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_d
                             const int32_t* row_expert, const float* row_w, int32_t rows,
                             void* out, moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_rows_forward with stage timing, in the event layout of moe_layer_forward_timed
+ * (events [0] and [1] are recorded together: there is no route stage). MOE_ERR_NULL if
+ * events is NULL; otherwise the same checks, kernels and launch configurations as
+ * moe_rows_forward. */
+moe_status moe_rows_forward_timed(const moe_experts* w, const void* x, moe_dtype act_dt,
+                                  const int32_t* row_expert, const float* row_w, int32_t rows,
+                                  void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
+                                  void* stream, void* const* events);
+
 /* Per 1 x 128 block fp8 quantisation of activation rows, as the fp8 expert path applies it
  * to its inputs (the FP8 grouped GEMM inputs of GC-MoE, key_changes, fourth item):
  * scale = fp32(amax / 448) per block of 128 consecutive elements of a row (1 for an

@@ -54,7 +54,8 @@ EXPORTS = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size"
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
            "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_rows_workspace_size",
-           "moe_rows_forward", "moe_quantize_fp8", "moe_status_str", "moe_last_hip_error"]
+           "moe_rows_forward", "moe_rows_forward_timed", "moe_quantize_fp8", "moe_status_str",
+           "moe_last_hip_error"]
 
 
 def lib():
@@ -84,8 +85,11 @@ def lib():
     L.moe_rows_workspace_size.argtypes = [P(moe_experts), ci, i32]
     L.moe_rows_workspace_size.restype = sz
     L.moe_rows_forward.argtypes = [P(moe_experts), vp, ci, vp, vp, i32, vp, ci, vp, sz, vp]
+    L.moe_rows_forward_timed.argtypes = [P(moe_experts), vp, ci, vp, vp, i32, vp, ci, vp, sz, vp,
+                                         P(vp)]
     for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
-              "moe_layer_forward", "moe_layer_forward_timed", "moe_rows_forward"):
+              "moe_layer_forward", "moe_layer_forward_timed", "moe_rows_forward",
+              "moe_rows_forward_timed"):
         getattr(L, f).restype = ci
     L.moe_quantize_fp8.argtypes = [vp, i32, i32, vp, vp, vp]
     L.moe_quantize_fp8.restype = ci
@@ -280,6 +284,16 @@ def moe_rows_forward(experts: Experts, x, row_expert, row_w, out, ws, stream=Non
     st = lib().moe_rows_forward(ctypes.byref(cw), _ptr(x), _act_dt(x), _ptr(row_expert), _ptr(row_w),
                                 rows, _ptr(out), _act_dt(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_rows_forward")
+
+
+def moe_rows_forward_timed(experts: Experts, x, row_expert, row_w, out, ws, events: StageEvents,
+                           stream=None):
+    cw = experts.c()
+    rows = x.shape[0]
+    st = lib().moe_rows_forward_timed(ctypes.byref(cw), _ptr(x), _act_dt(x), _ptr(row_expert),
+                                      _ptr(row_w), rows, _ptr(out), _act_dt(out), _ptr(ws),
+                                      ws.numel(), _stream(stream), events.ev)
+    _check(st, "moe_rows_forward_timed")
 
 
 class MoELayer:

@@ -458,9 +458,10 @@ size_t moe_rows_workspace_size(const moe_experts* w, moe_dtype act_dt, int32_t r
   return plan_rows(w, act_dt, rows, o, &fp, &qp);
 }
 
-moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_dt,
-                            const int32_t* row_expert, const float* row_w, int32_t rows,
-                            void* out, moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
+static moe_status rows_forward(const moe_experts* w, const void* x, moe_dtype act_dt,
+                               const int32_t* row_expert, const float* row_w, int32_t rows,
+                               void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
+                               void* stream, void* const* events) {
   if (!w) return MOE_ERR_NULL;
   if (rows < 0 || (int64_t)rows * 2 >= ((int64_t)1 << 31) || w->E > 1024) return MOE_ERR_SHAPE;
   moe_status st = check_bank(w, w->H, true);
@@ -476,9 +477,19 @@ moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_d
   if (ws_bytes < total) return MOE_ERR_WORKSPACE;
   char* base = reinterpret_cast<char*>(ws);
   hipStream_t s = (hipStream_t)stream;
+  hipEvent_t ev[MOE_STAGE_EVENTS] = {};
+  if (events)
+    for (int i = 0; i < MOE_STAGE_EVENTS; ++i) ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
+  hipError_t e = hipSuccess;
+  // the stage layout of moe_layer_forward_timed; there is no route stage here
+#define MOE_MARK(i)                                                                    \
+  if (events && (e = hipEventRecord(ev[i], s)) != hipSuccess)                         \
+    return hip_fail(e, "moe_rows_forward event");
+  MOE_MARK(0);
+  MOE_MARK(1);
   int32_t* inv_perm = reinterpret_cast<int32_t*>(base + o[3]);
   int32_t* row_token = reinterpret_cast<int32_t*>(base + o[4]);
-  hipError_t e = launch_permute_maps(row_expert, rows, 1, w->E, reinterpret_cast<int32_t*>(base + o[0]),
+  e = launch_permute_maps(row_expert, rows, 1, w->E, reinterpret_cast<int32_t*>(base + o[0]),
                                      reinterpret_cast<int32_t*>(base + o[1]),
                                      reinterpret_cast<int32_t*>(base + o[2]), inv_perm, row_token,
                                      reinterpret_cast<Tile*>(base + p.o_tiles),
@@ -494,10 +505,31 @@ moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_d
     f.a_q = reinterpret_cast<const uint8_t*>(base + qp.o_q);
     f.a_qscale = reinterpret_cast<const float*>(base + qp.o_qs);
   }
-  e = launch_grouped_ffn(f, base + p.o_scratch, s);
+  MOE_MARK(2);
+  e = launch_grouped_ffn(f, base + p.o_scratch, s, events ? ev[3] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "moe_rows_forward grouped_ffn");
+  MOE_MARK(4);
   e = launch_combine(y, p.y_dt, inv_perm, row_w, rows, 1, w->H, nullptr, out, out_dt, s);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_rows_forward combine");
+  if (e != hipSuccess) return hip_fail(e, "moe_rows_forward combine");
+  MOE_MARK(5);
+#undef MOE_MARK
+  return MOE_OK;
+}
+
+moe_status moe_rows_forward(const moe_experts* w, const void* x, moe_dtype act_dt,
+                            const int32_t* row_expert, const float* row_w, int32_t rows,
+                            void* out, moe_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
+  return rows_forward(w, x, act_dt, row_expert, row_w, rows, out, out_dt, ws, ws_bytes, stream,
+                      nullptr);
+}
+
+moe_status moe_rows_forward_timed(const moe_experts* w, const void* x, moe_dtype act_dt,
+                                  const int32_t* row_expert, const float* row_w, int32_t rows,
+                                  void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
+                                  void* stream, void* const* events) {
+  if (!events) return MOE_ERR_NULL;
+  return rows_forward(w, x, act_dt, row_expert, row_w, rows, out, out_dt, ws, ws_bytes, stream,
+                      events);
 }
 
 // --------------------------------------------------------------- fp8 quantiser

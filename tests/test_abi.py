@@ -180,6 +180,8 @@ def test_other_entry_point_validation():
     assert L.moe_quantize_fp8(P, 0, 256, None, None, None) == moe.MOE_OK
     assert L.moe_rows_forward(ctypes.byref(b), P, moe.MOE_BF16, P, P, 16, P, moe.MOE_BF16, P, 16,
                               None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_rows_forward_timed(ctypes.byref(b), P, moe.MOE_BF16, P, P, 16, P, moe.MOE_BF16, P,
+                                    1 << 30, None, None) == moe.MOE_ERR_NULL   # no events
     for H, I in ((192, 128), (256, 192)):                  # MXFP4 needs H % 128 and I % 128
         fb = bank("mxfp4", H=H, I=I, scales=True)
         assert L.moe_rows_forward(ctypes.byref(fb), P, moe.MOE_BF16, P, P, 16, P, moe.MOE_BF16, P,

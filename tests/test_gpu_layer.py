@@ -266,6 +266,25 @@ def test_mxfp4_rows_match_oracle(cfg):
     assert err <= TOL["mxfp4"], (describe(cfg), err)
 
 
+def test_rows_forward_timed_matches_untimed():
+    """The timed pre-routed entry point runs the same kernels: identical output, and stage
+    times that add up (no route stage)."""
+    cfg = MX_ROWS[0]
+    _, dev = problems(cfg)
+    want = run_rows(cfg, dev)["out"]
+    e = experts(dev.routed)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    ws = moe.workspace(moe.moe_rows_workspace_size(e, moe.DTYPES[cfg.act], cfg.T))
+    ev = moe.StageEvents()
+    moe.moe_rows_forward_timed(e, dev.x, dev.topk_idx.view(-1), dev.topk_w.view(-1), out, ws, ev)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, want)
+    st = ev.elapsed_ms()
+    # events [0] and [1] are recorded back to back: only the recording gap separates them
+    assert st["route"] < 0.05 and all(v >= 0 for v in st.values()) and st["gate_up"] > 0
+
+
 def test_mxfp4_routed_layer_matches_oracle():
     cfg = MoEConfig("mxfp4_routed_shared", T=300, H=256, E=8, k=2, I=128, score="sigmoid",
                     use_bias=True, scale=2.5, shared_I=128, act="bf16", wdt="mxfp4", out="bf16",
