@@ -40,7 +40,10 @@ namespace {
 #define MOE_T2_STAGES 2
 #endif
 #ifndef MOE_T2_MX_STAGES
-#define MOE_T2_MX_STAGES 3
+#define MOE_T2_MX_STAGES 2
+#endif
+#ifndef MOE_T2_MX_TN
+#define MOE_T2_MX_TN 8
 #endif
 #ifndef MOE_T2_WAVES_PER_SIMD
 #define MOE_T2_WAVES_PER_SIMD 2
@@ -81,11 +84,17 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
   constexpr int STAGE = BM * 128 + BSTAGE;
   constexpr int RPI = NW * 8;                  // LDS rows filled per DMA instruction round
   constexpr int CA = BM / RPI;                 // DMA instructions per thread per K block: A,
-  constexpr int CB = kMX ? BN * 32 / (1024 * NW) : BN / RPI;  // B,
-  constexpr int CS = kMX ? 1 : 0;                              // MXFP4 scales
+  // MXFP4: each wavefront moves its UPW 16-B units of a stage's codes (CB instructions,
+  // the last one with LPW lanes) and its SPW rows' scale dwords (one instruction)
+  constexpr int UPW = BN * 2 / NW;
+  constexpr int CB = kMX ? (UPW + 63) / 64 : BN / RPI;  // B,
+  constexpr int LPW = UPW - 64 * (CB - 1);
+  constexpr int CS = kMX ? 1 : 0;                       // MXFP4 scales
   constexpr int OPS = CA + CB + CS;
+  constexpr int SPW = BN / NW;
   static_assert(BM % RPI == 0 && BN % RPI == 0 && BM % 16 == 0, "tile rows per DMA round");
-  static_assert(!kMX || (BN * 32 % (1024 * NW) == 0 && BN == 32 * NW), "MXFP4 DMA rounds");
+  static_assert(!kMX || (BN * 2 % NW == 0 && UPW % 2 == 0 && BN % NW == 0 && SPW <= 64),
+                "MXFP4 DMA rounds");
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   // tile-major order, as in k_tiled
@@ -135,9 +144,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     if (kMX) {
-      // lane l: row 32 q + l / 2, physical 16-B half l % 2 of its 32-B slice
-      const int r = 32 * (NW * i + wave) + (l >> 1);
-      const int lh = (l & 1) ^ ((r >> 3) & 1);
+      // lane l of instruction i: 16-B unit UPW w + 64 i + l of the codes, i.e. row
+      // (unit / 2) and physical half l % 2 of its 32-B slice (idle lanes repeat lane 0)
+      const int u = UPW * wave + 64 * i + ((i + 1 < CB || l < LPW) ? l : 0);
+      const int r = u >> 1;
+      const int lh = (u & 1) ^ ((r >> 3) & 1);
       bg[i] = wbase + weight_row(r) * wrow_bytes + lh * 16;
     } else {
       int r, cc;
@@ -146,11 +157,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
     }
   }
   if (kMX) {
-    // lanes 0..31 of wavefront w fetch the scale dword of B-tile row 32 w + lane
+    // lanes l < SPW of wavefront w fetch the scale dword of B-tile row SPW w + l
     const uint8_t* sbase = reinterpret_cast<const uint8_t*>(kGateUp ? a.bank[bank].w13_scale
                                                                     : a.bank[bank].w2_scale) +
                            ge * wrows * (K / 32);
-    sg = sbase + weight_row(32 * wave + (l & 31)) * (int64_t)(K / 32);
+    sg = sbase + weight_row(SPW * wave + (l < SPW ? l : 0)) * (int64_t)(K / 32);
   }
   auto issue = [&](int kt, int stage) {
     const int64_t o = (int64_t)kt * 128;
@@ -159,8 +170,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
     for (int i = 0; i < CA; ++i) dma16(ag[i] + o, st + (NW * i + wave) * 1024);
     if (kMX) {
 #pragma unroll
-      for (int i = 0; i < CB; ++i) dma16(bg[i] + (int64_t)kt * 32, st + BM * 128 + (NW * i + wave) * 1024);
-      if (l < 32) dma4(sg + (kt & ~1) * 2, st + BM * 128 + BN * 32 + wave * 128);
+      for (int i = 0; i < CB; ++i)
+        if (i + 1 < CB || l < LPW)
+          dma16(bg[i] + (int64_t)kt * 32, st + BM * 128 + (UPW * wave + 64 * i) * 16);
+      if (l < SPW) dma4(sg + (kt & ~1) * 2, st + BM * 128 + BN * 32 + wave * (SPW * 4));
     } else {
 #pragma unroll
       for (int i = 0; i < CB; ++i) dma16(bg[i] + o, st + BM * 128 + (NW * i + wave) * 1024);
@@ -250,28 +263,34 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
   }
 }
 
-}  // namespace
+// MXFP4 may take a wider weight tile (MOE_T2_MX_TN column tiles a wavefront): its K
+// slices are a quarter of bf16's, so the ring still leaves room for two workgroups a CU.
+constexpr int kMXN = MOE_T2_WGN * 16 * MOE_T2_MX_TN;
 
-hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
-  const int nb_gu = a.I_max / (kT2N / 2), nb_dn = a.H / kT2N;
+template <int TN, int S, bool kMX>
+hipError_t launch_tiled_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
+  constexpr int BN = MOE_T2_WGN * 16 * TN;
+  const int nb_gu = a.I_max / (BN / 2), nb_dn = a.H / BN;
   const dim3 gu(a.max_tiles * nb_gu), dn(a.max_tiles * nb_dn), blk(kT2Threads);
-  const bool yf32 = a.y_dt == MOE_F32;
-  if (a.wdt == MOE_MXFP4)
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES, true, false, true>), gu, blk, 0, s, a, nb_gu);
-  else
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, true, false, false>), gu, blk, 0, s, a, nb_gu);
+  hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, true, false, kMX>), gu, blk, 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
-  if (a.wdt == MOE_MXFP4 && yf32)
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES, false, true, true>), dn, blk, 0, s, a, nb_dn);
-  else if (a.wdt == MOE_MXFP4)
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES, false, false, true>), dn, blk, 0, s, a, nb_dn);
-  else if (yf32)
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, true, false>), dn, blk, 0, s, a, nb_dn);
+  if (a.y_dt == MOE_F32)
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, false, true, kMX>), dn, blk, 0, s, a, nb_dn);
   else
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES, false, false, false>), dn, blk, 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, false, false, kMX>), dn, blk, 0, s, a, nb_dn);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
+  if (a.wdt != MOE_MXFP4) return launch_tiled_pair<MOE_T2_TN, MOE_T2_STAGES, false>(a, s, mid_event);
+  const bool wide = kMXN != kT2N && a.H % kMXN == 0 && a.bank[0].I % (kMXN / 2) == 0 &&
+                    (!a.has_shared || a.bank[1].I % (kMXN / 2) == 0);
+  if (wide) return launch_tiled_pair<MOE_T2_MX_TN, MOE_T2_MX_STAGES, true>(a, s, mid_event);
+  return launch_tiled_pair<MOE_T2_TN, MOE_T2_MX_STAGES, true>(a, s, mid_event);
 }
 
 }  // namespace moe
