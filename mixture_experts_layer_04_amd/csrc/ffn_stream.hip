@@ -63,7 +63,13 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
 
 // K steps per loop iteration of the streaming kernels (tuning constants).
 #ifndef MOE_STREAM_UNROLL_GU
-#define MOE_STREAM_UNROLL_GU 4
+#define MOE_STREAM_UNROLL_GU 2
+#endif
+#ifndef MOE_STREAM_ROWS_GU  // 16-row weight groups per wavefront (bf16)
+#define MOE_STREAM_ROWS_GU 4
+#endif
+#ifndef MOE_STREAM_ROWS_DN
+#define MOE_STREAM_ROWS_DN 1
 #endif
 #ifndef MOE_STREAM_UNROLL_DN
 #define MOE_STREAM_UNROLL_DN 8
@@ -86,9 +92,10 @@ __device__ __forceinline__ f32x4 mma(const Frag32& w, const Frag32& x, f32x4 acc
   return kF32 ? mma_f32(w, x, acc) : mma_bf16(w, x, acc);
 }
 
-// Gate/up + SwiGLU. Workgroup = (tile, block of 64 h features); wavefront w computes
-// features [f0, f0+16) of h: gate rows f0.. and up rows I+f0.. of W13[e].
-template <bool kF32>
+// Gate/up + SwiGLU. Workgroup = (tile, block of 64 R h features); wavefront w computes
+// features [f0, f0 + 16 R) of h: gate rows f0.. and up rows I + f0.. of W13[e], R groups of
+// 16 rows each reusing one activation fragment per K step.
+template <bool kF32, int R>
 __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_tile) {
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int tile_id = blockIdx.x / fb_per_tile;
@@ -99,7 +106,7 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
   const int64_t ge = tl.group < a.E ? tl.group : 0;
   const int I = a.bank[bank].I;
   const int H = a.H;
-  const int f0 = fb * kFeatPerWG + wave * 16;
+  const int f0 = (fb * 4 + wave) * 16 * R;
   if (f0 >= I) return;
   const int m = l & 15, kq = l >> 4;
   const int esz = kF32 ? 4 : 2;
@@ -111,42 +118,61 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
   constexpr int kLane = kStep / 4;               // contiguous elements per lane per step
   constexpr int U = MOE_STREAM_UNROLL_GU;
   const int64_t lane_off = (int64_t)kq * kLane * esz;
-  const char* wg = w13 + (int64_t)(f0 + m) * H * esz + lane_off;
-  const char* wu = w13 + (int64_t)(I + f0 + m) * H * esz + lane_off;
+  const char* wg[R];
+  const char* wu[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    wg[r] = w13 + (int64_t)(f0 + 16 * r + m) * H * esz + lane_off;
+    wu[r] = w13 + (int64_t)(I + f0 + 16 * r + m) * H * esz + lane_off;
+  }
   const char* xr = reinterpret_cast<const char*>(a.a) + src * H * esz + lane_off;
-  f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+  f32x4 accg[R], accu[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) accg[r] = accu[r] = f32x4{0, 0, 0, 0};
   const int kmain = H - H % (kStep * U);
   for (int k0 = 0; k0 < kmain; k0 += kStep * U) {
-    Frag32 fg[U], fu[U], fx[U];
+    Frag32 fg[U][R], fu[U][R], fx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t o = (int64_t)(k0 + u * kStep) * esz;
-      fg[u] = load_w(wg + o);
-      fu[u] = load_w(wu + o);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        fg[u][r] = load_w(wg[r] + o);
+        fu[u][r] = load_w(wu[r] + o);
+      }
       fx[u] = load_x(xr + o, xv);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      accg = mma<kF32>(fg[u], fx[u], accg);
-      accu = mma<kF32>(fu[u], fx[u], accu);
-    }
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        accg[r] = mma<kF32>(fg[u][r], fx[u], accg[r]);
+        accu[r] = mma<kF32>(fu[u][r], fx[u], accu[r]);
+      }
   }
   for (int k0 = kmain; k0 < H; k0 += kStep) {
     const int64_t o = (int64_t)k0 * esz;
-    Frag32 fg = load_w(wg + o), fu = load_w(wu + o), fx = load_x(xr + o, xv);
-    accg = mma<kF32>(fg, fx, accg);
-    accu = mma<kF32>(fu, fx, accu);
+    const Frag32 fx = load_x(xr + o, xv);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      accg[r] = mma<kF32>(load_w(wg[r] + o), fx, accg[r]);
+      accu[r] = mma<kF32>(load_w(wu[r] + o), fx, accu[r]);
+    }
   }
   if (xv) {
-    f32x4 hv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hv[i] = silu_mul(accg[i], accu[i]);
-    store4<kF32>(a.h, (int64_t)(tl.row0 + m) * a.I_max + f0 + kq * 4, hv);
+    for (int r = 0; r < R; ++r) {
+      f32x4 hv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[i] = silu_mul(accg[r][i], accu[r][i]);
+      store4<kF32>(a.h, (int64_t)(tl.row0 + m) * a.I_max + f0 + 16 * r + kq * 4, hv);
+    }
   }
 }
 
-// Down projection. Workgroup = (tile, block of 64 output features of H).
-template <bool kF32, bool kYF32>
+// Down projection. Workgroup = (tile, block of 64 R output features of H); wavefront w
+// computes R groups of 16 output features, reusing one h fragment per K step.
+template <bool kF32, bool kYF32, int R>
 __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile) {
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int tile_id = blockIdx.x / fb_per_tile;
@@ -157,7 +183,7 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
   const int64_t ge = tl.group < a.E ? tl.group : 0;
   const int I = a.bank[bank].I;
   const int H = a.H;
-  const int f0 = fb * kFeatPerWG + wave * 16;
+  const int f0 = (fb * 4 + wave) * 16 * R;
   if (f0 >= H) return;
   const int m = l & 15, kq = l >> 4;
   const int esz = kF32 ? 4 : 2;
@@ -167,52 +193,67 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
   const int64_t lane_off = (int64_t)kq * kLane * esz;
   const bool xv = m < tl.nrows;
   const char* w2 = reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * esz;
-  const char* wr = w2 + (int64_t)(f0 + m) * I * esz + lane_off;
+  const char* wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wr[r] = w2 + (int64_t)(f0 + 16 * r + m) * I * esz + lane_off;
   const char* hr = reinterpret_cast<const char*>(a.h) +
                    (int64_t)(tl.row0 + (xv ? m : 0)) * a.I_max * esz + lane_off;
-  f32x4 acc = {0, 0, 0, 0};
+  f32x4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4{0, 0, 0, 0};
   const int kmain = I - I % (kStep * U);
   for (int k0 = 0; k0 < kmain; k0 += kStep * U) {
-    Frag32 fw[U], fh[U];
+    Frag32 fw[U][R], fh[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t o = (int64_t)(k0 + u * kStep) * esz;
-      fw[u] = load_w(wr + o);
+#pragma unroll
+      for (int r = 0; r < R; ++r) fw[u][r] = load_w(wr[r] + o);
       fh[u] = load_x(hr + o, xv);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc = mma<kF32>(fw[u], fh[u], acc);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = mma<kF32>(fw[u][r], fh[u], acc[r]);
   }
   for (int k0 = kmain; k0 < I; k0 += kStep) {
     const int64_t o = (int64_t)k0 * esz;
-    acc = mma<kF32>(load_w(wr + o), load_x(hr + o, xv), acc);
+    const Frag32 fh = load_x(hr + o, xv);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = mma<kF32>(load_w(wr[r] + o), fh, acc[r]);
   }
-  if (xv) store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + kq * 4, acc);
+  if (xv) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + 16 * r + kq * 4, acc[r]);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
-  const int fb_gu = (a.I_max + kFeatPerWG - 1) / kFeatPerWG;
-  const int fb_dn = (a.H + kFeatPerWG - 1) / kFeatPerWG;
+  constexpr int RG = MOE_STREAM_ROWS_GU, RD = MOE_STREAM_ROWS_DN;
+  const int fb_gu = (a.I_max + kFeatPerWG * RG - 1) / (kFeatPerWG * RG);
+  const int fb_dn = (a.H + kFeatPerWG * RD - 1) / (kFeatPerWG * RD);
   const bool f32 = a.wdt == MOE_F32;
   const bool yf32 = a.y_dt == MOE_F32;
   const dim3 blk(256);
   if (f32)
-    hipLaunchKernelGGL(k_gateup_stream<true>, dim3(a.max_tiles * fb_gu), blk, 0, s, a, fb_gu);
+    hipLaunchKernelGGL((k_gateup_stream<true, 1>), dim3(a.max_tiles * ((a.I_max + kFeatPerWG - 1) / kFeatPerWG)), blk, 0, s, a, (a.I_max + kFeatPerWG - 1) / kFeatPerWG);
   else
-    hipLaunchKernelGGL(k_gateup_stream<false>, dim3(a.max_tiles * fb_gu), blk, 0, s, a, fb_gu);
+    hipLaunchKernelGGL((k_gateup_stream<false, RG>), dim3(a.max_tiles * fb_gu), blk, 0, s, a, fb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
+  const int fb_dn1 = (a.H + kFeatPerWG - 1) / kFeatPerWG;
   if (f32 && yf32)
-    hipLaunchKernelGGL((k_down_stream<true, true>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
+    hipLaunchKernelGGL((k_down_stream<true, true, 1>), dim3(a.max_tiles * fb_dn1), blk, 0, s, a, fb_dn1);
   else if (f32)
-    hipLaunchKernelGGL((k_down_stream<true, false>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
+    hipLaunchKernelGGL((k_down_stream<true, false, 1>), dim3(a.max_tiles * fb_dn1), blk, 0, s, a, fb_dn1);
   else if (yf32)
-    hipLaunchKernelGGL((k_down_stream<false, true>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
+    hipLaunchKernelGGL((k_down_stream<false, true, RD>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
   else
-    hipLaunchKernelGGL((k_down_stream<false, false>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
+    hipLaunchKernelGGL((k_down_stream<false, false, RD>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
   return hipGetLastError();
 }
 
