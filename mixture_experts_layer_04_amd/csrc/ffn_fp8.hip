@@ -18,10 +18,10 @@ namespace moe {
 namespace {
 
 #ifndef MOE_F8_STAGES_GU
-#define MOE_F8_STAGES_GU 3
+#define MOE_F8_STAGES_GU 2
 #endif
 #ifndef MOE_F8_STAGES_DN
-#define MOE_F8_STAGES_DN 4
+#define MOE_F8_STAGES_DN 2
 #endif
 
 // fp32 -> E4M3FN code, round to nearest even, saturating at +-448 (NaN -> 0x7F).
