@@ -39,6 +39,9 @@ namespace {
 #ifndef MOE_T2_STAGES
 #define MOE_T2_STAGES 2
 #endif
+#ifndef MOE_T2_STAGES_B_DN  // weight-ring stages of the bf16 down launch: its h rows are
+#define MOE_T2_STAGES_B_DN 3  // L2-resident, its weights stream from HBM (80 KB: 2 WGs a CU)
+#endif
 #ifndef MOE_T2_MX_STAGES
 #define MOE_T2_MX_STAGES 2
 #endif
@@ -76,12 +79,12 @@ __device__ __forceinline__ bf16x8 e2m1x8_bf16(uint32_t w, float scale) {
 // quarter u ^ 2 ((r >> 3) & 1), which spreads the 64-bit fragment reads of 16 rows over
 // all banks) and 4 scale bytes a row (those of K blocks kt & ~1 and (kt & ~1) + 1, one
 // aligned dword), and fragments are decoded to bf16 in registers as they are read.
-template <int TM, int TN, int WGM, int WGN, int S, bool kGateUp, bool kYF32, bool kMX>
+template <int TM, int TN, int WGM, int WGN, int S, int SB, bool kGateUp, bool kYF32, bool kMX>
 __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled2(FfnArgs a, int nb_per_tile) {
   constexpr int NW = WGM * WGN;
   constexpr int BM = WGM * 16 * TM, BN = WGN * 16 * TN;
   constexpr int BSTAGE = kMX ? BN * 32 + BN * 4 : BN * 128;  // weight bytes of a stage
-  constexpr int STAGE = BM * 128 + BSTAGE;
+  constexpr int ASTAGE = BM * 128;                          // activation bytes of a stage
   constexpr int RPI = NW * 8;                  // LDS rows filled per DMA instruction round
   constexpr int CA = BM / RPI;                 // DMA instructions per thread per K block: A,
   // MXFP4: each wavefront moves its UPW 16-B units of a stage's codes (CB instructions,
@@ -90,12 +93,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
   constexpr int CB = kMX ? (UPW + 63) / 64 : BN / RPI;  // B,
   constexpr int LPW = UPW - 64 * (CB - 1);
   constexpr int CS = kMX ? 1 : 0;                       // MXFP4 scales
-  constexpr int OPS = CA + CB + CS;
   constexpr int SPW = BN / NW;
   static_assert(BM % RPI == 0 && BN % RPI == 0 && BM % 16 == 0, "tile rows per DMA round");
   static_assert(!kMX || (BN * 2 % NW == 0 && UPW % 2 == 0 && BN % NW == 0 && SPW <= 64),
                 "MXFP4 DMA rounds");
-  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+  // activation ring (S stages), then weight ring (SB stages): the weights, which mostly
+  // come from HBM, may be requested further ahead than the activations, mostly L2 hits
+  __shared__ __attribute__((aligned(1024))) char smem[S * ASTAGE + SB * BSTAGE];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   // tile-major order, as in k_tiled
   const int tidx = blockIdx.x / nb_per_tile;
@@ -163,20 +167,21 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
                            ge * wrows * (K / 32);
     sg = sbase + weight_row(SPW * wave + (l < SPW ? l : 0)) * (int64_t)(K / 32);
   }
-  auto issue = [&](int kt, int stage) {
-    const int64_t o = (int64_t)kt * 128;
-    char* st = smem + stage * STAGE;
+  auto issue_a = [&](int kt) {
+    char* st = smem + (kt % S) * ASTAGE;
 #pragma unroll
-    for (int i = 0; i < CA; ++i) dma16(ag[i] + o, st + (NW * i + wave) * 1024);
+    for (int i = 0; i < CA; ++i) dma16(ag[i] + (int64_t)kt * 128, st + (NW * i + wave) * 1024);
+  };
+  auto issue_b = [&](int kt) {
+    char* st = smem + S * ASTAGE + (kt % SB) * BSTAGE;
     if (kMX) {
 #pragma unroll
       for (int i = 0; i < CB; ++i)
-        if (i + 1 < CB || l < LPW)
-          dma16(bg[i] + (int64_t)kt * 32, st + BM * 128 + (UPW * wave + 64 * i) * 16);
-      if (l < SPW) dma4(sg + (kt & ~1) * 2, st + BM * 128 + BN * 32 + wave * (SPW * 4));
+        if (i + 1 < CB || l < LPW) dma16(bg[i] + (int64_t)kt * 32, st + (UPW * wave + 64 * i) * 16);
+      if (l < SPW) dma4(sg + (kt & ~1) * 2, st + BN * 32 + wave * (SPW * 4));
     } else {
 #pragma unroll
-      for (int i = 0; i < CB; ++i) dma16(bg[i] + o, st + BM * 128 + (NW * i + wave) * 1024);
+      for (int i = 0; i < CB; ++i) dma16(bg[i] + (int64_t)kt * 128, st + (NW * i + wave) * 1024);
     }
   };
   const int wm = wave % WGM, wn = wave / WGM;
@@ -192,29 +197,39 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
   for (int t = 0; t < TM; ++t) arow[t] = wm * (16 * TM) + t * 16 + m16;
 #pragma unroll
   for (int t = 0; t < TN; ++t) brow[t] = wn * (16 * TN) + t * 16 + m16;
+  // Step i issues A(i + S - 1), then B(i + SB - 1); the steps before the loop issue the
+  // blocks >= 0 of steps -(max(S, SB) - 1) .. -1. Block kt has landed once no more DMA
+  // instructions are outstanding than were issued after the later of A(kt) and B(kt).
+  constexpr int OA = CA, OB = CB + CS, SL = S > SB ? S : SB;
+  constexpr int AFTER = S < SB ? OB + (S - 2) * (OA + OB) : (SB - 2) * (OA + OB);
+  static_assert(S >= 2 && SB >= 2 && AFTER < 64, "ring depths");
 #pragma unroll
-  for (int p = 0; p < S - 1; ++p)
-    if (p < KT) issue(p, p);
+  for (int p = 1 - SL; p < 0; ++p) {
+    if (p + S - 1 >= 0 && p + S - 1 < KT) issue_a(p + S - 1);
+    if (p + SB - 1 >= 0 && p + SB - 1 < KT) issue_b(p + SB - 1);
+  }
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * OPS>();
+    if (kt + SL - 2 < KT) wait_vmcnt<AFTER>();
     else wait_vmcnt<0>();
     // A plain barrier, not __syncthreads(): its fence would wait for every outstanding
     // DMA of the ring. The wait above already covers this thread's part of block kt.
     __builtin_amdgcn_s_barrier();
-    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
-    const char* cur = smem + (kt % S) * STAGE;
+    if (kt + S - 1 < KT) issue_a(kt + S - 1);
+    if (kt + SB - 1 < KT) issue_b(kt + SB - 1);
+    const char* cur = smem + (kt % S) * ASTAGE;                 // activations of block kt
+    const char* curb = smem + S * ASTAGE + (kt % SB) * BSTAGE;  // weights of block kt
     // MXFP4: this lane's 16 codes (elements 16 g .. 16 g + 15 of the K block) and scale
     uint2 wq[kMX ? TN : 1];
     float wsc[kMX ? TN : 1];
     if (kMX) {
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
-        const char* rb = cur + BM * 128 + brow[t] * 32;
+        const char* rb = curb + brow[t] * 32;
         // two 32-bit reads: with one 64-bit read the compiler makes it wait for all DMA
         const char* q = rb + 8 * (g ^ (((brow[t] >> 3) & 1) << 1));
         wq[t].x = *reinterpret_cast<const uint32_t*>(q);
         wq[t].y = *reinterpret_cast<const uint32_t*>(q + 4);
-        wsc[t] = e8m0_f32(*reinterpret_cast<const uint8_t*>(cur + BM * 128 + BN * 32 + 4 * brow[t] +
+        wsc[t] = e8m0_f32(*reinterpret_cast<const uint8_t*>(curb + BN * 32 + 4 * brow[t] +
                                                              (kt & 1) * 2 + (g >> 1)));
       }
     }
@@ -228,7 +243,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         if (kMX) fb[t] = e2m1x8_bf16(ks ? wq[t].y : wq[t].x, wsc[t]);
-        else fb[t] = *reinterpret_cast<const bf16x8*>(cur + BM * 128 + lds_off(brow[t], c));
+        else fb[t] = *reinterpret_cast<const bf16x8*>(curb + lds_off(brow[t], c));
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -267,30 +282,36 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
 // slices are a quarter of bf16's, so the ring still leaves room for two workgroups a CU.
 constexpr int kMXN = MOE_T2_WGN * 16 * MOE_T2_MX_TN;
 
-template <int TN, int S, bool kMX>
+// SB: weight-ring stages of the gate/up launch, SBD of the down launch
+template <int TN, int S, int SB, int SBD, bool kMX>
 hipError_t launch_tiled_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
   constexpr int BN = MOE_T2_WGN * 16 * TN;
   const int nb_gu = a.I_max / (BN / 2), nb_dn = a.H / BN;
   const dim3 gu(a.max_tiles * nb_gu), dn(a.max_tiles * nb_dn), blk(kT2Threads);
-  hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, true, false, kMX>), gu, blk, 0, s, a, nb_gu);
+  hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, SB, true, false, kMX>), gu, blk, 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
   if (a.y_dt == MOE_F32)
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, false, true, kMX>), dn, blk, 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, SBD, false, true, kMX>), dn, blk, 0, s, a, nb_dn);
   else
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, false, false, kMX>), dn, blk, 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, SBD, false, false, kMX>), dn, blk, 0, s, a, nb_dn);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
-  if (a.wdt != MOE_MXFP4) return launch_tiled_pair<MOE_T2_TN, MOE_T2_STAGES, false>(a, s, mid_event);
+  if (a.wdt != MOE_MXFP4)
+    return launch_tiled_pair<MOE_T2_TN, MOE_T2_STAGES, MOE_T2_STAGES, MOE_T2_STAGES_B_DN, false>(
+        a, s, mid_event);
   const bool wide = kMXN != kT2N && a.H % kMXN == 0 && a.bank[0].I % (kMXN / 2) == 0 &&
                     (!a.has_shared || a.bank[1].I % (kMXN / 2) == 0);
-  if (wide) return launch_tiled_pair<MOE_T2_MX_TN, MOE_T2_MX_STAGES, true>(a, s, mid_event);
-  return launch_tiled_pair<MOE_T2_TN, MOE_T2_MX_STAGES, true>(a, s, mid_event);
+  if (wide)
+    return launch_tiled_pair<MOE_T2_MX_TN, MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, MOE_T2_MX_STAGES,
+                             true>(a, s, mid_event);
+  return launch_tiled_pair<MOE_T2_TN, MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, true>(
+      a, s, mid_event);
 }
 
 }  // namespace moe
