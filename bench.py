@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="r1_decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--cpu-tokens", type=int, default=24,
+                    help="tokens of the batch the CPU oracle leg computes (about 10 s of CPU work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (a known-size "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")

@@ -7,9 +7,10 @@
 // k_hist    one wavefront per block of 64 tokens: each lane ORs its bit into an LDS
 //           64-bit mask per expert (ds_or_b64; order-free, so deterministic). The masks
 //           and their popcounts (per-block counts) go to the workspace.
-// k_scan    one workgroup: per-expert totals, exclusive scan over experts (offsets), then
-//           each block's base row per expert; optionally the tile list for the grouped
-//           GEMM (row chunks of tile_m rows per expert, plus the shared group).
+// k_scan    one workgroup: per-expert totals (each expert's blocks split into chunks over
+//           the 1024 threads), exclusive scan over experts (offsets), then each block's
+//           base row per expert; optionally the tile list for the grouped GEMM (row
+//           chunks of tile_m rows per expert, plus the shared group).
 // k_scatter one wavefront per block: row = base[block][e] + number of earlier tokens of
 //           the block that chose e (popcount of the mask below the lane).
 // k_gather  x_perm[r] = x[perm_src[r] / k], 16 B per lane.
@@ -67,23 +68,52 @@ __global__ void __launch_bounds__(kScanThreads) k_scan(int32_t* __restrict__ cnt
                                                        int32_t* __restrict__ ntiles, int tile_m,
                                                        int with_shared) {
   __shared__ int sh[kScanThreads];
-  const int e = threadIdx.x;
-  int tot = 0;
-  if (e < E)
-    for (int b = 0; b < nb; ++b) tot += cnt[(int64_t)b * E + e];
+  __shared__ int part_sum[kScanThreads];
+  // Thread tid works on expert tid % E and on part tid / E of that expert's blocks: P
+  // contiguous chunks of C blocks, so that the per-block counts of one expert are summed
+  // and turned into running bases by P threads instead of one.
+  const int tid = threadIdx.x;
+  const int P = E <= kScanThreads ? kScanThreads / E : 1;
+  const int C = (nb + P - 1) / P;
+  const int pe = tid % E, part = tid / E;
+  const bool worker = part < P;
+  const int b0 = part * C, b1 = min(nb, b0 + C);
+  int s = 0;
+  if (worker)
+    for (int b = b0; b < b1; ++b) s += cnt[(int64_t)b * E + pe];
+  part_sum[tid] = worker ? s : 0;
+  __syncthreads();
+  // per expert: exclusive prefix over its parts, and its total
+  int pre = 0, tot_pe = 0;
+  if (worker)
+    for (int q = 0; q < P; ++q) {
+      const int v = part_sum[q * E + pe];
+      if (q < part) pre += v;
+      tot_pe += v;
+    }
+  // expert offsets: exclusive scan over experts (threads tid < E hold part 0)
+  const int e = tid;
+  const int tot = (e < E) ? tot_pe : 0;
   int all;
-  const int off = block_exclusive_scan(e < E ? tot : 0, sh, &all);
-  if (e < E) {
-    counts[e] = tot;
-    offsets[e] = off;
-    int run = off;
-    for (int b = 0; b < nb; ++b) {
-      const int c = cnt[(int64_t)b * E + e];
-      cnt[(int64_t)b * E + e] = run;
+  const int off = block_exclusive_scan(tot, sh, &all);
+  // off of expert pe, as seen by every part of it
+  __syncthreads();
+  if (e < E) sh[e] = off;
+  __syncthreads();
+  if (worker) {
+    int run = sh[pe] + pre;
+    for (int b = b0; b < b1; ++b) {
+      const int c = cnt[(int64_t)b * E + pe];
+      cnt[(int64_t)b * E + pe] = run;
       run += c;
     }
   }
+  if (e < E) {
+    counts[e] = tot;
+    offsets[e] = off;
+  }
   if (e == 0) offsets[E] = all;
+  __syncthreads();  // every part has read its expert's offset from sh before sh is reused
   if (tiles) {
     // routed groups: ceil(count / tile_m) tiles each; the shared group E holds T rows
     // starting at row T*k
