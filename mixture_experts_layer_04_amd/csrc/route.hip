@@ -120,6 +120,9 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
     lg[i] = 0.0f;
     if (e < E) {
       double s = 0.0;
+      // unrolled so that the loads of a group of partials are in flight together; the
+      // sum still runs in split order
+#pragma unroll 8
       for (int p = 0; p < S; ++p) s += part[((int64_t)p * T + t) * E + e];
       lg[i] = (float)s;
       if (logits) logits[(int64_t)t * E + e] = lg[i];
