@@ -17,6 +17,8 @@ What is computed, and where it comes from:
     "auxiliary-loss-free bias routing" named in the roadmap of "Chapter 7:
     Serving Mega-MoE at Scale". The pages give no formula; the reading used is
     key = score + bias for selection, weights from the unbiased scores.
+  * The update of that bias from the batch's expert loads is a reading too (the pages
+    name the technique, not its rule); see bias_update.
   * The expert FFN is SwiGLU, and fp8 / MXFP4 weights with fp8 re-quantisation
     of the SwiGLU output follow the FP8/FP4 grouped GEMM with fused SwiGLU and
     re-quantisation in "GC-MoE: Overlapping Expert-Parallel Token Dispatch with
@@ -236,6 +238,31 @@ def permutation(topk_idx: np.ndarray, E: int):
     inv_perm = np.empty(T * k, np.int32)
     inv_perm[order] = np.arange(T * k, dtype=np.int32)
     return counts, offsets.astype(np.int32), perm_src, inv_perm
+
+
+# ----------------------------------------------------------------------------- balancing
+
+def bias_update(bias, counts, u: float) -> np.ndarray:
+    """One step of auxiliary-loss-free balancing of the selection bias.
+
+    The pages name the technique ("auxiliary-loss-free bias routing", roadmap of
+    "Chapter 7: Serving Mega-MoE at Scale") and its purpose -- keep the router from
+    piling traffic on a few experts without an auxiliary loss term ("Decoding
+    Trillion-Parameter MoE LLMs", sections "Routing: Top-K Experts Plus a Shared Expert"
+    and "Engineering Reality: Sparse Activation Is Not Free") -- but print no rule. The
+    reading used: an expert's load is the number of tokens routed to it in the batch
+    (`counts`), the mean load is sum(counts) / E, and
+
+        b_e <- b_e + u * sign(mean - load_e)
+
+    so an under-loaded expert's key is raised by u, an over-loaded one's lowered by u, and
+    one exactly at the mean is left alone. Evaluated in float64; the result is stored in
+    fp32, the format the router reads the bias in.
+    """
+    c = np.asarray(counts, np.float64)
+    mean = c.sum() / c.size
+    b64 = np.asarray(bias, np.float32).astype(np.float64)
+    return (b64 + float(u) * np.sign(mean - c)).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------- experts
