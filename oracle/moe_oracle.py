@@ -256,13 +256,15 @@ def bias_update(bias, counts, u: float) -> np.ndarray:
         b_e <- b_e + u * sign(mean - load_e)
 
     so an under-loaded expert's key is raised by u, an over-loaded one's lowered by u, and
-    one exactly at the mean is left alone. Evaluated in float64; the result is stored in
-    fp32, the format the router reads the bias in.
+    one exactly at the mean gets b + u * 0. The step u is an fp32 number, like the bias
+    (the rule is written for a stored fp32 bias and step). Evaluated in float64; the result
+    is stored in fp32, the format the router reads the bias in.
     """
     c = np.asarray(counts, np.float64)
     mean = c.sum() / c.size
     b64 = np.asarray(bias, np.float32).astype(np.float64)
-    return (b64 + float(u) * np.sign(mean - c)).astype(np.float32)
+    u64 = np.float64(np.float32(u))
+    return (b64 + u64 * np.sign(mean - c)).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------- experts

@@ -101,3 +101,26 @@ def test_iterated_update_balances_a_skewed_router():
     w = O.routing_weights(s64, idx, 1.0)
     sel = np.take_along_axis(s64, idx.astype(np.int64), axis=1)
     np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-15)
+
+
+def test_step_is_the_ieee_fp32_sum_of_bias_and_fp32_step():
+    """The bias and the step u are fp32 numbers and the new bias is their fp32 sum: equal,
+    bit for bit, to torch's float32 add of b and u * sign (including -0 + 0 = +0 at the
+    mean, and u values such as 0.01 that fp32 cannot hold exactly)."""
+    import torch
+
+    rng = np.random.default_rng(6)
+    E = 512
+    bias = (rng.standard_normal(E) * 0.05).astype(np.float32)
+    bias[:4] = [-0.0, 0.0, 1e-40, -1e-40]
+    counts = rng.integers(0, 3, E).astype(np.int32)
+    counts[:4] = 1                                   # choose the mean for the first four
+    counts[4:] = np.where(np.arange(4, E) % 2 == 0, 0, 2)
+    assert counts.sum() == E
+    for u in (0.01, 1e-3, 2.0 ** -10, -0.3):
+        got = O.bias_update(bias, counts, u)
+        sgn = np.sign(counts.sum() / E - counts.astype(np.float64)).astype(np.float32)
+        want = (torch.from_numpy(bias) + torch.tensor(u, dtype=torch.float32) *
+                torch.from_numpy(sgn)).numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), u
+    assert O.bias_update(np.array([-0.0], np.float32), [5], 0.01).view(np.uint32)[0] == 0
