@@ -243,6 +243,19 @@ def main():
     stage_ms = {s_: float(np.mean(v)) for s_, v in stage.items()}
     log("stage ms: " + ", ".join(f"{s_}={v:.4f}" for s_, v in stage_ms.items()))
 
+    # the selection-bias balancing step (not part of the forward step): its own timing
+    bias_us = None
+    if cfg.routed and cfg.use_bias:
+        b = dev.bias.clone()
+        reps = 200
+        start.record(stream)
+        for _ in range(reps):
+            moe.moe_bias_update(counts, 1e-3, b)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        bias_us = start.elapsed_time(stop) / reps * 1e3
+        log(f"bias update: {bias_us:.2f} us per call")
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -290,7 +303,8 @@ def main():
                    "stage_ms": {s_: round(v, 5) for s_, v in stage_ms.items()},
                    "layer_algorithmic_bytes": layer_bytes, "layer_flops": layer_flops,
                    "layer_hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                   "down_frac": acct["down"]["frac_fn"](stage_ms["down"] / 1e3)},
+                   "down_frac": acct["down"]["frac_fn"](stage_ms["down"] / 1e3),
+                   "bias_update_us": bias_us},
         "roofline": {"bound": g["bound"], "kernel": f"grouped gate/up + SwiGLU ({g['kernel']})",
                      "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
                      "traffic": measured_traffic(cfg.name),

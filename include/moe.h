@@ -215,6 +215,24 @@ moe_status moe_rows_forward_timed(const moe_experts* w, const void* x, moe_dtype
 moe_status moe_quantize_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* q_scale,
                             void* stream);
 
+/* ---------------------------------------------------------------- bias balancing */
+
+/* One step of auxiliary-loss-free balancing of the selection bias (the bias routing named
+ * in the roadmap of "Chapter 7: Serving Mega-MoE at Scale"; the pages give no update rule,
+ * and the one implemented is the plainest reading of the name):
+ *     bias[e] <- bias[e] + u * sign(mean - counts[e]),   mean = sum(counts) / E,
+ * i.e. +u for an expert that received fewer than the mean number of tokens in the batch,
+ * -u for one that received more, unchanged at exactly the mean. The sign is taken in exact
+ * integer arithmetic and the bias moves by one fp32 add, so the result is deterministic.
+ *   counts [E] int32 routed tokens per expert (moe_permute's counts, or moe_layer_forward's
+ *          counts_out); values are used as given (not checked on the device).
+ *   bias   [E] f32, updated in place (the bias moe_route and moe_layer_forward read).
+ *   u      step size; any finite float.
+ * Limits: 1 <= E <= 1024. MOE_ERR_SHAPE for E out of range or a non-finite u. One
+ * single-workgroup kernel; stream-ordered after the call that wrote counts. */
+moe_status moe_bias_update(const int32_t* counts, int32_t E, float u, float* bias,
+                           void* stream);
+
 const char* moe_status_str(moe_status s);
 const char* moe_last_hip_error(void); /* thread-local text of the last MOE_ERR_HIP */
 

@@ -54,7 +54,8 @@ EXPORTS = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size"
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
            "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_rows_workspace_size",
-           "moe_rows_forward", "moe_rows_forward_timed", "moe_quantize_fp8", "moe_status_str",
+           "moe_rows_forward", "moe_rows_forward_timed", "moe_quantize_fp8", "moe_bias_update",
+           "moe_status_str",
            "moe_last_hip_error"]
 
 
@@ -93,6 +94,8 @@ def lib():
         getattr(L, f).restype = ci
     L.moe_quantize_fp8.argtypes = [vp, i32, i32, vp, vp, vp]
     L.moe_quantize_fp8.restype = ci
+    L.moe_bias_update.argtypes = [vp, i32, f32, vp, vp]
+    L.moe_bias_update.restype = ci
     L.moe_status_str.argtypes = [ci]
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_last_hip_error.argtypes = []
@@ -271,6 +274,14 @@ def moe_quantize_fp8(x, q, q_scale, stream=None):
     n, H = x.shape
     st = lib().moe_quantize_fp8(_ptr(x), n, H, _ptr(q), _ptr(q_scale), _stream(stream))
     _check(st, "moe_quantize_fp8")
+
+
+def moe_bias_update(counts, u: float, bias, stream=None):
+    """In-place selection-bias step from per-expert routed counts (int32 [E], f32 [E])."""
+    if counts.numel() != bias.numel():
+        raise ValueError(f"counts has {counts.numel()} experts, bias {bias.numel()}")
+    st = lib().moe_bias_update(_ptr(counts), counts.numel(), float(u), _ptr(bias), _stream(stream))
+    _check(st, "moe_bias_update")
 
 
 def moe_rows_workspace_size(experts: Experts, act_dtype, rows: int) -> int:

@@ -544,4 +544,16 @@ moe_status moe_quantize_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, flo
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_fp8");
 }
 
+// ------------------------------------------------------------- bias balancing
+
+moe_status moe_bias_update(const int32_t* counts, int32_t E, float u, float* bias,
+                           void* stream) {
+  if (E < 1 || E > 1024) return MOE_ERR_SHAPE;
+  if (!__builtin_isfinite(u)) return MOE_ERR_SHAPE;
+  if (!counts || !bias) return MOE_ERR_NULL;
+  if (!al16(counts) || !al16(bias)) return MOE_ERR_ALIGN;
+  hipError_t e = launch_bias_update(counts, E, u, bias, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_bias_update");
+}
+
 }  // extern "C"

@@ -125,6 +125,11 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s,
 hipError_t launch_quant_rows_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* qs,
                                  hipStream_t s);
 
+// balance.hip
+// In-place selection-bias update from per-expert routed counts (1 <= E <= 1024).
+hipError_t launch_bias_update(const int32_t* counts, int32_t E, float u, float* bias,
+                              hipStream_t s);
+
 // combine.hip
 hipError_t launch_combine(const void* y, moe_dtype y_dt, const int32_t* inv_perm,
                           const float* topk_w, int32_t T, int32_t k, int32_t H,

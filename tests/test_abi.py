@@ -186,3 +186,15 @@ def test_other_entry_point_validation():
         fb = bank("mxfp4", H=H, I=I, scales=True)
         assert L.moe_rows_forward(ctypes.byref(fb), P, moe.MOE_BF16, P, P, 16, P, moe.MOE_BF16, P,
                                   1 << 30, None) == moe.MOE_ERR_SHAPE
+
+
+def test_bias_update_validation():
+    L = moe.lib()
+    for E in (0, 1025, -3):
+        assert L.moe_bias_update(P, E, 0.01, P, None) == moe.MOE_ERR_SHAPE
+    for u in (float("inf"), float("-inf"), float("nan")):
+        assert L.moe_bias_update(P, 8, u, P, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_bias_update(None, 8, 0.01, P, None) == moe.MOE_ERR_NULL
+    assert L.moe_bias_update(P, 8, 0.01, None, None) == moe.MOE_ERR_NULL
+    assert L.moe_bias_update(MISALIGNED, 8, 0.01, P, None) == moe.MOE_ERR_ALIGN
+    assert L.moe_bias_update(P, 8, 0.01, MISALIGNED, None) == moe.MOE_ERR_ALIGN
