@@ -39,6 +39,9 @@ namespace {
 #ifndef MOE_T2_STAGES
 #define MOE_T2_STAGES 2
 #endif
+#ifndef MOE_T2_STAGES_B_GU  // weight-ring stages of the bf16 gate/up launch
+#define MOE_T2_STAGES_B_GU 2
+#endif
 #ifndef MOE_T2_STAGES_B_DN  // weight-ring stages of the bf16 down launch: its h rows are
 #define MOE_T2_STAGES_B_DN 3  // L2-resident, its weights stream from HBM (80 KB: 2 WGs a CU)
 #endif
@@ -48,6 +51,7 @@ namespace {
 #ifndef MOE_T2_MX_TN
 #define MOE_T2_MX_TN 8
 #endif
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt to them round-robin
 #ifndef MOE_T2_WAVES_PER_SIMD
 #define MOE_T2_WAVES_PER_SIMD 2
 #endif
@@ -101,10 +105,21 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
   // come from HBM, may be requested further ahead than the activations, mostly L2 hits
   __shared__ __attribute__((aligned(1024))) char smem[S * ASTAGE + SB * BSTAGE];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  // tile-major order, as in k_tiled
-  const int tidx = blockIdx.x / nb_per_tile;
-  if (tidx >= *a.ntiles) return;
-  const int nb = blockIdx.x - tidx * nb_per_tile;
+  // Work items (tile, weight block) are cut into kXcds equal contiguous chunks, chunk x run
+  // by the workgroups that the dispatcher deals to XCD x (blockIdx = x mod kXcds), so that
+  // each XCD's L2 serves the items that share data. Inside a chunk the items of a block
+  // of up to kTileBlock row tiles of one group run weight block by weight block, the
+  // block's row tiles side by side: they read the same weight rows at the same time, and
+  // the items that read one activation tile are at most kTileBlock apart.
+  const int nitems = *a.ntiles * nb_per_tile;
+  const int chunk = (nitems + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * chunk + slot;
+  if (slot >= chunk || item >= nitems) return;
+  const Tile tb = a.tiles[item / nb_per_tile];
+  const int o = item - tb.blk0 * nb_per_tile;
+  const int nb = o / tb.nblk;
+  const int tidx = tb.blk0 + (o - nb * tb.nblk);
   const Tile tl = a.tiles[tidx];
   const int bank = tl.group < a.E ? 0 : 1;
   const int64_t ge = tl.group < a.E ? tl.group : 0;
@@ -185,6 +200,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
     }
   };
   const int wm = wave % WGM, wn = wave / WGM;
+  const bool live = wm * 16 * TM < tl.nrows;
   const int m16 = l & 15, g = l >> 4;
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -216,6 +232,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
     __builtin_amdgcn_s_barrier();
     if (kt + S - 1 < KT) issue_a(kt + S - 1);
     if (kt + SB - 1 < KT) issue_b(kt + SB - 1);
+    // a wavefront whose rows all lie past the tile's last row has nothing to multiply (it
+    // still moves its share of the DMA and meets every barrier)
+    if (!live) continue;
     const char* cur = smem + (kt % S) * ASTAGE;                 // activations of block kt
     const char* curb = smem + S * ASTAGE + (kt % SB) * BSTAGE;  // weights of block kt
     // MXFP4: this lane's 16 codes (elements 16 g .. 16 g + 15 of the K block) and scale
@@ -283,35 +302,39 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
 constexpr int kMXN = MOE_T2_WGN * 16 * MOE_T2_MX_TN;
 
 // SB: weight-ring stages of the gate/up launch, SBD of the down launch
-template <int TN, int S, int SB, int SBD, bool kMX>
+template <int TM, int TN, int WGM, int WGN, int S, int SB, int SBD, bool kMX>
 hipError_t launch_tiled_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
-  constexpr int BN = MOE_T2_WGN * 16 * TN;
+  constexpr int BN = WGN * 16 * TN;
   const int nb_gu = a.I_max / (BN / 2), nb_dn = a.H / BN;
-  const dim3 gu(a.max_tiles * nb_gu), dn(a.max_tiles * nb_dn), blk(kT2Threads);
-  hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, SB, true, false, kMX>), gu, blk, 0, s, a, nb_gu);
+  // whole rounds of kXcds workgroups, so that every chunk's last item has a workgroup
+  const dim3 gu((a.max_tiles * nb_gu + kXcds - 1) / kXcds * kXcds),
+      dn((a.max_tiles * nb_dn + kXcds - 1) / kXcds * kXcds), blk(64 * WGM * WGN);
+  hipLaunchKernelGGL((k_tiled2<TM, TN, WGM, WGN, S, SB, true, false, kMX>), gu, blk, 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
   if (a.y_dt == MOE_F32)
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, SBD, false, true, kMX>), dn, blk, 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_tiled2<TM, TN, WGM, WGN, S, SBD, false, true, kMX>), dn, blk, 0, s, a, nb_dn);
   else
-    hipLaunchKernelGGL((k_tiled2<MOE_T2_TM, TN, MOE_T2_WGM, MOE_T2_WGN, S, SBD, false, false, kMX>), dn, blk, 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_tiled2<TM, TN, WGM, WGN, S, SBD, false, false, kMX>), dn, blk, 0, s, a, nb_dn);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
+  // MXFP4: weight blocks of kMXN rows (gate/up: kMXN / 2 features) when every bank allows
+  auto fits = [&](int n) {
+    return a.H % n == 0 && a.bank[0].I % (n / 2) == 0 && (!a.has_shared || a.bank[1].I % (n / 2) == 0);
+  };
   if (a.wdt != MOE_MXFP4)
-    return launch_tiled_pair<MOE_T2_TN, MOE_T2_STAGES, MOE_T2_STAGES, MOE_T2_STAGES_B_DN, false>(
-        a, s, mid_event);
-  const bool wide = kMXN != kT2N && a.H % kMXN == 0 && a.bank[0].I % (kMXN / 2) == 0 &&
-                    (!a.has_shared || a.bank[1].I % (kMXN / 2) == 0);
-  if (wide)
-    return launch_tiled_pair<MOE_T2_MX_TN, MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, MOE_T2_MX_STAGES,
-                             true>(a, s, mid_event);
-  return launch_tiled_pair<MOE_T2_TN, MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, true>(
-      a, s, mid_event);
+    return launch_tiled_pair<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES,
+                             MOE_T2_STAGES_B_GU, MOE_T2_STAGES_B_DN, false>(a, s, mid_event);
+  if (kMXN != kT2N && fits(kMXN))
+    return launch_tiled_pair<MOE_T2_TM, MOE_T2_MX_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES,
+                             MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, true>(a, s, mid_event);
+  return launch_tiled_pair<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES,
+                           MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, true>(a, s, mid_event);
 }
 
 }  // namespace moe

@@ -34,11 +34,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // A row range of one group (expert): rows [row0, row0 + nrows) of the permuted row
 // space, all belonging to `group`. Groups 0..E-1 are routed experts; group E, when
 // present, is the shared expert. Built on the device by the permute scan kernel.
+// Consecutive tiles of one group are also cut into blocks of up to kTileBlock tiles; the
+// tiled GEMMs order their work items block by block (see ffn_tiled.hip).
+#ifndef MOE_TILE_BLOCK
+#define MOE_TILE_BLOCK 8
+#endif
+constexpr int kTileBlock = MOE_TILE_BLOCK;
 struct Tile {
   int32_t group;
   int32_t row0;
   int32_t nrows;
-  int32_t pad[5];  // 32-byte entries
+  int32_t blk0;    // index of the first tile of this tile's block
+  int32_t nblk;    // tiles in that block (1 .. kTileBlock)
+  int32_t pad[3];  // 32-byte entries
 };
 
 // Upper bound of the tile count for n_rows rows in n_groups groups with tiles of m rows.

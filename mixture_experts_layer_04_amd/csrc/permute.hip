@@ -61,6 +61,20 @@ __device__ int block_exclusive_scan(int v, int* sh, int* total) {
   return incl - v;
 }
 
+// Tile i of the nt tiles of group g (rows [row0, row0 + rows)), placed at index toff + i:
+// tile_m-row chunks, in blocks of up to kTileBlock consecutive tiles.
+__device__ Tile make_tile(int g, int row0, int rows, int i, int nt, int toff, int tile_m) {
+  Tile tl;
+  tl.group = g;
+  tl.row0 = row0 + i * tile_m;
+  tl.nrows = min(tile_m, rows - i * tile_m);
+  const int b0 = i / kTileBlock * kTileBlock;
+  tl.blk0 = toff + b0;
+  tl.nblk = min(kTileBlock, nt - b0);
+  tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
+  return tl;
+}
+
 __global__ void __launch_bounds__(kScanThreads) k_scan(int32_t* __restrict__ cnt, int nb, int E,
                                                        int T, int k, int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets,
@@ -123,14 +137,7 @@ __global__ void __launch_bounds__(kScanThreads) k_scan(int32_t* __restrict__ cnt
     nt = (rows + tile_m - 1) / tile_m;
     int ntot;
     const int toff = block_exclusive_scan(nt, sh, &ntot);
-    for (int i = 0; i < nt; ++i) {
-      Tile tl;
-      tl.group = e;
-      tl.row0 = row0 + i * tile_m;
-      tl.nrows = min(tile_m, rows - i * tile_m);
-      tl.pad[0] = tl.pad[1] = tl.pad[2] = tl.pad[3] = tl.pad[4] = 0;
-      tiles[toff + i] = tl;
-    }
+    for (int i = 0; i < nt; ++i) tiles[toff + i] = make_tile(e, row0, rows, i, nt, toff, tile_m);
     if (e == 0) *ntiles = ntot;
   }
 }
@@ -186,14 +193,7 @@ __global__ void __launch_bounds__(kScanThreads) k_tiles_from_offsets(const int32
   const int nt = (rows + tile_m - 1) / tile_m;
   int ntot;
   const int toff = block_exclusive_scan(nt, sh, &ntot);
-  for (int i = 0; i < nt; ++i) {
-    Tile tl;
-    tl.group = e;
-    tl.row0 = row0 + i * tile_m;
-    tl.nrows = min(tile_m, rows - i * tile_m);
-    tl.pad[0] = tl.pad[1] = tl.pad[2] = tl.pad[3] = tl.pad[4] = 0;
-    tiles[toff + i] = tl;
-  }
+  for (int i = 0; i < nt; ++i) tiles[toff + i] = make_tile(e, row0, rows, i, nt, toff, tile_m);
   if (e == 0) *ntiles = ntot;
 }
 

@@ -33,8 +33,7 @@ SMALL = [
               weight_seed=15),
     MoEConfig("bf16_f32_out_k16", T=70, H=256, E=40, k=16, I=128, score="sigmoid", use_bias=True,
               scale=2.5, out="f32", seed=16, weight_seed=16),
-    # more than 32 rows per expert: the LDS-tiled grouped GEMMs, with ragged 128-row tiles;
-    # H % 256 and I % 128 select the 128 x 256 kernel, other shapes the 128 x 128 one
+    # more than 32 rows per expert: the LDS-tiled grouped GEMMs with ragged 128-row tiles
     MoEConfig("bf16_t3_sigmoid_shared", T=900, H=512, E=10, k=3, I=256, score="sigmoid",
               use_bias=True, scale=2.5, shared_I=128, seed=19, weight_seed=19),
     MoEConfig("bf16_t3_softmax_f32out", T=1200, H=768, E=5, k=2, I=384, score="softmax",
@@ -43,6 +42,9 @@ SMALL = [
               use_bias=True, scale=2.5, shared_I=128, seed=17, weight_seed=17),
     MoEConfig("bf16_tiled_softmax_f32out", T=1000, H=384, E=6, k=2, I=128, score="softmax",
               out="f32", seed=18, weight_seed=18),
+    # a group of more tiles than one tile block (the shared expert's 2100 rows: nine tiles)
+    MoEConfig("bf16_tile_blocks", T=2100, H=512, E=3, k=1, I=128, score="sigmoid",
+              use_bias=True, scale=2.5, shared_I=128, out="f32", seed=21, weight_seed=21),
 ]
 
 
