@@ -51,9 +51,32 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// E8M0 scale byte -> its power of two as fp32 (0xFF is NaN; 0 is 2^-127, a subnormal).
+// Written as selects: with early returns the compiler branched on them lane by lane.
+__device__ __forceinline__ float e8m0_f32(uint32_t c) {
+  uint32_t bits = c << 23;
+  bits = c == 0u ? 0x00400000u : bits;     // 2^-127
+  bits = c == 0xFFu ? 0x7FC00000u : bits;  // NaN
+  return __uint_as_float(bits);
+}
+
+// Eight E2M1 values (one 32-bit word, low nibble first) times their E8M0 block scale, as
+// the bf16 fragment of one MFMA k-step (v_cvt_scalef32_pk_bf16_fp4 is exact: every
+// E2M1 value times a power of two in range is a bf16).
+__device__ __forceinline__ bf16x8 e2m1x8_bf16(uint32_t w, float scale) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // Launchers of the kernel families (FfnArgs as set up by launch_grouped_ffn; mid_event,
 // if not null, is recorded between the gate/up and the down launches).
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);
+// Whether the MXFP4 streaming kernels take this H and I (multiples of their K iteration).
+bool ffn_stream_mx_ok(int32_t H, int32_t I);
 hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);
 hipError_t launch_ffn_fp8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);
 

@@ -229,7 +229,223 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
   }
 }
 
+// ------------------------------------------------------------------ MXFP4 weights
+// The same streaming scheme for MXFP4 weights (E2M1 codes, 2 a byte, with an E8M0 scale
+// per 32 elements): per iteration each lane owns KL = 64 U contiguous elements of a weight
+// row -- 32 U bytes of codes (a 128-B line per 4 lanes for U = 1, two lines for U = 2),
+// 2 U scale bytes -- and the same KL elements of its activation row. Word i of the codes
+// (elements 8 i .. 8 i + 7) is decoded exactly to bf16 in registers and multiplied with
+// the activation's elements 8 i .. 8 i + 7 by one v_mfma_f32_16x16x32_bf16, so the K
+// index a (lane group, word) pair carries is the same in both operands.
+#ifndef MOE_STREAM_MX_U
+#define MOE_STREAM_MX_U 2
+#endif
+#ifndef MOE_STREAM_MX_ROWS_GU
+#define MOE_STREAM_MX_ROWS_GU 2
+#endif
+#ifndef MOE_STREAM_MX_ROWS_DN
+#define MOE_STREAM_MX_ROWS_DN 4
+#endif
+#ifndef MOE_STREAM_MX_PIPE
+#define MOE_STREAM_MX_PIPE 1
+#endif
+constexpr int kMxStreamK = 256 * MOE_STREAM_MX_U;  // K elements per iteration (divides H, I)
+
+template <int U>
+struct MxCodes {  // 32 U bytes of E2M1 codes and their 2 U E8M0 scale bytes
+  u32x4 q[2 * U];
+  uint32_t sc;
+};
+
+template <int U>
+__device__ __forceinline__ MxCodes<U> load_mx(const uint8_t* codes, const uint8_t* scales) {
+  MxCodes<U> c;
+#pragma unroll
+  for (int i = 0; i < 2 * U; ++i) c.q[i] = reinterpret_cast<const u32x4*>(codes)[i];
+  if (U == 2) c.sc = *reinterpret_cast<const uint32_t*>(scales);
+  else c.sc = *reinterpret_cast<const uint16_t*>(scales);
+  return c;
+}
+
+// acc += (decoded codes) x (8 U bf16x8 activation fragments)
+template <int U>
+__device__ __forceinline__ f32x4 mma_mx(const MxCodes<U>& w, const u32x4* x, f32x4 acc) {
+#pragma unroll
+  for (int i = 0; i < 8 * U; ++i) {
+    const float sc = e8m0_f32((w.sc >> (8 * (i >> 2))) & 0xFFu);
+    const bf16x8 a = e2m1x8_bf16(w.q[i >> 2][i & 3], sc);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(x[i]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+template <int U>
+__device__ __forceinline__ void load_x_mx(const char* p, bool valid, u32x4* x) {
+#pragma unroll
+  for (int i = 0; i < 8 * U; ++i)
+    x[i] = valid ? reinterpret_cast<const u32x4*>(p)[i] : u32x4{0, 0, 0, 0};
+}
+
+// Gate/up + SwiGLU: wavefront w computes features [f0, f0 + 16 R) of h from the gate rows
+// f0.. and the up rows I + f0.. of W13[e].
+template <int R, int U>
+__global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_tile) {
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int tile_id = blockIdx.x / fb_per_tile;
+  const int fb = blockIdx.x - tile_id * fb_per_tile;
+  if (tile_id >= *a.ntiles) return;
+  const Tile tl = a.tiles[tile_id];
+  const int bank = tl.group < a.E ? 0 : 1;
+  const int64_t ge = tl.group < a.E ? tl.group : 0;
+  const int I = a.bank[bank].I;
+  const int H = a.H;
+  const int f0 = (fb * 4 + wave) * 16 * R;
+  if (f0 >= I) return;
+  const int m = l & 15, kq = l >> 4;
+  constexpr int KL = 64 * U;
+  const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.bank[bank].w13) + ge * 2 * I * (int64_t)(H / 2);
+  const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.bank[bank].w13_scale) + ge * 2 * I * (int64_t)(H / 32);
+  const uint8_t *cg[R], *cu[R], *sg[R], *su[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t g = f0 + 16 * r + m, u = I + g;
+    cg[r] = codes + g * (H / 2) + kq * (KL / 2);
+    cu[r] = codes + u * (H / 2) + kq * (KL / 2);
+    sg[r] = scales + g * (H / 32) + kq * (KL / 32);
+    su[r] = scales + u * (H / 32) + kq * (KL / 32);
+  }
+  const bool xv = m < tl.nrows;
+  const int row = tl.row0 + (xv ? m : 0);
+  const int64_t src = a.a_rowmap ? a.a_rowmap[row] : row;
+  const char* xr = reinterpret_cast<const char*>(a.a) + src * H * 2 + kq * KL * 2;
+  f32x4 accg[R], accu[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) accg[r] = accu[r] = f32x4{0, 0, 0, 0};
+#if MOE_STREAM_MX_PIPE
+  // the codes of iteration k0 + KI are requested before iteration k0 is multiplied
+  MxCodes<U> wg[R], wu[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    wg[r] = load_mx<U>(cg[r], sg[r]);
+    wu[r] = load_mx<U>(cu[r], su[r]);
+  }
+  for (int k0 = 0; k0 < H; k0 += 256 * U) {
+    u32x4 x[8 * U];
+    load_x_mx<U>(xr + (int64_t)k0 * 2, xv, x);
+    MxCodes<U> ng[R], nu[R];
+    const int kn = k0 + 256 * U < H ? k0 + 256 * U : k0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      ng[r] = load_mx<U>(cg[r] + kn / 2, sg[r] + kn / 32);
+      nu[r] = load_mx<U>(cu[r] + kn / 2, su[r] + kn / 32);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      accg[r] = mma_mx<U>(wg[r], x, accg[r]);
+      accu[r] = mma_mx<U>(wu[r], x, accu[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      wg[r] = ng[r];
+      wu[r] = nu[r];
+    }
+  }
+#else
+  for (int k0 = 0; k0 < H; k0 += 256 * U) {
+    MxCodes<U> wg[R], wu[R];
+    u32x4 x[8 * U];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      wg[r] = load_mx<U>(cg[r] + k0 / 2, sg[r] + k0 / 32);
+      wu[r] = load_mx<U>(cu[r] + k0 / 2, su[r] + k0 / 32);
+    }
+    load_x_mx<U>(xr + (int64_t)k0 * 2, xv, x);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      accg[r] = mma_mx<U>(wg[r], x, accg[r]);
+      accu[r] = mma_mx<U>(wu[r], x, accu[r]);
+    }
+  }
+#endif
+  if (xv) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      f32x4 hv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[i] = silu_mul(accg[r][i], accu[r][i]);
+      store4<false>(a.h, (int64_t)(tl.row0 + m) * a.I_max + f0 + 16 * r + kq * 4, hv);
+    }
+  }
+}
+
+// Down projection: wavefront w computes output features [f0, f0 + 16 R) from W2[e] rows.
+template <bool kYF32, int R, int U>
+__global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_tile) {
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int tile_id = blockIdx.x / fb_per_tile;
+  const int fb = blockIdx.x - tile_id * fb_per_tile;
+  if (tile_id >= *a.ntiles) return;
+  const Tile tl = a.tiles[tile_id];
+  const int bank = tl.group < a.E ? 0 : 1;
+  const int64_t ge = tl.group < a.E ? tl.group : 0;
+  const int I = a.bank[bank].I;
+  const int H = a.H;
+  const int f0 = (fb * 4 + wave) * 16 * R;
+  if (f0 >= H) return;
+  const int m = l & 15, kq = l >> 4;
+  constexpr int KL = 64 * U;
+  const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.bank[bank].w2) + ge * (int64_t)H * (I / 2);
+  const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.bank[bank].w2_scale) + ge * (int64_t)H * (I / 32);
+  const uint8_t *cw[R], *sw[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t o = f0 + 16 * r + m;
+    cw[r] = codes + o * (I / 2) + kq * (KL / 2);
+    sw[r] = scales + o * (I / 32) + kq * (KL / 32);
+  }
+  const bool xv = m < tl.nrows;
+  const char* hr = reinterpret_cast<const char*>(a.h) +
+                   (int64_t)(tl.row0 + (xv ? m : 0)) * a.I_max * 2 + kq * KL * 2;
+  f32x4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4{0, 0, 0, 0};
+#if MOE_STREAM_MX_PIPE
+  MxCodes<U> w[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) w[r] = load_mx<U>(cw[r], sw[r]);
+  for (int k0 = 0; k0 < I; k0 += 256 * U) {
+    u32x4 x[8 * U];
+    load_x_mx<U>(hr + (int64_t)k0 * 2, xv, x);
+    MxCodes<U> nw[R];
+    const int kn = k0 + 256 * U < I ? k0 + 256 * U : k0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) nw[r] = load_mx<U>(cw[r] + kn / 2, sw[r] + kn / 32);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = mma_mx<U>(w[r], x, acc[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[r] = nw[r];
+  }
+#else
+  for (int k0 = 0; k0 < I; k0 += 256 * U) {
+    MxCodes<U> w[R];
+    u32x4 x[8 * U];
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[r] = load_mx<U>(cw[r] + k0 / 2, sw[r] + k0 / 32);
+    load_x_mx<U>(hr + (int64_t)k0 * 2, xv, x);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = mma_mx<U>(w[r], x, acc[r]);
+  }
+#endif
+  if (xv) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + 16 * r + kq * 4, acc[r]);
+  }
+}
+
 }  // namespace
+
+bool ffn_stream_mx_ok(int32_t H, int32_t I) { return H % kMxStreamK == 0 && I % kMxStreamK == 0; }
 
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
   constexpr int RG = MOE_STREAM_ROWS_GU, RD = MOE_STREAM_ROWS_DN;
@@ -238,6 +454,20 @@ hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_eve
   const bool f32 = a.wdt == MOE_F32;
   const bool yf32 = a.y_dt == MOE_F32;
   const dim3 blk(256);
+  if (a.wdt == MOE_MXFP4) {
+    constexpr int U = MOE_STREAM_MX_U, MG = MOE_STREAM_MX_ROWS_GU, MD = MOE_STREAM_MX_ROWS_DN;
+    const int fg = (a.I_max + kFeatPerWG * MG - 1) / (kFeatPerWG * MG);
+    const int fd = (a.H + kFeatPerWG * MD - 1) / (kFeatPerWG * MD);
+    hipLaunchKernelGGL((k_gateup_stream_mx<MG, U>), dim3(a.max_tiles * fg), blk, 0, s, a, fg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (mid_event && (e = hipEventRecord(mid_event, s)) != hipSuccess) return e;
+    if (yf32)
+      hipLaunchKernelGGL((k_down_stream_mx<true, MD, U>), dim3(a.max_tiles * fd), blk, 0, s, a, fd);
+    else
+      hipLaunchKernelGGL((k_down_stream_mx<false, MD, U>), dim3(a.max_tiles * fd), blk, 0, s, a, fd);
+    return hipGetLastError();
+  }
   if (f32)
     hipLaunchKernelGGL((k_gateup_stream<true, 1>), dim3(a.max_tiles * ((a.I_max + kFeatPerWG - 1) / kFeatPerWG)), blk, 0, s, a, (a.I_max + kFeatPerWG - 1) / kFeatPerWG);
   else

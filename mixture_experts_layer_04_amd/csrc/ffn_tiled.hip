@@ -59,24 +59,6 @@ constexpr int kT2Threads = 64 * MOE_T2_WGM * MOE_T2_WGN;
 constexpr int kT2M = MOE_T2_WGM * 16 * MOE_T2_TM, kT2N = MOE_T2_WGN * 16 * MOE_T2_TN;
 static_assert(kT2M == kTiledM && kT2N == kTiledN, "tile shape of the tile list");
 
-__device__ __forceinline__ float e8m0_f32(uint32_t c) {
-  if (c == 0xFFu) return __uint_as_float(0x7FC00000u);
-  if (c == 0u) return __uint_as_float(0x00400000u);  // 2^-127
-  return __uint_as_float(c << 23);
-}
-
-// Eight E2M1 values (one 32-bit word, low nibble first) times their E8M0 block scale, as
-// the bf16 fragment of one MFMA k-step (v_cvt_scalef32_pk_bf16_fp4 is exact: every
-// E2M1 value times a power of two in range is a bf16).
-__device__ __forceinline__ bf16x8 e2m1x8_bf16(uint32_t w, float scale) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
 // Workgroup of WGM x WGN wavefronts; each wavefront computes (16 TM) x (16 TN).
 // kMX: MXFP4 weights. A K block of a weight row is then 32 B of E2M1 codes plus 2 E8M0
 // scale bytes; the ring stages the codes (32 B a row: the 8-B quarter u of row r at

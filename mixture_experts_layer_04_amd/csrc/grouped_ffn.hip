@@ -30,7 +30,12 @@ bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I) {
 int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32_t I_routed,
                    int32_t I_shared) {
   if (wdt == MOE_FP8_E4M3) return kF8TileM;
-  if (wdt == MOE_MXFP4) return kTiledM;
+  // MXFP4: streaming kernels for few rows per expert where the shapes allow, else tiled
+  if (wdt == MOE_MXFP4)
+    return (int64_t)rows <= 32 * (int64_t)groups && ffn_stream_mx_ok(H, I_routed) &&
+                   (I_shared == 0 || ffn_stream_mx_ok(H, I_shared))
+               ? kStreamTileM
+               : kTiledM;
   // Few rows per expert: stream the weights (each weight element read once per tile of
   // <= 16 rows). Many rows: LDS-tiled GEMM with 128-row tiles.
   const bool tiled_ok =

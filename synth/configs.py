@@ -76,6 +76,14 @@ CONFIGS = {
     "ep32_mxfp4": MoEConfig("ep32_mxfp4", T=16384, H=7168, E=32, k=1, I=2048, score="none",
                             act="bf16", wdt="mxfp4", out="bf16", seed=5000, weight_seed=5000,
                             dirichlet_alpha=0.5),
+    # r1_decode with the expert weights in fp8 or MXFP4, the low-precision grouped GEMM
+    # formats of the GC-MoE record: same seeds, so the same router and routing
+    "r1_decode_fp8": MoEConfig("r1_decode_fp8", T=128, H=7168, E=256, k=8, I=2048,
+                               score="sigmoid", use_bias=True, scale=2.5, shared_I=2048,
+                               wdt="fp8", seed=2000, weight_seed=2000),
+    "r1_decode_mxfp4": MoEConfig("r1_decode_mxfp4", T=128, H=7168, E=256, k=8, I=2048,
+                                 score="sigmoid", use_bias=True, scale=2.5, shared_I=2048,
+                                 wdt="mxfp4", seed=2000, weight_seed=2000),
 }
 
 ORDER = ["tiny_fp32", "r1_decode", "r1_prefill", "e384_fp8", "ep32_mxfp4"]

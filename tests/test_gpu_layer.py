@@ -169,6 +169,25 @@ def test_r1_decode_full_size():
     assert np.isfinite(got["out"]).all()
 
 
+@pytest.mark.parametrize("name", ["r1_decode_fp8", "r1_decode_mxfp4"])
+def test_r1_decode_low_precision_full_size(name):
+    """r1_decode with fp8 or MXFP4 expert weights at its real size: the routing is the bf16
+    layer's, bit-exact; sampled tokens' outputs against the oracle's decode of the same
+    weights."""
+    cfg = CONFIGS[name]
+    print("case", describe(cfg), flush=True)
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
+    got = run_layer(cfg, dev)
+    tokens = [0, 77]
+    want = O.layer_forward(host, tokens=tokens)
+    check_routing(got, want, cfg)
+    err = O.rel_err(got["out"][tokens], want["out"])
+    print(name, "sampled rel err", err, flush=True)
+    assert err <= TOL[cfg.wdt]
+    assert np.isfinite(got["out"]).all()
+
+
 def test_r1_prefill_full_size():
     """DeepSeek-R1-shaped prefill layer with Zipf-skewed routing at its real size: routing of
     all 8192 tokens bit-exact, outputs of sampled tokens against the oracle."""
@@ -287,10 +306,24 @@ def test_rows_forward_timed_matches_untimed():
     assert st["route"] < 0.05 and all(v >= 0 for v in st.values()) and st["gate_up"] > 0
 
 
-def test_mxfp4_routed_layer_matches_oracle():
-    cfg = MoEConfig("mxfp4_routed_shared", T=300, H=256, E=8, k=2, I=128, score="sigmoid",
-                    use_bias=True, scale=2.5, shared_I=128, act="bf16", wdt="mxfp4", out="bf16",
-                    seed=53, weight_seed=53)
+MX_ROUTED = [
+    # many rows per expert: the tiled kernel
+    MoEConfig("mxfp4_routed_shared", T=300, H=256, E=8, k=2, I=128, score="sigmoid",
+              use_bias=True, scale=2.5, shared_I=128, act="bf16", wdt="mxfp4", out="bf16",
+              seed=53, weight_seed=53),
+    # decode-like (at most 32 rows per expert, H and I multiples of 512): the streaming
+    # kernels, with ragged 16-row tiles, an f32 output, and a shared expert
+    MoEConfig("mxfp4_stream_shared", T=40, H=1024, E=16, k=3, I=512, score="sigmoid",
+              use_bias=True, scale=2.5, shared_I=512, act="bf16", wdt="mxfp4", out="bf16",
+              seed=54, weight_seed=54),
+    MoEConfig("mxfp4_stream_f32out", T=9, H=512, E=6, k=2, I=1024, score="softmax",
+              act="bf16", wdt="mxfp4", out="f32", seed=55, weight_seed=55),
+]
+
+
+@pytest.mark.parametrize("cfg", MX_ROUTED, ids=lambda c: c.name)
+def test_mxfp4_routed_layer_matches_oracle(cfg):
+    print("case", describe(cfg), flush=True)
     host, dev = problems(cfg)
     got = run_layer(cfg, dev)
     want = O.layer_forward(host)
