@@ -108,7 +108,7 @@ def ffn_accounting(cfg, touched):
     """Algorithmic HBM bytes and flops of the grouped gate/up (+SwiGLU) and down launches:
     every touched expert's weights read once, every routed/shared row's input read once and
     its output written once; which of HBM or MFMA bounds each launch; the kernel the library
-    picks for it (fp8: k_fp8; MXFP4, and bf16 with more than 32 routed rows per expert on
+    picks for it (fp8: k_fp8; bf16 and MXFP4 with more than 32 routed rows per expert on
     average: k_tiled2; otherwise the streaming kernels)."""
     T, H, I, Is, k = cfg.T, cfg.H, cfg.I, cfg.shared_I, cfg.k
     rows_r = T * k if cfg.routed else T
@@ -124,6 +124,8 @@ def ffn_accounting(cfg, touched):
     fl_dn = 2.0 * (rows_r * I * H + (T * Is * H if Is else 0))
     if cfg.wdt == "fp8":
         kgu, kdn = "k_fp8<gate/up>", "k_fp8<down>"
+    elif cfg.wdt == "mxfp4" and rows_r <= 32 * cfg.E and H % 512 == 0 and I % 512 == 0:
+        kgu, kdn = "k_gateup_stream_mx", "k_down_stream_mx"
     elif cfg.wdt == "mxfp4":
         kgu, kdn = "k_tiled2<gate/up, MXFP4>", "k_tiled2<down, MXFP4>"
     elif cfg.wdt == "bf16" and rows_r > 32 * cfg.E:

@@ -231,12 +231,14 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
 
 // ------------------------------------------------------------------ MXFP4 weights
 // The same streaming scheme for MXFP4 weights (E2M1 codes, 2 a byte, with an E8M0 scale
-// per 32 elements): per iteration each lane owns KL = 64 U contiguous elements of a weight
-// row -- 32 U bytes of codes (a 128-B line per 4 lanes for U = 1, two lines for U = 2),
-// 2 U scale bytes -- and the same KL elements of its activation row. Word i of the codes
-// (elements 8 i .. 8 i + 7) is decoded exactly to bf16 in registers and multiplied with
-// the activation's elements 8 i .. 8 i + 7 by one v_mfma_f32_16x16x32_bf16, so the K
-// index a (lane group, word) pair carries is the same in both operands.
+// per 32 elements). An iteration covers 256 U elements of every weight row: 128 U bytes of
+// codes, read as 2 U loads of 64 contiguous bytes a row (16 B for each of the 4 lane
+// groups kq: load i gives lane group kq the 32 elements from 32 kq + 128 i), plus the
+// 8 U scale bytes of those elements (all lanes of a row load them; lane group kq uses
+// byte kq of each dword). Word w of a lane's codes is decoded exactly to bf16 in registers
+// and multiplied with the same 8 elements of the activation row by one
+// v_mfma_f32_16x16x32_bf16, so a (lane group, word) pair carries the same K index in both
+// operands.
 #ifndef MOE_STREAM_MX_U
 #define MOE_STREAM_MX_U 2
 #endif
@@ -246,44 +248,57 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
 #ifndef MOE_STREAM_MX_ROWS_DN
 #define MOE_STREAM_MX_ROWS_DN 4
 #endif
-#ifndef MOE_STREAM_MX_PIPE
-#define MOE_STREAM_MX_PIPE 1
-#endif
 constexpr int kMxStreamK = 256 * MOE_STREAM_MX_U;  // K elements per iteration (divides H, I)
 
 template <int U>
-struct MxCodes {  // 32 U bytes of E2M1 codes and their 2 U E8M0 scale bytes
+struct MxCodes {  // this lane's 32 U bytes of E2M1 codes and the row's 8 U scale bytes
   u32x4 q[2 * U];
-  uint32_t sc;
+  uint32_t sc[2 * U];
 };
 
+// codes: the row's codes at the iteration's start, already offset by 16 kq; scales: the
+// row's scale bytes at the iteration's start
 template <int U>
 __device__ __forceinline__ MxCodes<U> load_mx(const uint8_t* codes, const uint8_t* scales) {
   MxCodes<U> c;
 #pragma unroll
-  for (int i = 0; i < 2 * U; ++i) c.q[i] = reinterpret_cast<const u32x4*>(codes)[i];
-  if (U == 2) c.sc = *reinterpret_cast<const uint32_t*>(scales);
-  else c.sc = *reinterpret_cast<const uint16_t*>(scales);
+  for (int i = 0; i < 2 * U; ++i) c.q[i] = *reinterpret_cast<const u32x4*>(codes + 64 * i);
+  if (U == 2) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(scales);
+#pragma unroll
+    for (int i = 0; i < 2 * U; ++i) c.sc[i] = v[i];
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(scales);
+    c.sc[0] = v.x;
+    c.sc[1 % (2 * U)] = v.y;
+  }
   return c;
 }
 
-// acc += (decoded codes) x (8 U bf16x8 activation fragments)
+// acc += (decoded codes) x (8 U bf16x8 activation fragments); kq: this lane's group
 template <int U>
-__device__ __forceinline__ f32x4 mma_mx(const MxCodes<U>& w, const u32x4* x, f32x4 acc) {
+__device__ __forceinline__ f32x4 mma_mx(const MxCodes<U>& w, const u32x4* x, int kq, f32x4 acc) {
 #pragma unroll
-  for (int i = 0; i < 8 * U; ++i) {
-    const float sc = e8m0_f32((w.sc >> (8 * (i >> 2))) & 0xFFu);
-    const bf16x8 a = e2m1x8_bf16(w.q[i >> 2][i & 3], sc);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(x[i]), acc, 0, 0, 0);
+  for (int i = 0; i < 2 * U; ++i) {
+    const float sc = e8m0_f32((w.sc[i] >> (8 * kq)) & 0xFFu);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 a = e2m1x8_bf16(w.q[i][j], sc);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(x[4 * i + j]), acc, 0, 0, 0);
+    }
   }
   return acc;
 }
 
+// the activation elements that match a lane's codes: 32 from 32 kq + 128 i for each i
+// (p: the row at the iteration's start, already offset by 64 kq bytes)
 template <int U>
 __device__ __forceinline__ void load_x_mx(const char* p, bool valid, u32x4* x) {
 #pragma unroll
-  for (int i = 0; i < 8 * U; ++i)
-    x[i] = valid ? reinterpret_cast<const u32x4*>(p)[i] : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < 2 * U; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[4 * i + j] = valid ? *reinterpret_cast<const u32x4*>(p + 256 * i + 16 * j) : u32x4{0, 0, 0, 0};
 }
 
 // Gate/up + SwiGLU: wavefront w computes features [f0, f0 + 16 R) of h from the gate rows
@@ -302,55 +317,24 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
   const int f0 = (fb * 4 + wave) * 16 * R;
   if (f0 >= I) return;
   const int m = l & 15, kq = l >> 4;
-  constexpr int KL = 64 * U;
   const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.bank[bank].w13) + ge * 2 * I * (int64_t)(H / 2);
   const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.bank[bank].w13_scale) + ge * 2 * I * (int64_t)(H / 32);
   const uint8_t *cg[R], *cu[R], *sg[R], *su[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t g = f0 + 16 * r + m, u = I + g;
-    cg[r] = codes + g * (H / 2) + kq * (KL / 2);
-    cu[r] = codes + u * (H / 2) + kq * (KL / 2);
-    sg[r] = scales + g * (H / 32) + kq * (KL / 32);
-    su[r] = scales + u * (H / 32) + kq * (KL / 32);
+    cg[r] = codes + g * (H / 2) + 16 * kq;
+    cu[r] = codes + u * (H / 2) + 16 * kq;
+    sg[r] = scales + g * (H / 32);
+    su[r] = scales + u * (H / 32);
   }
   const bool xv = m < tl.nrows;
   const int row = tl.row0 + (xv ? m : 0);
   const int64_t src = a.a_rowmap ? a.a_rowmap[row] : row;
-  const char* xr = reinterpret_cast<const char*>(a.a) + src * H * 2 + kq * KL * 2;
+  const char* xr = reinterpret_cast<const char*>(a.a) + src * H * 2 + 64 * kq;
   f32x4 accg[R], accu[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) accg[r] = accu[r] = f32x4{0, 0, 0, 0};
-#if MOE_STREAM_MX_PIPE
-  // the codes of iteration k0 + KI are requested before iteration k0 is multiplied
-  MxCodes<U> wg[R], wu[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    wg[r] = load_mx<U>(cg[r], sg[r]);
-    wu[r] = load_mx<U>(cu[r], su[r]);
-  }
-  for (int k0 = 0; k0 < H; k0 += 256 * U) {
-    u32x4 x[8 * U];
-    load_x_mx<U>(xr + (int64_t)k0 * 2, xv, x);
-    MxCodes<U> ng[R], nu[R];
-    const int kn = k0 + 256 * U < H ? k0 + 256 * U : k0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      ng[r] = load_mx<U>(cg[r] + kn / 2, sg[r] + kn / 32);
-      nu[r] = load_mx<U>(cu[r] + kn / 2, su[r] + kn / 32);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      accg[r] = mma_mx<U>(wg[r], x, accg[r]);
-      accu[r] = mma_mx<U>(wu[r], x, accu[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      wg[r] = ng[r];
-      wu[r] = nu[r];
-    }
-  }
-#else
   for (int k0 = 0; k0 < H; k0 += 256 * U) {
     MxCodes<U> wg[R], wu[R];
     u32x4 x[8 * U];
@@ -362,11 +346,10 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
     load_x_mx<U>(xr + (int64_t)k0 * 2, xv, x);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      accg[r] = mma_mx<U>(wg[r], x, accg[r]);
-      accu[r] = mma_mx<U>(wu[r], x, accu[r]);
+      accg[r] = mma_mx<U>(wg[r], x, kq, accg[r]);
+      accu[r] = mma_mx<U>(wu[r], x, kq, accu[r]);
     }
   }
-#endif
   if (xv) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -393,39 +376,21 @@ __global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_ti
   const int f0 = (fb * 4 + wave) * 16 * R;
   if (f0 >= H) return;
   const int m = l & 15, kq = l >> 4;
-  constexpr int KL = 64 * U;
   const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.bank[bank].w2) + ge * (int64_t)H * (I / 2);
   const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.bank[bank].w2_scale) + ge * (int64_t)H * (I / 32);
   const uint8_t *cw[R], *sw[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t o = f0 + 16 * r + m;
-    cw[r] = codes + o * (I / 2) + kq * (KL / 2);
-    sw[r] = scales + o * (I / 32) + kq * (KL / 32);
+    cw[r] = codes + o * (I / 2) + 16 * kq;
+    sw[r] = scales + o * (I / 32);
   }
   const bool xv = m < tl.nrows;
   const char* hr = reinterpret_cast<const char*>(a.h) +
-                   (int64_t)(tl.row0 + (xv ? m : 0)) * a.I_max * 2 + kq * KL * 2;
+                   (int64_t)(tl.row0 + (xv ? m : 0)) * a.I_max * 2 + 64 * kq;
   f32x4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4{0, 0, 0, 0};
-#if MOE_STREAM_MX_PIPE
-  MxCodes<U> w[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) w[r] = load_mx<U>(cw[r], sw[r]);
-  for (int k0 = 0; k0 < I; k0 += 256 * U) {
-    u32x4 x[8 * U];
-    load_x_mx<U>(hr + (int64_t)k0 * 2, xv, x);
-    MxCodes<U> nw[R];
-    const int kn = k0 + 256 * U < I ? k0 + 256 * U : k0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) nw[r] = load_mx<U>(cw[r] + kn / 2, sw[r] + kn / 32);
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = mma_mx<U>(w[r], x, acc[r]);
-#pragma unroll
-    for (int r = 0; r < R; ++r) w[r] = nw[r];
-  }
-#else
   for (int k0 = 0; k0 < I; k0 += 256 * U) {
     MxCodes<U> w[R];
     u32x4 x[8 * U];
@@ -433,9 +398,8 @@ __global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_ti
     for (int r = 0; r < R; ++r) w[r] = load_mx<U>(cw[r] + k0 / 2, sw[r] + k0 / 32);
     load_x_mx<U>(hr + (int64_t)k0 * 2, xv, x);
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = mma_mx<U>(w[r], x, acc[r]);
+    for (int r = 0; r < R; ++r) acc[r] = mma_mx<U>(w[r], x, kq, acc[r]);
   }
-#endif
   if (xv) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
