@@ -10,9 +10,10 @@
 // unbiased scores.
 //
 // Kernel 1 (k_router_gemm): logits partial sums on the fp64 matrix cores
-//   (v_mfma_f64_16x16x4_f64). One wavefront per 16-token x 16-expert tile and K-split;
-//   each lane loads 16 contiguous bytes of its token row and of its expert row and feeds
-//   8 MFMAs, so loads are 16 B/lane and every input element is read once per tile.
+//   (v_mfma_f64_16x16x4_f64). One wavefront per K split and per tile of 16 tokens x 16
+//   experts, or of 4 x 2 such tiles for large batches; each lane loads 16 contiguous bytes
+//   of each of its token and expert rows, and each loaded fragment feeds 8 MFMAs per tile
+//   it belongs to.
 // Kernel 2 (k_topk): one wavefront per token; sums the K-split partials in a fixed order
 //   (deterministic), rounds to fp32, scores, and selects k experts by k rounds of a
 //   64-lane max over packed (key, expert) 64-bit values.
@@ -37,41 +38,77 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, double* v) 
   }
 }
 
-// part[s][t][e] = sum over k in split s of x[t,k] * wr[e,k], in fp64.
-template <bool kBF16>
+// K splits are added until about this many wavefronts run (four a SIMD).
+constexpr int kRouterWaves = 4096;
+// Tokens from which a wavefront takes 4 x 2 tiles (each token fragment feeds 2 tiles,
+// each expert fragment 4); below it, one tile.
+constexpr int kRouterBigT = 512;
+
+// part[s][t][e] = sum over k in split s of x[t,k] * wr[e,k], in fp64; a wavefront computes
+// kRT x kRE tiles of 16 tokens x 16 experts.
+template <bool kBF16, int kRT, int kRE>
 __global__ void __launch_bounds__(64) k_router_gemm(const void* __restrict__ x,
                                                      const void* __restrict__ wr, int T, int H,
                                                      int E, int klen, double* __restrict__ part) {
   const int l = threadIdx.x;
   const int m = l & 15, kq = l >> 4;
-  const int t = blockIdx.y * 16 + m;
-  const int e = blockIdx.x * 16 + m;
-  const int64_t xrow = (int64_t)(t < T ? t : T - 1) * H;
-  const int64_t wrow = (int64_t)(e < E ? e : E - 1) * H;
+  const int t0 = blockIdx.y * 16 * kRT, e0 = blockIdx.x * 16 * kRE;
+  int64_t xrow[kRT], wrow[kRE];
+#pragma unroll
+  for (int i = 0; i < kRT; ++i) {
+    const int t = t0 + 16 * i + m;
+    xrow[i] = (int64_t)(t < T ? t : T - 1) * H;
+  }
+#pragma unroll
+  for (int j = 0; j < kRE; ++j) {
+    const int e = e0 + 16 * j + m;
+    wrow[j] = (int64_t)(e < E ? e : E - 1) * H;
+  }
   const int kb = blockIdx.z * klen;
   const int ke = min(H, kb + klen);
-  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  f64x4 acc[kRT][kRE];
+#pragma unroll
+  for (int i = 0; i < kRT; ++i)
+#pragma unroll
+    for (int j = 0; j < kRE; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
   for (int k0 = kb; k0 < ke; k0 += 32) {
     const int kk = k0 + kq * 8;
-    double a[8], b[8];
+    double a[kRT][8], b[kRE][8];
     if (kk < ke) {
-      load8<kBF16>(x, xrow + kk, a);
-      load8<kBF16>(wr, wrow + kk, b);
+#pragma unroll
+      for (int i = 0; i < kRT; ++i) load8<kBF16>(x, xrow[i] + kk, a[i]);
+#pragma unroll
+      for (int j = 0; j < kRE; ++j) load8<kBF16>(wr, wrow[j] + kk, b[j]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) { a[j] = 0.0; b[j] = 0.0; }
+      for (int q = 0; q < 8; ++q) {
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) a[i][q] = 0.0;
+#pragma unroll
+        for (int j = 0; j < kRE; ++j) b[j][q] = 0.0;
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[j], b[j], acc, 0, 0, 0);
-  }
-  // the f64 16x16x4 MFMA leaves D[row kq + 4*i][column m] in lane l, register i
-  // (unlike the 16x16 f32-accumulating forms, whose rows are 4*kq + i)
-  const int eo = blockIdx.x * 16 + m;
+    for (int q = 0; q < 8; ++q)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int to = blockIdx.y * 16 + kq + 4 * i;
-    if (to < T && eo < E) part[((int64_t)blockIdx.z * T + to) * E + eo] = acc[i];
+      for (int i = 0; i < kRT; ++i)
+#pragma unroll
+        for (int j = 0; j < kRE; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i][q], b[j][q], acc[i][j], 0, 0, 0);
   }
+  // the f64 16x16x4 MFMA leaves D[row kq + 4*r][column m] in lane l, register r
+  // (unlike the 16x16 f32-accumulating forms, whose rows are 4*kq + r)
+#pragma unroll
+  for (int i = 0; i < kRT; ++i)
+#pragma unroll
+    for (int j = 0; j < kRE; ++j) {
+      const int eo = e0 + 16 * j + m;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int to = t0 + 16 * i + kq + 4 * r;
+        if (to < T && eo < E) part[((int64_t)blockIdx.z * T + to) * E + eo] = acc[i][j][r];
+      }
+    }
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
@@ -198,9 +235,16 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
   }
 }
 
+void router_tiles(int32_t T, int* tt, int* te) {
+  *tt = T >= kRouterBigT ? 4 : 1;
+  *te = T >= kRouterBigT ? 2 : 1;
+}
+
 int route_splits(int32_t T, int32_t H, int32_t E, int* klen) {
-  const int64_t tiles = (int64_t)((E + 15) / 16) * ((T + 15) / 16);
-  int64_t s = (1024 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  int tt, te;
+  router_tiles(T, &tt, &te);
+  const int64_t tiles = (int64_t)((E + 16 * te - 1) / (16 * te)) * ((T + 16 * tt - 1) / (16 * tt));
+  int64_t s = (kRouterWaves + tiles - 1) / (tiles > 0 ? tiles : 1);
   int64_t smax = H / 256 > 1 ? H / 256 : 1;
   if (s > smax) s = smax;
   if (s < 1) s = 1;
@@ -226,11 +270,17 @@ hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const flo
   int klen;
   int S = route_splits(T, H, E, &klen);
   double* part = reinterpret_cast<double*>(ws);
-  dim3 g1((E + 15) / 16, (T + 15) / 16, S);
-  if (x_dt == MOE_BF16)
-    hipLaunchKernelGGL(k_router_gemm<true>, g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
+  int tt, te;
+  router_tiles(T, &tt, &te);
+  const dim3 g1((E + 16 * te - 1) / (16 * te), (T + 16 * tt - 1) / (16 * tt), S);
+  if (x_dt == MOE_BF16 && tt == 4)
+    hipLaunchKernelGGL((k_router_gemm<true, 4, 2>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
+  else if (x_dt == MOE_BF16)
+    hipLaunchKernelGGL((k_router_gemm<true, 1, 1>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
+  else if (tt == 4)
+    hipLaunchKernelGGL((k_router_gemm<false, 4, 2>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
   else
-    hipLaunchKernelGGL(k_router_gemm<false>, g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
+    hipLaunchKernelGGL((k_router_gemm<false, 1, 1>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, part, S, T, E, k, (int)fn, scale,
