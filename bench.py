@@ -245,6 +245,21 @@ def main():
     stage_ms = {s_: float(np.mean(v)) for s_, v in stage.items()}
     log("stage ms: " + ", ".join(f"{s_}={v:.4f}" for s_, v in stage_ms.items()))
 
+    # the same step with the shared expert on a side stream beside the routed experts
+    ovl_ms = None
+    if cfg.routed and cfg.shared_I:
+        fj = moe.ForkJoin()
+        for _ in range(args.warmup):
+            layer.forward_overlap(dev.x, out, fj, counts=counts)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            layer.forward_overlap(dev.x, out, fj, counts=counts)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ovl_ms = start.elapsed_time(stop) / args.steps
+        log(f"overlapped shared expert: {ovl_ms:.4f} ms/step")
+
     # the selection-bias balancing step (not part of the forward step): its own timing
     bias_us = None
     if cfg.routed and cfg.use_bias:
@@ -306,7 +321,8 @@ def main():
                    "layer_algorithmic_bytes": layer_bytes, "layer_flops": layer_flops,
                    "layer_hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                    "down_frac": acct["down"]["frac_fn"](stage_ms["down"] / 1e3),
-                   "bias_update_us": bias_us},
+                   "bias_update_us": bias_us,
+                   "ms_per_step_shared_overlapped": ovl_ms},
         "roofline": {"bound": g["bound"], "kernel": f"grouped gate/up + SwiGLU ({g['kernel']})",
                      "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
                      "traffic": measured_traffic(cfg.name),

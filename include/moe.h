@@ -178,6 +178,23 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, void* out,
                              int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
                              float* logits_out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer_forward with the always-on shared expert run beside the rest: its grouped FFN
+ * goes on side_stream, forked after `stream`'s earlier work and joined back before the
+ * combine, so it overlaps the router, the permutation and the routed experts (the
+ * single-GPU counterpart of the concurrent shared-expert node in the CUDA-graph design of
+ * "GC-MoE: Overlapping Expert-Parallel Token Dispatch with FP8/FP4 Grouped GEMM via CUDA
+ * Green Contexts", key_changes, second item). Same arguments, checks, workspace size and
+ * results (bit for bit) as moe_layer_forward, plus:
+ *   side_stream  a hipStream_t other than `stream` (NULL is the default stream);
+ *   fork_event, join_event  hipEvent_t created by the caller (timing may be disabled);
+ *                MOE_ERR_NULL if either is NULL.
+ * Only events are recorded and waited on, so the pair of streams can be captured into a
+ * HIP graph from `stream`. Without a shared expert this is moe_layer_forward. */
+moe_status moe_layer_forward_overlap(const moe_layer_desc* d, const void* x, void* out,
+                                     int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                                     float* logits_out, void* ws, size_t ws_bytes, void* stream,
+                                     void* side_stream, void* fork_event, void* join_event);
+
 /* moe_layer_forward with stage timing: `events` points to MOE_STAGE_EVENTS hipEvent_t
  * handles created by the caller (hipEventCreate); they are recorded on `stream` at the
  * stage boundaries  [0] route [1] permute [2] gate/up+SwiGLU [3] down [4] combine [5],

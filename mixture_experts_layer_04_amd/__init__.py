@@ -53,6 +53,7 @@ _lib = None
 EXPORTS = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
            "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_timed",
+           "moe_layer_forward_overlap",
            "moe_rows_workspace_size",
            "moe_rows_forward", "moe_rows_forward_timed", "moe_quantize_fp8", "moe_bias_update",
            "moe_status_str",
@@ -83,13 +84,16 @@ def lib():
     L.moe_layer_forward.argtypes = [P(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_layer_forward_timed.argtypes = [P(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                           P(vp)]
+    L.moe_layer_forward_overlap.argtypes = [P(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                            vp, vp, vp]
     L.moe_rows_workspace_size.argtypes = [P(moe_experts), ci, i32]
     L.moe_rows_workspace_size.restype = sz
     L.moe_rows_forward.argtypes = [P(moe_experts), vp, ci, vp, vp, i32, vp, ci, vp, sz, vp]
     L.moe_rows_forward_timed.argtypes = [P(moe_experts), vp, ci, vp, vp, i32, vp, ci, vp, sz, vp,
                                          P(vp)]
     for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
-              "moe_layer_forward", "moe_layer_forward_timed", "moe_rows_forward",
+              "moe_layer_forward", "moe_layer_forward_timed", "moe_layer_forward_overlap",
+              "moe_rows_forward",
               "moe_rows_forward_timed"):
         getattr(L, f).restype = ci
     L.moe_quantize_fp8.argtypes = [vp, i32, i32, vp, vp, vp]
@@ -270,6 +274,38 @@ def moe_layer_forward_timed(desc: moe_layer_desc, x, out, ws, events: StageEvent
     _check(st, "moe_layer_forward_timed")
 
 
+class ForkJoin:
+    """A side stream and the fork/join event pair moe_layer_forward_overlap takes."""
+
+    def __init__(self, device=None):
+        self.side = torch.cuda.Stream(device=device)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(2):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(h), 0x2) != 0:  # timing disabled
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(h)
+
+    def __del__(self):
+        try:
+            for h in self.ev:
+                self.hip.hipEventDestroy(h)
+        except Exception:
+            pass
+
+
+def moe_layer_forward_overlap(desc: moe_layer_desc, x, out, ws, fj: ForkJoin, topk_idx=None,
+                              topk_w=None, counts=None, logits=None, stream=None):
+    st = lib().moe_layer_forward_overlap(ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(topk_idx),
+                                         _ptr(topk_w), _ptr(counts), _ptr(logits), _ptr(ws),
+                                         ws.numel(), _stream(stream), _stream(fj.side), fj.ev[0],
+                                         fj.ev[1])
+    _check(st, "moe_layer_forward_overlap")
+
+
 def moe_quantize_fp8(x, q, q_scale, stream=None):
     n, H = x.shape
     st = lib().moe_quantize_fp8(_ptr(x), n, H, _ptr(q), _ptr(q_scale), _stream(stream))
@@ -321,4 +357,10 @@ class MoELayer:
 
     def forward(self, x, out, topk_idx=None, topk_w=None, counts=None, logits=None, stream=None):
         moe_layer_forward(self.desc, x, out, self.ws, topk_idx, topk_w, counts, logits, stream)
+        return out
+
+    def forward_overlap(self, x, out, fj: ForkJoin, topk_idx=None, topk_w=None, counts=None,
+                        logits=None, stream=None):
+        moe_layer_forward_overlap(self.desc, x, out, self.ws, fj, topk_idx, topk_w, counts, logits,
+                                  stream)
         return out

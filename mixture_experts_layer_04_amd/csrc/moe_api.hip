@@ -92,6 +92,9 @@ void plan_ffn(Carve& c, FfnPlan& p, moe_dtype wdt, moe_dtype act, int32_t H, int
 struct LayerPlan {
   size_t o_route = 0, o_idx = 0, o_w = 0, o_counts = 0, o_offsets = 0, o_perm_src = 0,
          o_inv_perm = 0, o_row_token = 0, o_perm_ws = 0, o_xq = 0, o_xqs = 0;
+  // the shared group's own tile list, for the launch that runs beside the routed experts
+  size_t o_sh_tiles = 0, o_sh_ntiles = 0;
+  int32_t sh_max_tiles = 0;
   FfnPlan ffn;
   size_t total = 0;
 };
@@ -117,6 +120,11 @@ LayerPlan plan_layer(const moe_layer_desc* d) {
   }
   plan_ffn(c, p.ffn, d->routed.dtype, d->act_dtype, H, d->routed.I, shared ? d->shared.I : 0,
            (int32_t)rows, E, shared ? T : 0, true);
+  if (shared) {
+    p.sh_max_tiles = (T + p.ffn.tile_m - 1) / p.ffn.tile_m;
+    p.o_sh_tiles = c.take((size_t)(p.sh_max_tiles > 0 ? p.sh_max_tiles : 1) * sizeof(Tile));
+    p.o_sh_ntiles = c.take(sizeof(int32_t));
+  }
   p.total = c.off;
   return p;
 }
@@ -348,10 +356,17 @@ moe_status moe_layer_workspace_size(const moe_layer_desc* d, size_t* bytes) {
   return MOE_OK;
 }
 
+// side != nullptr: the shared expert runs on `side` between the fork and join events,
+// beside route, permute and the routed experts on `stream`.
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
+
 static moe_status layer_forward(const moe_layer_desc* d, const void* x, void* out,
                                 int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
                                 float* logits_out, void* ws, size_t ws_bytes, void* stream,
-                                void* const* events) {
+                                void* const* events, const SideStream* side = nullptr) {
   moe_status st = check_layer(d);
   if (st != MOE_OK) return st;
   if (!ws || (d->T > 0 && (!x || !out))) return MOE_ERR_NULL;
@@ -379,23 +394,8 @@ static moe_status layer_forward(const moe_layer_desc* d, const void* x, void* ou
 #define MOE_MARK(i)                                                                    \
   if (events && (e = hipEventRecord(ev[i], s)) != hipSuccess)                         \
     return hip_fail(e, "moe_layer_forward event");
-  MOE_MARK(0);
-  e = launch_route(x, d->act_dtype, d->w_router, d->bias, T, H, E, k, d->score_fn,
-                              d->route_scale, idx, w, logits_out, base + p.o_route, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward route");
-  MOE_MARK(1);
-  e = launch_permute_maps(idx, T, k, E, counts, offsets, perm_src, inv_perm, row_token,
-                          reinterpret_cast<Tile*>(base + p.ffn.o_tiles),
-                          reinterpret_cast<int32_t*>(base + p.ffn.o_ntiles), p.ffn.tile_m,
-                          shared ? 1 : 0, base + p.o_perm_ws, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward permute");
   const bool fp8 = d->routed.dtype == MOE_FP8_E4M3;
-  if (fp8) {
-    e = launch_quant_rows_fp8(x, T, H, reinterpret_cast<uint8_t*>(base + p.o_xq),
-                              reinterpret_cast<float*>(base + p.o_xqs), s);
-    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward quantise");
-  }
-  MOE_MARK(2);
+  const bool beside = side && shared && T > 0;
   void* y = base + p.ffn.o_y;
   FfnArgs f = ffn_args(p.ffn, base, d->routed, shared ? &d->shared : nullptr, d->act_dtype, H, x,
                        row_token, y);
@@ -403,8 +403,49 @@ static moe_status layer_forward(const moe_layer_desc* d, const void* x, void* ou
     f.a_q = reinterpret_cast<const uint8_t*>(base + p.o_xq);
     f.a_qscale = reinterpret_cast<const float*>(base + p.o_xqs);
   }
+  MOE_MARK(0);
+  if (fp8 && beside) {  // the shared launch reads the quantised activations too
+    e = launch_quant_rows_fp8(x, T, H, reinterpret_cast<uint8_t*>(base + p.o_xq),
+                              reinterpret_cast<float*>(base + p.o_xqs), s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward quantise");
+  }
+  if (beside) {
+    if ((e = hipEventRecord(side->fork, s)) != hipSuccess ||
+        (e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess)
+      return hip_fail(e, "moe_layer_forward fork");
+    Tile* sh_tiles = reinterpret_cast<Tile*>(base + p.o_sh_tiles);
+    int32_t* sh_nt = reinterpret_cast<int32_t*>(base + p.o_sh_ntiles);
+    e = launch_shared_group(T, k, E, p.ffn.tile_m, row_token, sh_tiles, sh_nt, side->s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward shared rows");
+    FfnArgs fs = f;
+    fs.tiles = sh_tiles;
+    fs.ntiles = sh_nt;
+    fs.max_tiles = p.sh_max_tiles;
+    e = launch_grouped_ffn(fs, base + p.ffn.o_scratch, side->s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward shared ffn");
+    if ((e = hipEventRecord(side->join, side->s)) != hipSuccess)
+      return hip_fail(e, "moe_layer_forward join");
+  }
+  e = launch_route(x, d->act_dtype, d->w_router, d->bias, T, H, E, k, d->score_fn,
+                              d->route_scale, idx, w, logits_out, base + p.o_route, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward route");
+  MOE_MARK(1);
+  e = launch_permute_maps(idx, T, k, E, counts, offsets, perm_src, inv_perm, row_token,
+                          reinterpret_cast<Tile*>(base + p.ffn.o_tiles),
+                          reinterpret_cast<int32_t*>(base + p.ffn.o_ntiles), p.ffn.tile_m,
+                          shared && !beside ? 1 : 0, base + p.o_perm_ws, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward permute");
+  if (fp8 && !beside) {
+    e = launch_quant_rows_fp8(x, T, H, reinterpret_cast<uint8_t*>(base + p.o_xq),
+                              reinterpret_cast<float*>(base + p.o_xqs), s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward quantise");
+  }
+  MOE_MARK(2);
+  if (beside) f.max_tiles = p.ffn.max_tiles - p.sh_max_tiles;  // routed groups only
   e = launch_grouped_ffn(f, base + p.ffn.o_scratch, s, events ? ev[3] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "moe_layer_forward grouped_ffn");
+  if (beside && (e = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess)
+    return hip_fail(e, "moe_layer_forward join");
   MOE_MARK(4);
   const void* ysh = shared ? reinterpret_cast<const char*>(y) +
                                  (size_t)T * k * H * dt_bytes(p.ffn.y_dt)
@@ -421,6 +462,16 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, void* out,
                              float* logits_out, void* ws, size_t ws_bytes, void* stream) {
   return layer_forward(d, x, out, topk_idx_out, topk_w_out, counts_out, logits_out, ws, ws_bytes,
                        stream, nullptr);
+}
+
+moe_status moe_layer_forward_overlap(const moe_layer_desc* d, const void* x, void* out,
+                                     int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                                     float* logits_out, void* ws, size_t ws_bytes, void* stream,
+                                     void* side_stream, void* fork_event, void* join_event) {
+  if (!fork_event || !join_event) return MOE_ERR_NULL;
+  const SideStream side{(hipStream_t)side_stream, (hipEvent_t)fork_event, (hipEvent_t)join_event};
+  return layer_forward(d, x, out, topk_idx_out, topk_w_out, counts_out, logits_out, ws, ws_bytes,
+                       stream, nullptr, &side);
 }
 
 moe_status moe_layer_forward_timed(const moe_layer_desc* d, const void* x, void* out,

@@ -114,6 +114,9 @@ hipError_t launch_permute_maps(const int32_t* topk_idx, int32_t T, int32_t k, in
 hipError_t launch_gather_rows(const void* x, int32_t elem_bytes, int32_t H,
                               const int32_t* perm_src, int32_t k, int32_t rows, void* x_perm,
                               hipStream_t s);
+// Row map and tile list of the shared group alone (rows T*k .. T*k + T - 1, group E).
+hipError_t launch_shared_group(int32_t T, int32_t k, int32_t E, int32_t tile_m, int32_t* row_token,
+                               Tile* tiles, int32_t* ntiles, hipStream_t s);
 // Tile list straight from a device offsets array (grouped FFN called on its own).
 hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* tiles,
                                      int32_t* ntiles, int32_t tile_m, hipStream_t s);

@@ -170,6 +170,18 @@ __global__ void k_shared_rows(int32_t* __restrict__ row_token, int T, int k) {
   if (i < T) row_token[(int64_t)T * k + i] = i;
 }
 
+// The shared expert's group on its own: row_token of rows T*k .. T*k + T - 1 (token i at
+// row T*k + i) and the tile list of that one group (group E), for a grouped-FFN launch that
+// runs beside the routed one.
+__global__ void k_shared_group(int32_t* __restrict__ row_token, int T, int k, int E, int tile_m,
+                               Tile* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nt = (T + tile_m - 1) / tile_m;
+  if (i < T) row_token[(int64_t)T * k + i] = i;
+  if (i < nt) tiles[i] = make_tile(E, T * k, T, i, nt, 0, tile_m);
+  if (i == 0) *ntiles = nt;
+}
+
 __global__ void __launch_bounds__(256) k_gather(const uint4* __restrict__ x, int vec_per_row,
                                                 const int32_t* __restrict__ perm_src, int k,
                                                 int rows, uint4* __restrict__ xp) {
@@ -245,6 +257,14 @@ hipError_t launch_gather_rows(const void* x, int32_t elem_bytes, int32_t H,
   const int gx = (vec + 255) / 256;
   hipLaunchKernelGGL(k_gather, dim3(rows, gx), dim3(256), 0, s, reinterpret_cast<const uint4*>(x),
                      vec, perm_src, k, rows, reinterpret_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_group(int32_t T, int32_t k, int32_t E, int32_t tile_m, int32_t* row_token,
+                               Tile* tiles, int32_t* ntiles, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_shared_group, dim3((T + 255) / 256), dim3(256), 0, s, row_token, T, k, E,
+                     tile_m, tiles, ntiles);
   return hipGetLastError();
 }
 

@@ -198,3 +198,15 @@ def test_bias_update_validation():
     assert L.moe_bias_update(P, 8, 0.01, None, None) == moe.MOE_ERR_NULL
     assert L.moe_bias_update(MISALIGNED, 8, 0.01, P, None) == moe.MOE_ERR_ALIGN
     assert L.moe_bias_update(P, 8, 0.01, MISALIGNED, None) == moe.MOE_ERR_ALIGN
+
+
+def test_layer_overlap_needs_both_events():
+    L = moe.lib()
+    d = desc(T=16)
+    n = ws_size(d)[1]
+    for fork, join in ((None, P), (P, None), (None, None)):
+        assert L.moe_layer_forward_overlap(ctypes.byref(d), P, P, None, None, None, None, P, n,
+                                           None, None, fork, join) == moe.MOE_ERR_NULL
+    # the same argument checks as moe_layer_forward come first after the events
+    assert L.moe_layer_forward_overlap(ctypes.byref(d), P, P, None, None, None, None, P, 16,
+                                       None, None, P, P) == moe.MOE_ERR_WORKSPACE
