@@ -120,6 +120,49 @@ def quantise_rows_e4m3(v32: np.ndarray, block: int = 128):
     return codes, s, deq.reshape(R, C)
 
 
+def _e2m1_grid() -> np.ndarray:
+    """The 8 non-negative E2M1 values, indexed by their code 0..7."""
+    return e2m1_to_f64(np.arange(8, dtype=np.uint8))
+
+
+def encode_e2m1_rne_sat(v: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code (a nibble) to each value, ties to the even code, magnitudes beyond
+    6 clamped to 6: the nearest point of the value grid, written as the definition."""
+    v = np.asarray(v, np.float64)
+    grid = _e2m1_grid()
+    a = np.minimum(np.abs(v), grid[-1])
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, 7)
+    lo = np.clip(hi - 1, 0, 7)
+    dlo = a - grid[lo]
+    dhi = grid[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a == grid[hi], hi, code).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x8, code).astype(np.uint8)
+
+
+def quantise_rows_mxfp4(v32: np.ndarray, block: int = 32):
+    """Per-row, per-32-column MXFP4 quantisation of fp32 values (the W4A4 path).
+
+    Reading, from the OCP MX format the FP4 grouped GEMM of GC-MoE uses (the pages fix no
+    recipe): the block's shared scale is 2^e with e = floor(log2(amax)) - 2, where 2 is the
+    exponent of E2M1's largest value 6 (e clamped to [-127, 127]; e = 0 for an all-zero
+    block); each element's code is E2M1(v / 2^e), round to nearest even, saturating at 6.
+    Returns (codes uint8 nibbles [R, C], E8M0 scale codes uint8 [R, C/block], dequantised
+    f64 [R, C]).
+    """
+    v = np.asarray(v32, np.float32).astype(np.float64)
+    R, C = v.shape
+    vb = v.reshape(R, C // block, block)
+    amax = np.abs(vb).max(axis=2)
+    _, ex = np.frexp(amax)                    # amax = m * 2^ex, m in [0.5, 1)
+    e = np.where(amax == 0, 0, np.clip(ex - 1 - 2, -127, 127)).astype(np.int64)
+    scale = np.exp2(e.astype(np.float64))
+    codes = encode_e2m1_rne_sat(vb / scale[:, :, None]).reshape(R, C)
+    deq = (e2m1_to_f64(codes).reshape(R, C // block, block) * scale[:, :, None]).reshape(R, C)
+    return codes, (e + 127).astype(np.uint8), deq
+
+
 def decode_matrix(fmt: str, part: dict) -> np.ndarray:
     """One expert matrix [R, C] in storage format -> float64.
 
@@ -136,7 +179,7 @@ def decode_matrix(fmt: str, part: dict) -> np.ndarray:
         s = np.asarray(part["scale"], np.float32).astype(np.float64)
         full = np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
         return e4m3_to_f64(w) * full
-    if fmt == "mxfp4":
+    if fmt in ("mxfp4", "mxfp4a4"):
         p = np.asarray(w, np.uint8)
         R = p.shape[0]
         C = p.shape[1] * 2
@@ -274,16 +317,19 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(a64: np.ndarray, w13_64: np.ndarray, w2_64: np.ndarray, requant_h: bool = False):
+def expert_ffn(a64: np.ndarray, w13_64: np.ndarray, w2_64: np.ndarray, requant_h=False):
     """SwiGLU expert: g = a Wg^T, u = a Wu^T, h = SiLU(g) * u, y = h W2^T, where W13's
-    first I rows are Wg and the next I rows Wu. With requant_h, h is re-quantised to
-    E4M3 per 1x128 block (from its fp32 value) before the down projection, as the
-    fused SwiGLU + re-quantisation of the fp8 grouped GEMM does."""
+    first I rows are Wg and the next I rows Wu. With requant_h (True or "fp8"), h is
+    re-quantised to E4M3 per 1x128 block (from its fp32 value) before the down
+    projection, as the fused SwiGLU + re-quantisation of the fp8 grouped GEMM does; with
+    "mxfp4", to MXFP4 per 1x32 block (the W4A4 path)."""
     I = w13_64.shape[0] // 2
     g = a64 @ w13_64[:I].T
     u = a64 @ w13_64[I:].T
     h = silu(g) * u
-    if requant_h:
+    if requant_h == "mxfp4":
+        _, _, h = quantise_rows_mxfp4(h.astype(np.float32))
+    elif requant_h:
         _, _, h = quantise_rows_e4m3(h.astype(np.float32))
     return h @ w2_64.T
 
@@ -321,10 +367,15 @@ def layer_forward(prob, tokens=None, with_routing: bool = True):
     res.update(counts=counts, offsets=offsets, perm_src=perm_src, inv_perm=inv_perm)
 
     fp8 = cfg.wdt == "fp8"
+    a4 = cfg.wdt == "mxfp4a4"
+    requant = "mxfp4" if a4 else fp8
     xs = x64[tokens]
     if fp8:
         # activations enter the expert GEMMs quantised per 1x128 block (from bf16/fp32)
         _, _, a = quantise_rows_e4m3(xs.astype(np.float32))
+    elif a4:
+        # W4A4: activations quantised to MXFP4 per 1x32 block
+        _, _, a = quantise_rows_mxfp4(xs.astype(np.float32))
     else:
         a = xs
     out = np.zeros((len(tokens), cfg.H), np.float64)
@@ -333,12 +384,12 @@ def layer_forward(prob, tokens=None, with_routing: bool = True):
     for e in np.unique(sel):
         rows, slots = np.nonzero(sel == e)
         w13, w2 = expert_weights(prob.routed, int(e))
-        y = expert_ffn(a[rows], w13, w2, requant_h=fp8)
+        y = expert_ffn(a[rows], w13, w2, requant_h=requant)
         out[rows] += wsel[rows, slots][:, None] * y
         del w13, w2
     if prob.shared is not None:
         w13, w2 = expert_weights(prob.shared, 0)
-        out += expert_ffn(a, w13, w2, requant_h=fp8)
+        out += expert_ffn(a, w13, w2, requant_h=requant)
     res["tokens"] = tokens
     res["out"] = out
     return res
