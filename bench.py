@@ -98,10 +98,12 @@ def cpu_baseline(cfg, host, n_tokens):
 
 
 # bytes per stored element (block scales included) of each storage format
-ELEM_BYTES = {"f32": 4.0, "bf16": 2.0, "fp8": 1.0 + 4.0 / (128 * 128), "mxfp4": 0.5 + 1.0 / 32}
+ELEM_BYTES = {"f32": 4.0, "bf16": 2.0, "fp8": 1.0 + 4.0 / (128 * 128), "mxfp4": 0.5 + 1.0 / 32,
+              "mxfp4a4": 0.5 + 1.0 / 32}
 # dense MFMA peak (TFLOP/s) of the product each weight format is computed with: MXFP4 weights
 # are decoded to bf16 in registers and multiplied on the bf16 MFMA
-MFMA_PEAK = {"f32": 157.3, "bf16": BF16_PEAK_TFLOPS, "fp8": 5000.0, "mxfp4": BF16_PEAK_TFLOPS}
+MFMA_PEAK = {"f32": 157.3, "bf16": BF16_PEAK_TFLOPS, "fp8": 5000.0, "mxfp4": BF16_PEAK_TFLOPS,
+             "mxfp4a4": 10100.0}
 
 
 def ffn_accounting(cfg, touched):
@@ -115,8 +117,10 @@ def ffn_accounting(cfg, touched):
     rows = rows_r + (T if Is else 0)
     wb = ELEM_BYTES[cfg.wdt]
     q8 = 1.0 + 4.0 / 128          # an E4M3 code plus its share of a 1 x 128 fp32 scale
-    xb = q8 if cfg.wdt == "fp8" else ELEM_BYTES[cfg.act]
-    hb = q8 if cfg.wdt == "fp8" else (4.0 if cfg.wdt == "f32" else 2.0)
+    q4 = 0.5 + 1.0 / 32           # an E2M1 code plus its share of a 1 x 32 E8M0 scale
+    xb = q8 if cfg.wdt == "fp8" else (q4 if cfg.wdt == "mxfp4a4" else ELEM_BYTES[cfg.act])
+    hb = q8 if cfg.wdt == "fp8" else (q4 if cfg.wdt == "mxfp4a4" else
+                                      (4.0 if cfg.wdt == "f32" else 2.0))
     h_elems = rows_r * I + (T * Is if Is else 0)
     w13 = (touched * 2 * I * H + (2 * Is * H if Is else 0)) * wb
     w2 = (touched * I * H + (Is * H if Is else 0)) * wb
@@ -128,6 +132,8 @@ def ffn_accounting(cfg, touched):
         kgu, kdn = "k_gateup_stream_mx", "k_down_stream_mx"
     elif cfg.wdt == "mxfp4":
         kgu, kdn = "k_tiled2<gate/up, MXFP4>", "k_tiled2<down, MXFP4>"
+    elif cfg.wdt == "mxfp4a4":
+        kgu, kdn = "k_w4a4<gate/up>", "k_w4a4<down>"
     elif cfg.wdt == "bf16" and rows_r > 32 * cfg.E:
         kgu, kdn = "k_tiled2<gate/up>", "k_tiled2<down>"
     else:

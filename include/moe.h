@@ -52,8 +52,13 @@ typedef enum {
   MOE_F32 = 0,      /* IEEE binary32 */
   MOE_BF16 = 1,     /* bfloat16 */
   MOE_FP8_E4M3 = 2, /* OCP E4M3FN codes, with fp32 block scales */
-  MOE_MXFP4 = 3     /* OCP MX E2M1 pairs per byte (element 2i in the low nibble),
+  MOE_MXFP4 = 3,    /* OCP MX E2M1 pairs per byte (element 2i in the low nibble),
                        with E8M0 scales per 32 elements along the contiguous dimension */
+  MOE_MXFP4_A4 = 4  /* expert weights only: stored as MOE_MXFP4, and the layer quantises the
+                       activations (and the SwiGLU output) to MXFP4 too, per 1 x 32 block:
+                       scale 2^(floor(log2 amax) - 2) (1 for a zero block), codes E2M1 with
+                       round to nearest even, saturating at 6 -- both operands of the expert
+                       GEMMs are then FP4 (W4A4) */
 } moe_dtype;
 
 typedef enum {
@@ -68,6 +73,7 @@ typedef enum {
  *           (one scale per 128 x 128 block; value = code * scale). H, I multiples of 128.
  * MXFP4:    w13 bytes [E, 2I, H/2], w2 bytes [E, H, I/2]; w13_scale u8 [E, 2I, H/32],
  *           w2_scale u8 [E, H, I/32] (value = e2m1 * 2^(scale - 127)). H, I multiples of 128.
+ * MXFP4_A4: the MXFP4 layout; activations BF16 in, quantised inside. H, I multiples of 128.
  * F32/BF16: no scales (NULL). H, I multiples of 64.
  * The fp8 and MXFP4 expert formats are the FP8/FP4 grouped GEMM inputs of "GC-MoE:
  * Overlapping Expert-Parallel Token Dispatch with FP8/FP4 Grouped GEMM via CUDA Green
@@ -249,6 +255,17 @@ moe_status moe_quantize_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, flo
  * single-workgroup kernel; stream-ordered after the call that wrote counts. */
 moe_status moe_bias_update(const int32_t* counts, int32_t E, float u, float* bias,
                            void* stream);
+
+/* Per 1 x 32 block MXFP4 quantisation of activation rows, as the W4A4 expert path
+ * (MOE_MXFP4_A4) applies it to its inputs and to the SwiGLU output: e = floor(log2(amax))
+ * - 2 clamped to [-127, 127] (0 for an all-zero block), scale code e + 127, element codes
+ * E2M1(x * 2^-e) rounded to nearest even and saturated at 6 (the OCP MX rule for the FP4
+ * operands of the GC-MoE grouped GEMM, key_changes, fourth item).
+ *   x [n, H] BF16; q [n, H/2] bytes (element 2i in the low nibble of byte i);
+ *   q_scale [n, H/32] E8M0 bytes. H a multiple of 32. Non-finite inputs give unspecified
+ *   codes. */
+moe_status moe_quantize_mxfp4(const void* x, int32_t n, int32_t H, uint8_t* q, uint8_t* q_scale,
+                              void* stream);
 
 const char* moe_status_str(moe_status s);
 const char* moe_last_hip_error(void); /* thread-local text of the last MOE_ERR_HIP */

@@ -79,5 +79,6 @@ hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_eve
 bool ffn_stream_mx_ok(int32_t H, int32_t I);
 hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);
 hipError_t launch_ffn_fp8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);
+hipError_t launch_ffn_w4a4(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);
 
 }  // namespace moe

@@ -1,0 +1,280 @@
+// W4A4 grouped FFN: MXFP4 weights and MXFP4 activations on gfx950's scaled FP4 matrix
+// instruction (v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1), the FP4 grouped
+// GEMM of "GC-MoE: Overlapping Expert-Parallel Token Dispatch with FP8/FP4 Grouped GEMM via
+// CUDA Green Contexts" (key_changes, fourth item) with its operands' E8M0 block scales fed
+// to the instruction itself.
+//
+// Operand layout of one 16 x 16 x 128 instruction: lane (m, q) = (lane % 16, lane / 16)
+// holds row m's 32 elements 32 q .. 32 q + 31 as 16 bytes (element 2i in the low nibble of
+// byte i) and, in its scale register, the E8M0 scale of that 32-element block; the result
+// lane holds D[4 q + i][m]. Activation rows are the A operand, weight rows the B operand.
+//
+// A workgroup computes 128 rows x 128 weight rows (gate/up: gate and up rows of 64 features,
+// alternating by 16) with 4 wavefronts of 64 x 64; each 128-element K block of both
+// operands (64 B of codes and 4 scale bytes a row) goes global -> LDS by DMA through an
+// S-stage ring, the kernel's only LDS object. Codes sit in 64-B rows with the 16-B chunk c
+// of row r at c ^ ((r >> 2) & 3), so the 16 rows one fragment read touches hit 16 distinct
+// bank groups.
+//
+// The activations are quantised once per token before the gate/up launch
+// (k_quant_rows_mxfp4), and the gate/up epilogue quantises h the same way: per 1 x 32
+// block, scale 2^e with e = floor(log2(amax)) - 2 (e = 0 for a zero block, clamped to
+// [-127, 127]), codes E2M1(v * 2^-e) rounded to nearest even and saturated at 6.
+#include "ffn_common.h"
+
+namespace moe {
+namespace {
+
+#ifndef MOE_A4_STAGES
+#define MOE_A4_STAGES 4
+#endif
+constexpr int kA4Xcds = 8;
+
+// E2M1 code of v (already divided by the block scale): nearest of 0, .5, 1, 1.5, 2, 3, 4,
+// 6, ties to the even code, larger magnitudes to 6; the sign in bit 3 (also for zero).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                     (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
+// Shared-scale exponent e of a block from its amax (a non-negative fp32).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const int be = (int)(__float_as_uint(amax) >> 23);  // biased exponent (amax >= 0)
+  if (amax == 0.0f) return 0;
+  if (be == 0) return -127;                            // subnormal amax: below 2^-125
+  const int e = be - 127 - 2;
+  return e < -127 ? -127 : e;
+}
+
+__device__ __forceinline__ float exp2i(int e) {  // 2^e for e in [-127, 127], exact
+  return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// One thread per 32-element block of a bf16 row: codes [n, H/2] bytes, scales [n, H/32].
+__global__ void __launch_bounds__(256) k_quant_rows_mxfp4(const uint16_t* __restrict__ x, int n,
+                                                          int H, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ qs) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nb = H / 32;
+  if (b >= (int64_t)n * nb) return;
+  const int64_t row = b / nb;
+  const int blk = (int)(b - row * nb);
+  const uint4* src = reinterpret_cast<const uint4*>(x + row * H + blk * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = src[i];
+    v[8 * i + 0] = bf16_lo(w.x); v[8 * i + 1] = bf16_hi(w.x);
+    v[8 * i + 2] = bf16_lo(w.y); v[8 * i + 3] = bf16_hi(w.y);
+    v[8 * i + 4] = bf16_lo(w.z); v[8 * i + 5] = bf16_hi(w.z);
+    v[8 * i + 6] = bf16_lo(w.w); v[8 * i + 7] = bf16_hi(w.w);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx_exponent(amax);
+  const float inv = exp2i(-e);
+  uint32_t wd[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) wd[i >> 3] |= e2m1_code(v[i] * inv) << (4 * (i & 7));
+  *reinterpret_cast<uint4*>(q + row * (H / 2) + blk * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  qs[row * nb + blk] = (uint8_t)(e + 127);
+}
+
+// LDS offset of logical 16-B chunk c of 64-B code row r.
+__device__ __forceinline__ int a4_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+template <bool kGateUp, bool kYF32>
+__global__ void __launch_bounds__(256, 2) k_w4a4(FfnArgs a, int nb_per_tile) {
+  constexpr int S = MOE_A4_STAGES;
+  constexpr int TM = 4, TN = 4, WGM = 2;
+  constexpr int BM = 128, BN = 128;
+  constexpr int CODES = BM * 64;              // bytes of one operand's codes a stage
+  constexpr int STG = 2 * CODES + 2 * BM * 4;  // codes of both operands, then their scales
+  constexpr int OPS = 5;                      // DMA instructions per thread a stage
+  static_assert(S >= 2 && (S - 2) * OPS < 64, "ring depth");
+  __shared__ __attribute__((aligned(1024))) char ring[S * STG];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int nitems = *a.ntiles * nb_per_tile;
+  const int chunk = (nitems + kA4Xcds - 1) / kA4Xcds;
+  const int slot = blockIdx.x / kA4Xcds;
+  const int item = (blockIdx.x % kA4Xcds) * chunk + slot;
+  if (slot >= chunk || item >= nitems) return;
+  const Tile tb = a.tiles[item / nb_per_tile];
+  const int o = item - tb.blk0 * nb_per_tile;
+  const int nb = o / tb.nblk;
+  const Tile tl = a.tiles[tb.blk0 + (o - nb * tb.nblk)];
+  const int bank = tl.group < a.E ? 0 : 1;
+  const int64_t ge = tl.group < a.E ? tl.group : 0;
+  const int I = a.bank[bank].I;
+  const int H = a.H;
+  const int K = kGateUp ? H : I;
+  const int f0 = nb * (kGateUp ? BN / 2 : BN);
+  if (f0 >= (kGateUp ? I : H)) return;
+  const int64_t wrows = kGateUp ? 2 * I : H;
+  const uint8_t* wc = reinterpret_cast<const uint8_t*>(kGateUp ? a.bank[bank].w13 : a.bank[bank].w2) +
+                      ge * wrows * (K / 2);
+  const uint8_t* ws = reinterpret_cast<const uint8_t*>(kGateUp ? a.bank[bank].w13_scale
+                                                               : a.bank[bank].w2_scale) +
+                      ge * wrows * (K / 32);
+  auto weight_row = [&](int r) {
+    if (kGateUp) {
+      const int blk = r / (16 * TN), jj = r % (16 * TN), nt = jj >> 4, within = jj & 15;
+      const int feat = f0 + blk * (8 * TN) + (nt >> 1) * 16 + within;
+      return (nt & 1) ? I + feat : feat;
+    }
+    return f0 + r;
+  };
+  auto act_row = [&](int r) -> int64_t {  // source row of tile row r (clamped to the tile)
+    const int grow = tl.row0 + (r < tl.nrows ? r : tl.nrows - 1);
+    return kGateUp && a.a_rowmap ? a.a_rowmap[grow] : grow;
+  };
+  // codes: instruction i of wavefront w fills 1-KB block q = 4 i + w (rows 16 q ..) of the
+  // activation (i < 2) or weight (i >= 2) codes; lane l writes row 16 q + l / 4, physical
+  // chunk l % 4
+  const uint8_t* cp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = 4 * (i & 1) + wave;
+    const int r = 16 * q + (l >> 2);
+    const int c = (l & 3) ^ ((r >> 2) & 3);
+    if (i < 2) {
+      cp[i] = (kGateUp ? a.a_q : reinterpret_cast<const uint8_t*>(a.h)) +
+              act_row(r) * (int64_t)(kGateUp ? H / 2 : a.I_max / 2) + c * 16;
+    } else {
+      cp[i] = wc + (int64_t)weight_row(r) * (K / 2) + c * 16;
+    }
+  }
+  // scales: wavefronts 0, 1 fetch the activation rows 64 w + l, wavefronts 2, 3 the weight
+  // rows 64 (w - 2) + l, one dword (4 blocks of 32) a row
+  const uint8_t* sp;
+  if (wave < 2) {
+    const int r = 64 * wave + l;
+    sp = (kGateUp ? a.a_xs : a.h_xs) + act_row(r) * (int64_t)(kGateUp ? H / 32 : a.I_max / 32);
+  } else {
+    sp = ws + (int64_t)weight_row(64 * (wave - 2) + l) * (K / 32);
+  }
+  auto issue = [&](int kt) {
+    char* st = ring + (kt % S) * STG;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma16(cp[i] + (int64_t)kt * 64, st + (i >> 1) * CODES + (4 * (i & 1) + wave) * 1024);
+    dma4(sp + (int64_t)kt * 4, st + 2 * CODES + wave * 256);
+  };
+  const int wm = wave % WGM, wn = wave / WGM;
+  const bool live = wm * 16 * TM < tl.nrows;
+  const int m16 = l & 15, g = l >> 4;
+  int arow[TM], brow[TN];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) arow[t] = wm * (16 * TM) + t * 16 + m16;
+#pragma unroll
+  for (int t = 0; t < TN; ++t) brow[t] = wn * (16 * TN) + t * 16 + m16;
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  const int KT = K / 128;
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < KT) issue(p);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * OPS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + S - 1 < KT) issue(kt + S - 1);
+    if (!live) continue;
+    const char* st = ring + (kt % S) * STG;
+    i32x8 fa[TM], fb[TN];
+    int sa[TM], sb[TN];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + a4_off(arow[t], g));
+      fa[t] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+      sa[t] = (int)(*reinterpret_cast<const uint32_t*>(st + 2 * CODES + 4 * arow[t]) >> (8 * g));
+    }
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + CODES + a4_off(brow[t], g));
+      fb[t] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+      sb[t] = (int)(*reinterpret_cast<const uint32_t*>(st + 2 * CODES + 4 * (BM + brow[t])) >> (8 * g));
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], 4, 4,
+                                                                      0, sa[i], 0, sb[j]);
+  }
+  // lane holds D[row 4 g + i of row tile mt][column m16 of weight tile nt]
+#pragma unroll
+  for (int mt = 0; mt < TM; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = wm * (16 * TM) + mt * 16 + 4 * g + i;
+      const bool valid = rl < tl.nrows;  // uniform over the 16 lanes that share a row
+      const int64_t row = tl.row0 + rl;
+      if (kGateUp) {
+        // h of features f0 + 32 wn + 16 p + m16 (p = 0, 1): one 1 x 32 block per row
+        float hv[TN / 2];
+        float amax = 0.0f;
+#pragma unroll
+        for (int p = 0; p < TN / 2; ++p) {
+          hv[p] = silu_mul(acc[mt][2 * p][i], acc[mt][2 * p + 1][i]);
+          amax = fmaxf(amax, fabsf(hv[p]));
+        }
+#pragma unroll
+        for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
+        const int e = mx_exponent(amax);
+        const float inv = exp2i(-e);
+        const int fb0 = f0 + wn * 32;
+#pragma unroll
+        for (int p = 0; p < TN / 2; ++p) {
+          const uint32_t c = e2m1_code(hv[p] * inv);
+          const uint32_t cn = __shfl_xor(c, 1, 64);
+          if (valid && (m16 & 1) == 0)
+            reinterpret_cast<uint8_t*>(a.h)[row * (a.I_max / 2) + fb0 / 2 + p * 8 + m16 / 2] =
+                (uint8_t)(c | (cn << 4));
+        }
+        if (valid && m16 == 0) a.h_xs[row * (a.I_max / 32) + fb0 / 32] = (uint8_t)(e + 127);
+      } else if (valid) {
+#pragma unroll
+        for (int nt = 0; nt < TN; ++nt) {
+          const int64_t o2 = row * H + f0 + wn * (16 * TN) + nt * 16 + m16;
+          if (kYF32) reinterpret_cast<float*>(a.y)[o2] = acc[mt][nt][i];
+          else reinterpret_cast<uint16_t*>(a.y)[o2] = f32_to_bf16(acc[mt][nt][i]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ffn_w4a4(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
+  const int nb_gu = a.I_max / 64, nb_dn = a.H / 128;
+  const dim3 gu((a.max_tiles * nb_gu + kA4Xcds - 1) / kA4Xcds * kA4Xcds),
+      dn((a.max_tiles * nb_dn + kA4Xcds - 1) / kA4Xcds * kA4Xcds), blk(256);
+  hipLaunchKernelGGL((k_w4a4<true, false>), gu, blk, 0, s, a, nb_gu);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
+  if (a.y_dt == MOE_F32)
+    hipLaunchKernelGGL((k_w4a4<false, true>), dn, blk, 0, s, a, nb_dn);
+  else
+    hipLaunchKernelGGL((k_w4a4<false, false>), dn, blk, 0, s, a, nb_dn);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_mxfp4(const void* x, int32_t n, int32_t H, uint8_t* q, uint8_t* qs,
+                                   hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (int64_t)n * (H / 32);
+  hipLaunchKernelGGL(k_quant_rows_mxfp4, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(x), n, H, q, qs);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -23,6 +23,8 @@ bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I) {
     case MOE_FP8_E4M3: return H % kF8Feat == 0 && I % kF8Feat == 0;
     // the tiled kernel's weight-row blocks, and dword-aligned scale bytes of every row
     case MOE_MXFP4: return H % kTiledN == 0 && I % 128 == 0;
+    // 128-element K blocks of the FP4 instruction
+    case MOE_MXFP4_A4: return H % 128 == 0 && I % 128 == 0;
   }
   return false;
 }
@@ -30,6 +32,7 @@ bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I) {
 int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32_t I_routed,
                    int32_t I_shared) {
   if (wdt == MOE_FP8_E4M3) return kF8TileM;
+  if (wdt == MOE_MXFP4_A4) return kTiledM;
   // MXFP4: streaming kernels for few rows per expert where the shapes allow, else tiled
   if (wdt == MOE_MXFP4)
     return (int64_t)rows <= 32 * (int64_t)groups && ffn_stream_mx_ok(H, I_routed) &&
@@ -50,6 +53,10 @@ size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I
     const size_t q = ((size_t)rows_total * I_max + 255) / 256 * 256;
     return q + ((size_t)rows_total * (I_max / kF8K) * sizeof(float) + 255) / 256 * 256;
   }
+  if (wdt == MOE_MXFP4_A4) {
+    const size_t q = ((size_t)rows_total * (I_max / 2) + 255) / 256 * 256;
+    return q + ((size_t)rows_total * (I_max / 32) + 255) / 256 * 256;
+  }
   const size_t hb = (wdt == MOE_F32) ? 4 : 2;
   return ((size_t)rows_total * I_max * hb + 255) / 256 * 256;
 }
@@ -63,6 +70,10 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
     a.h_scale = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) +
                                          ((size_t)a.rows_total * a.I_max + 255) / 256 * 256);
     return launch_ffn_fp8(a, s, mid_event);
+  }
+  if (a.wdt == MOE_MXFP4_A4) {
+    a.h_xs = reinterpret_cast<uint8_t*>(scratch) + ((size_t)a.rows_total * (a.I_max / 2) + 255) / 256 * 256;
+    return launch_ffn_w4a4(a, s, mid_event);
   }
   if (a.tile_m == kTiledM && (a.wdt == MOE_BF16 || a.wdt == MOE_MXFP4))
     return launch_ffn_tiled(a, s, mid_event);

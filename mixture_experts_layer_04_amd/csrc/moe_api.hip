@@ -33,6 +33,7 @@ moe_status check_bank(const moe_experts* w, int32_t H, bool need_scales) {
       break;
     case MOE_FP8_E4M3:
     case MOE_MXFP4:
+    case MOE_MXFP4_A4:
       if (need_scales && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_NULL;
       break;
     default:
@@ -48,7 +49,8 @@ moe_status check_bank(const moe_experts* w, int32_t H, bool need_scales) {
 // Activation dtype that goes with a weight dtype.
 bool act_ok(moe_dtype act, moe_dtype wdt) {
   if (wdt == MOE_F32) return act == MOE_F32;
-  if (wdt == MOE_BF16 || wdt == MOE_FP8_E4M3 || wdt == MOE_MXFP4) return act == MOE_BF16;
+  if (wdt == MOE_BF16 || wdt == MOE_FP8_E4M3 || wdt == MOE_MXFP4 || wdt == MOE_MXFP4_A4)
+    return act == MOE_BF16;
   return false;
 }
 bool io_dt_ok(moe_dtype d) { return d == MOE_F32 || d == MOE_BF16; }
@@ -89,9 +91,42 @@ void plan_ffn(Carve& c, FfnPlan& p, moe_dtype wdt, moe_dtype act, int32_t H, int
   if (need_y) p.o_y = c.take((size_t)p.rows_total * H * dt_bytes(p.y_dt));
 }
 
+// Staging of quantised activations: fp8 (E4M3 codes [rows, H], fp32 scales [rows, H/128])
+// or W4A4 (E2M1 codes [rows, H/2], E8M0 scales [rows, H/32]).
+struct QPlan {
+  size_t o_q = 0, o_qs = 0;
+};
+void plan_quant(Carve& c, QPlan& q, moe_dtype wdt, int32_t rows, int32_t H) {
+  if (wdt == MOE_FP8_E4M3) {
+    q.o_q = c.take((size_t)rows * H);
+    q.o_qs = c.take((size_t)rows * (H / 128) * sizeof(float));
+  } else if (wdt == MOE_MXFP4_A4) {
+    q.o_q = c.take((size_t)rows * (H / 2));
+    q.o_qs = c.take((size_t)rows * (H / 32));
+  }
+}
+// Quantises the rows of x for the expert GEMMs (if the format needs it) and points f at them.
+hipError_t quantise_acts(moe_dtype wdt, const void* x, int32_t rows, int32_t H, char* base,
+                         const QPlan& q, FfnArgs& f, hipStream_t s) {
+  if (wdt == MOE_FP8_E4M3) {
+    f.a_q = reinterpret_cast<const uint8_t*>(base + q.o_q);
+    f.a_qscale = reinterpret_cast<const float*>(base + q.o_qs);
+    return launch_quant_rows_fp8(x, rows, H, reinterpret_cast<uint8_t*>(base + q.o_q),
+                                 reinterpret_cast<float*>(base + q.o_qs), s);
+  }
+  if (wdt == MOE_MXFP4_A4) {
+    f.a_q = reinterpret_cast<const uint8_t*>(base + q.o_q);
+    f.a_xs = reinterpret_cast<const uint8_t*>(base + q.o_qs);
+    return launch_quant_rows_mxfp4(x, rows, H, reinterpret_cast<uint8_t*>(base + q.o_q),
+                                   reinterpret_cast<uint8_t*>(base + q.o_qs), s);
+  }
+  return hipSuccess;
+}
+
 struct LayerPlan {
   size_t o_route = 0, o_idx = 0, o_w = 0, o_counts = 0, o_offsets = 0, o_perm_src = 0,
-         o_inv_perm = 0, o_row_token = 0, o_perm_ws = 0, o_xq = 0, o_xqs = 0;
+         o_inv_perm = 0, o_row_token = 0, o_perm_ws = 0;
+  QPlan q;
   // the shared group's own tile list, for the launch that runs beside the routed experts
   size_t o_sh_tiles = 0, o_sh_ntiles = 0;
   int32_t sh_max_tiles = 0;
@@ -114,10 +149,7 @@ LayerPlan plan_layer(const moe_layer_desc* d) {
   p.o_inv_perm = c.take(rows * sizeof(int32_t));
   p.o_row_token = c.take((rows + (shared ? T : 0)) * sizeof(int32_t));
   p.o_perm_ws = c.take(permute_ws_bytes(T, E));
-  if (d->routed.dtype == MOE_FP8_E4M3) {
-    p.o_xq = c.take((size_t)T * H);
-    p.o_xqs = c.take((size_t)T * (H / 128) * sizeof(float));
-  }
+  plan_quant(c, p.q, d->routed.dtype, T, H);
   plan_ffn(c, p.ffn, d->routed.dtype, d->act_dtype, H, d->routed.I, shared ? d->shared.I : 0,
            (int32_t)rows, E, shared ? T : 0, true);
   if (shared) {
@@ -269,15 +301,6 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
 
 // ------------------------------------------------------------------- grouped FFN
 
-// Staging of fp8 activations: E4M3 codes [rows, H] and fp32 scales [rows, H/128].
-struct QPlan {
-  size_t o_q = 0, o_qs = 0;
-};
-static void plan_quant(Carve& c, QPlan& q, moe_dtype wdt, int32_t rows, int32_t H) {
-  if (wdt != MOE_FP8_E4M3) return;
-  q.o_q = c.take((size_t)rows * H);
-  q.o_qs = c.take((size_t)rows * (H / 128) * sizeof(float));
-}
 
 static bool plan_grouped(const moe_experts* w, moe_dtype act_dt, int32_t rows, FfnPlan* p,
                          QPlan* q, size_t* total) {
@@ -320,13 +343,8 @@ moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype a
   if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn tiles");
   FfnArgs f = ffn_args(p, base, *w, nullptr, act_dt, w->H, x_perm, nullptr, y_perm);
   f.y_dt = y_dt;
-  if (w->dtype == MOE_FP8_E4M3) {
-    e = launch_quant_rows_fp8(x_perm, rows, w->H, reinterpret_cast<uint8_t*>(base + q.o_q),
-                              reinterpret_cast<float*>(base + q.o_qs), s);
-    if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn quantise");
-    f.a_q = reinterpret_cast<const uint8_t*>(base + q.o_q);
-    f.a_qscale = reinterpret_cast<const float*>(base + q.o_qs);
-  }
+  e = quantise_acts(w->dtype, x_perm, rows, w->H, base, q, f, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn quantise");
   e = launch_grouped_ffn(f, base + p.o_scratch, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_ffn");
 }
@@ -394,19 +412,13 @@ static moe_status layer_forward(const moe_layer_desc* d, const void* x, void* ou
 #define MOE_MARK(i)                                                                    \
   if (events && (e = hipEventRecord(ev[i], s)) != hipSuccess)                         \
     return hip_fail(e, "moe_layer_forward event");
-  const bool fp8 = d->routed.dtype == MOE_FP8_E4M3;
   const bool beside = side && shared && T > 0;
   void* y = base + p.ffn.o_y;
   FfnArgs f = ffn_args(p.ffn, base, d->routed, shared ? &d->shared : nullptr, d->act_dtype, H, x,
                        row_token, y);
-  if (fp8) {
-    f.a_q = reinterpret_cast<const uint8_t*>(base + p.o_xq);
-    f.a_qscale = reinterpret_cast<const float*>(base + p.o_xqs);
-  }
   MOE_MARK(0);
-  if (fp8 && beside) {  // the shared launch reads the quantised activations too
-    e = launch_quant_rows_fp8(x, T, H, reinterpret_cast<uint8_t*>(base + p.o_xq),
-                              reinterpret_cast<float*>(base + p.o_xqs), s);
+  if (beside) {  // the shared launch reads the quantised activations too
+    e = quantise_acts(d->routed.dtype, x, T, H, base, p.q, f, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer_forward quantise");
   }
   if (beside) {
@@ -435,9 +447,8 @@ static moe_status layer_forward(const moe_layer_desc* d, const void* x, void* ou
                           reinterpret_cast<int32_t*>(base + p.ffn.o_ntiles), p.ffn.tile_m,
                           shared && !beside ? 1 : 0, base + p.o_perm_ws, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer_forward permute");
-  if (fp8 && !beside) {
-    e = launch_quant_rows_fp8(x, T, H, reinterpret_cast<uint8_t*>(base + p.o_xq),
-                              reinterpret_cast<float*>(base + p.o_xqs), s);
+  if (!beside) {
+    e = quantise_acts(d->routed.dtype, x, T, H, base, p.q, f, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer_forward quantise");
   }
   MOE_MARK(2);
@@ -549,13 +560,8 @@ static moe_status rows_forward(const moe_experts* w, const void* x, moe_dtype ac
   if (e != hipSuccess) return hip_fail(e, "moe_rows_forward permute");
   void* y = base + p.o_y;
   FfnArgs f = ffn_args(p, base, *w, nullptr, act_dt, w->H, x, row_token, y);
-  if (w->dtype == MOE_FP8_E4M3) {
-    e = launch_quant_rows_fp8(x, rows, w->H, reinterpret_cast<uint8_t*>(base + qp.o_q),
-                              reinterpret_cast<float*>(base + qp.o_qs), s);
-    if (e != hipSuccess) return hip_fail(e, "moe_rows_forward quantise");
-    f.a_q = reinterpret_cast<const uint8_t*>(base + qp.o_q);
-    f.a_qscale = reinterpret_cast<const float*>(base + qp.o_qs);
-  }
+  e = quantise_acts(w->dtype, x, rows, w->H, base, qp, f, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_rows_forward quantise");
   MOE_MARK(2);
   e = launch_grouped_ffn(f, base + p.o_scratch, s, events ? ev[3] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "moe_rows_forward grouped_ffn");
@@ -605,6 +611,18 @@ moe_status moe_bias_update(const int32_t* counts, int32_t E, float u, float* bia
   if (!al16(counts) || !al16(bias)) return MOE_ERR_ALIGN;
   hipError_t e = launch_bias_update(counts, E, u, bias, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_bias_update");
+}
+
+// ------------------------------------------------------------- MXFP4 quantiser
+
+moe_status moe_quantize_mxfp4(const void* x, int32_t n, int32_t H, uint8_t* q, uint8_t* q_scale,
+                              void* stream) {
+  if (n < 0 || H < 32 || H % 32) return MOE_ERR_SHAPE;
+  if (n == 0) return MOE_OK;
+  if (!x || !q || !q_scale) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(q)) return MOE_ERR_ALIGN;
+  hipError_t e = launch_quant_rows_mxfp4(x, n, H, q, q_scale, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_mxfp4");
 }
 
 }  // extern "C"

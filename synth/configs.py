@@ -84,6 +84,11 @@ CONFIGS = {
     "r1_decode_mxfp4": MoEConfig("r1_decode_mxfp4", T=128, H=7168, E=256, k=8, I=2048,
                                  score="sigmoid", use_bias=True, scale=2.5, shared_I=2048,
                                  wdt="mxfp4", seed=2000, weight_seed=2000),
+    # one GPU's expert-parallel share with both GEMM operands in MXFP4 (W4A4): ep32_mxfp4's
+    # weights, rows and loads, with the activations quantised to MXFP4 inside
+    "ep32_w4a4": MoEConfig("ep32_w4a4", T=16384, H=7168, E=32, k=1, I=2048, score="none",
+                           act="bf16", wdt="mxfp4a4", out="bf16", seed=5000, weight_seed=5000,
+                           dirichlet_alpha=0.5),
 }
 
 ORDER = ["tiny_fp32", "r1_decode", "r1_prefill", "e384_fp8", "ep32_mxfp4"]

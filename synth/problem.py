@@ -51,7 +51,7 @@ class HostBank:
         if self.fmt == "fp8":
             c, s = fp8_bank(self.seed, tid, e, 1, rows, cols, self.std)
             return {"w": c[0], "scale": s[0]}
-        if self.fmt == "mxfp4":
+        if self.fmt in ("mxfp4", "mxfp4a4"):
             p, s = mxfp4_bank(self.seed, tid, e, 1, rows, cols, self.std)
             return {"w": p[0], "scale": s[0]}
         raise ValueError(self.fmt)
@@ -162,10 +162,10 @@ def _dev_bank(cfg: MoEConfig, E: int, I: int, tid13: int, tid2: int, device) -> 
         c13, s13 = dev_fp8_bank(s, tid13, E, 2 * I, H, std, device)
         c2, s2 = dev_fp8_bank(s, tid2, E, H, I, std, device)
         return DevBank("fp8", E, H, I, c13, c2, s13, s2)
-    if cfg.wdt == "mxfp4":
+    if cfg.wdt in ("mxfp4", "mxfp4a4"):  # the same weights; mxfp4a4 also quantises activations
         p13, s13 = dev_mxfp4_bank(s, tid13, E, 2 * I, H, std, device)
         p2, s2 = dev_mxfp4_bank(s, tid2, E, H, I, std, device)
-        return DevBank("mxfp4", E, H, I, p13, p2, s13, s2)
+        return DevBank(cfg.wdt, E, H, I, p13, p2, s13, s2)
     raise ValueError(cfg.wdt)
 
 

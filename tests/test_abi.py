@@ -210,3 +210,17 @@ def test_layer_overlap_needs_both_events():
     # the same argument checks as moe_layer_forward come first after the events
     assert L.moe_layer_forward_overlap(ctypes.byref(d), P, P, None, None, None, None, P, 16,
                                        None, None, P, P) == moe.MOE_ERR_WORKSPACE
+
+
+def test_quantize_mxfp4_validation():
+    L = moe.lib()
+    assert L.moe_quantize_mxfp4(P, 4, 48, P, P, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_quantize_mxfp4(None, 4, 64, P, P, None) == moe.MOE_ERR_NULL
+    assert L.moe_quantize_mxfp4(P, 0, 64, None, None, None) == moe.MOE_OK
+    assert L.moe_quantize_mxfp4(MISALIGNED, 4, 64, P, P, None) == moe.MOE_ERR_ALIGN
+    b = bank("mxfp4a4", H=256, I=192, scales=True)         # I not a multiple of 128
+    assert L.moe_rows_forward(ctypes.byref(b), P, moe.MOE_BF16, P, P, 16, P, moe.MOE_BF16, P,
+                              1 << 30, None) == moe.MOE_ERR_SHAPE
+    b = bank("mxfp4a4", H=256, I=128, scales=True)
+    assert L.moe_rows_forward(ctypes.byref(b), P, moe.MOE_F32, P, P, 16, P, moe.MOE_BF16, P,
+                              1 << 30, None) == moe.MOE_ERR_DTYPE   # activations must be bf16
