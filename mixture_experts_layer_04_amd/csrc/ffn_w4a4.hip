@@ -9,10 +9,11 @@
 // byte i) and, in its scale register, the E8M0 scale of that 32-element block; the result
 // lane holds D[4 q + i][m]. Activation rows are the A operand, weight rows the B operand.
 //
-// A workgroup computes 128 rows x 128 weight rows (gate/up: gate and up rows of 64 features,
-// alternating by 16) with 4 wavefronts of 64 x 64; each 128-element K block of both
-// operands (64 B of codes and 4 scale bytes a row) goes global -> LDS by DMA through an
-// S-stage ring, the kernel's only LDS object. Codes sit in 64-B rows with the 16-B chunk c
+// A workgroup computes 128 rows x 256 weight rows (gate/up: gate and up rows of 128
+// features, alternating by 16; 128 x 128 where H or I do not allow 256) with wavefronts of
+// 64 x 64; each 128-element K block of both operands (64 B of codes and 4 scale bytes a
+// row) goes global -> LDS by DMA through a 3-stage ring (78 KB, two workgroups a CU), the
+// kernel's only LDS object. Codes sit in 64-B rows with the 16-B chunk c
 // of row r at c ^ ((r >> 2) & 3), so the 16 rows one fragment read touches hit 16 distinct
 // bank groups.
 //
@@ -26,7 +27,10 @@ namespace moe {
 namespace {
 
 #ifndef MOE_A4_STAGES
-#define MOE_A4_STAGES 4
+#define MOE_A4_STAGES 3
+#endif
+#ifndef MOE_A4_WGN  // 4: 128 x 256 tiles where the shapes allow; 2: always 128 x 128
+#define MOE_A4_WGN 4
 #endif
 constexpr int kA4Xcds = 8;
 
@@ -86,14 +90,18 @@ __global__ void __launch_bounds__(256) k_quant_rows_mxfp4(const uint16_t* __rest
 // LDS offset of logical 16-B chunk c of 64-B code row r.
 __device__ __forceinline__ int a4_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
-template <bool kGateUp, bool kYF32>
-__global__ void __launch_bounds__(256, 2) k_w4a4(FfnArgs a, int nb_per_tile) {
+// WGN: wavefronts along the weight rows (2: 128 x 128 tiles, 4 wavefronts; 4: 128 x 256,
+// 8 wavefronts).
+template <int WGN, bool kGateUp, bool kYF32>
+__global__ void __launch_bounds__(128 * WGN, 2) k_w4a4(FfnArgs a, int nb_per_tile) {
   constexpr int S = MOE_A4_STAGES;
-  constexpr int TM = 4, TN = 4, WGM = 2;
-  constexpr int BM = 128, BN = 128;
-  constexpr int CODES = BM * 64;              // bytes of one operand's codes a stage
-  constexpr int STG = 2 * CODES + 2 * BM * 4;  // codes of both operands, then their scales
-  constexpr int OPS = 5;                      // DMA instructions per thread a stage
+  constexpr int TM = 4, TN = 4, WGM = 2, NW = WGM * WGN;
+  constexpr int BM = 128, BN = 64 * WGN;
+  constexpr int ACODES = BM * 64, BCODES = BN * 64;  // code bytes of each operand a stage
+  constexpr int STG = ACODES + BCODES + NW * 256;    // then one 256-B scale slot a wavefront
+  constexpr int CPW = (BM + BN) / 16 / NW;           // 1-KB code blocks a wavefront moves
+  constexpr int OPS = CPW + 1;                       // DMA instructions per thread a stage
+  static_assert((BM + BN) / 16 % NW == 0 && (BM + BN) / 64 <= NW, "DMA shares");
   static_assert(S >= 2 && (S - 2) * OPS < 64, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[S * STG];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
@@ -131,37 +139,40 @@ __global__ void __launch_bounds__(256, 2) k_w4a4(FfnArgs a, int nb_per_tile) {
     const int grow = tl.row0 + (r < tl.nrows ? r : tl.nrows - 1);
     return kGateUp && a.a_rowmap ? a.a_rowmap[grow] : grow;
   };
-  // codes: instruction i of wavefront w fills 1-KB block q = 4 i + w (rows 16 q ..) of the
-  // activation (i < 2) or weight (i >= 2) codes; lane l writes row 16 q + l / 4, physical
-  // chunk l % 4
-  const uint8_t* cp[4];
+  // codes: instruction i of wavefront w fills 1-KB block q = NW i + w of the stage's code
+  // area (activation rows 16 q .. for q < BM / 16, then weight rows); lane l writes row
+  // 16 q + l / 4 of its operand, physical chunk l % 4
+  const uint8_t* cp[CPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = 4 * (i & 1) + wave;
-    const int r = 16 * q + (l >> 2);
+  for (int i = 0; i < CPW; ++i) {
+    const int q = NW * i + wave;
+    const bool act = q < BM / 16;
+    const int r = 16 * (act ? q : q - BM / 16) + (l >> 2);
     const int c = (l & 3) ^ ((r >> 2) & 3);
-    if (i < 2) {
+    if (act) {
       cp[i] = (kGateUp ? a.a_q : reinterpret_cast<const uint8_t*>(a.h)) +
               act_row(r) * (int64_t)(kGateUp ? H / 2 : a.I_max / 2) + c * 16;
     } else {
       cp[i] = wc + (int64_t)weight_row(r) * (K / 2) + c * 16;
     }
   }
-  // scales: wavefronts 0, 1 fetch the activation rows 64 w + l, wavefronts 2, 3 the weight
-  // rows 64 (w - 2) + l, one dword (4 blocks of 32) a row
+  // scales, one dword (4 blocks of 32) a row: wavefront w fetches rows 64 w + l of the
+  // activation rows followed by the weight rows (wavefronts past them repeat the last row
+  // into their own slot, so that every wavefront issues the same DMA)
   const uint8_t* sp;
-  if (wave < 2) {
-    const int r = 64 * wave + l;
-    sp = (kGateUp ? a.a_xs : a.h_xs) + act_row(r) * (int64_t)(kGateUp ? H / 32 : a.I_max / 32);
-  } else {
-    sp = ws + (int64_t)weight_row(64 * (wave - 2) + l) * (K / 32);
+  {
+    const int r = 64 * wave + l < BM + BN ? 64 * wave + l : BM + BN - 1;
+    if (r < BM) {
+      sp = (kGateUp ? a.a_xs : a.h_xs) + act_row(r) * (int64_t)(kGateUp ? H / 32 : a.I_max / 32);
+    } else {
+      sp = ws + (int64_t)weight_row(r - BM) * (K / 32);
+    }
   }
   auto issue = [&](int kt) {
     char* st = ring + (kt % S) * STG;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dma16(cp[i] + (int64_t)kt * 64, st + (i >> 1) * CODES + (4 * (i & 1) + wave) * 1024);
-    dma4(sp + (int64_t)kt * 4, st + 2 * CODES + wave * 256);
+    for (int i = 0; i < CPW; ++i) dma16(cp[i] + (int64_t)kt * 64, st + (NW * i + wave) * 1024);
+    dma4(sp + (int64_t)kt * 4, st + ACODES + BCODES + wave * 256);
   };
   const int wm = wave % WGM, wn = wave / WGM;
   const bool live = wm * 16 * TM < tl.nrows;
@@ -193,13 +204,13 @@ __global__ void __launch_bounds__(256, 2) k_w4a4(FfnArgs a, int nb_per_tile) {
     for (int t = 0; t < TM; ++t) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(st + a4_off(arow[t], g));
       fa[t] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-      sa[t] = (int)(*reinterpret_cast<const uint32_t*>(st + 2 * CODES + 4 * arow[t]) >> (8 * g));
+      sa[t] = (int)(*reinterpret_cast<const uint32_t*>(st + ACODES + BCODES + 4 * arow[t]) >> (8 * g));
     }
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + CODES + a4_off(brow[t], g));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + ACODES + a4_off(brow[t], g));
       fb[t] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-      sb[t] = (int)(*reinterpret_cast<const uint32_t*>(st + 2 * CODES + 4 * (BM + brow[t])) >> (8 * g));
+      sb[t] = (int)(*reinterpret_cast<const uint32_t*>(st + ACODES + BCODES + 4 * (BM + brow[t])) >> (8 * g));
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -251,21 +262,29 @@ __global__ void __launch_bounds__(256, 2) k_w4a4(FfnArgs a, int nb_per_tile) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_ffn_w4a4(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
-  const int nb_gu = a.I_max / 64, nb_dn = a.H / 128;
+template <int WGN>
+hipError_t launch_w4a4_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
+  const int nb_gu = a.I_max / (32 * WGN), nb_dn = a.H / (64 * WGN);
   const dim3 gu((a.max_tiles * nb_gu + kA4Xcds - 1) / kA4Xcds * kA4Xcds),
-      dn((a.max_tiles * nb_dn + kA4Xcds - 1) / kA4Xcds * kA4Xcds), blk(256);
-  hipLaunchKernelGGL((k_w4a4<true, false>), gu, blk, 0, s, a, nb_gu);
+      dn((a.max_tiles * nb_dn + kA4Xcds - 1) / kA4Xcds * kA4Xcds), blk(128 * WGN);
+  hipLaunchKernelGGL((k_w4a4<WGN, true, false>), gu, blk, 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
   if (a.y_dt == MOE_F32)
-    hipLaunchKernelGGL((k_w4a4<false, true>), dn, blk, 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_w4a4<WGN, false, true>), dn, blk, 0, s, a, nb_dn);
   else
-    hipLaunchKernelGGL((k_w4a4<false, false>), dn, blk, 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_w4a4<WGN, false, false>), dn, blk, 0, s, a, nb_dn);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ffn_w4a4(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
+  // 256 weight rows a workgroup (128 features for gate/up) where every bank allows it
+  const bool wide = MOE_A4_WGN == 4 && a.H % 256 == 0 && a.bank[0].I % 128 == 0 &&
+                    (!a.has_shared || a.bank[1].I % 128 == 0);
+  return wide ? launch_w4a4_pair<4>(a, s, mid_event) : launch_w4a4_pair<2>(a, s, mid_event);
 }
 
 hipError_t launch_quant_rows_mxfp4(const void* x, int32_t n, int32_t H, uint8_t* q, uint8_t* qs,
