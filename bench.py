@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="r1_decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--overlap", action="store_true",
+                    help="also time the step with the shared expert on a side stream")
     ap.add_argument("--cpu-tokens", type=int, default=24,
                     help="tokens of the batch the CPU oracle leg computes (about 10 s of CPU work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -253,7 +255,7 @@ def main():
 
     # the same step with the shared expert on a side stream beside the routed experts
     ovl_ms = None
-    if cfg.routed and cfg.shared_I:
+    if args.overlap and cfg.routed and cfg.shared_I:
         fj = moe.ForkJoin()
         for _ in range(args.warmup):
             layer.forward_overlap(dev.x, out, fj, counts=counts)
