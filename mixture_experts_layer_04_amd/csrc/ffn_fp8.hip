@@ -8,7 +8,9 @@
 //  - a workgroup of 8 wavefronts computes 128 rows x 128 output features (one scale block);
 //    wavefront w owns features 16 w .. 16 w + 15 with the weights as the MFMA A operand
 //    and the tile's <= 128 rows as B. Each K block of both operands and of their scales
-//    goes global -> LDS by DMA through a ring (k_fp8 describes it).
+//    goes global -> LDS by DMA through a ring (k_fp8 describes it): 3 stages of 49 KB for
+//    gate/up (one workgroup a CU, two blocks of weights in flight while one is
+//    multiplied), 2 stages of 33 KB for down (two workgroups a CU).
 //  - gate/up epilogue: h = SiLU(g) * u in fp32, per-token amax over the workgroup's 128
 //    features (wavefront shuffles, then LDS across wavefronts), scale = amax / 448,
 //    E4M3 codes of h / scale -- exactly one 1 x 128 quantisation block per workgroup.
@@ -18,7 +20,7 @@ namespace moe {
 namespace {
 
 #ifndef MOE_F8_STAGES_GU
-#define MOE_F8_STAGES_GU 2
+#define MOE_F8_STAGES_GU 3
 #endif
 #ifndef MOE_F8_STAGES_DN
 #define MOE_F8_STAGES_DN 2
@@ -80,6 +82,11 @@ __global__ void __launch_bounds__(256) k_quant_rows_fp8(const uint16_t* __restri
     }
   }
 }
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
 
 template <bool kGateUp>
 __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
@@ -176,33 +183,37 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   for (int p = 0; p < S - 1; ++p)
     if (p < KB) issue(p);
   const int wr0 = wave * 16 + m16;  // this lane's gate (or down) weight row in the tile
-  for (int kb = 0; kb < KB; ++kb) {
-    // block kb has landed once at most (blocks issued after it) * A ops are outstanding
-    if (kb + S - 2 < KB) wait_vmcnt<(S - 2) * A>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kb + S - 1 < KB) issue(kb + S - 1);
-    const char* st = ring + (kb % S) * STG;
-    i32x8 wa, wb;
-    {
-      const u32x4 p0 = *reinterpret_cast<const u32x4*>(st + lds_off(wr0, 2 * g));
-      const u32x4 p1 = *reinterpret_cast<const u32x4*>(st + lds_off(wr0, 2 * g + 1));
-      wa[0] = p0[0]; wa[1] = p0[1]; wa[2] = p0[2]; wa[3] = p0[3];
-      wa[4] = p1[0]; wa[5] = p1[1]; wa[6] = p1[2]; wa[7] = p1[3];
-      if (kGateUp) {
-        const u32x4 q0 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g));
-        const u32x4 q1 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g + 1));
-        wb[0] = q0[0]; wb[1] = q0[1]; wb[2] = q0[2]; wb[3] = q0[3];
-        wb[4] = q1[0]; wb[5] = q1[1]; wb[6] = q1[2]; wb[7] = q1[3];
-      } else {
-        wb = wa;
+  // The K loop for NT 16-row sub-tiles of tokens: NT is fixed per workgroup, so each
+  // count gets its own branch-free loop, in which the sub-tiles' LDS reads and MFMAs can
+  // be interleaved (a per-sub-tile branch would serialise them).
+  auto kloop = [&](auto nt_c) {
+    constexpr int NT = decltype(nt_c)::value;
+    for (int kb = 0; kb < KB; ++kb) {
+      // block kb has landed once at most (blocks issued after it) * A ops are outstanding
+      if (kb + S - 2 < KB) wait_vmcnt<(S - 2) * A>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kb + S - 1 < KB) issue(kb + S - 1);
+      const char* st = ring + (kb % S) * STG;
+      i32x8 wa, wb;
+      {
+        const u32x4 p0 = *reinterpret_cast<const u32x4*>(st + lds_off(wr0, 2 * g));
+        const u32x4 p1 = *reinterpret_cast<const u32x4*>(st + lds_off(wr0, 2 * g + 1));
+        wa[0] = p0[0]; wa[1] = p0[1]; wa[2] = p0[2]; wa[3] = p0[3];
+        wa[4] = p1[0]; wa[5] = p1[1]; wa[6] = p1[2]; wa[7] = p1[3];
+        if (kGateUp) {
+          const u32x4 q0 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g));
+          const u32x4 q1 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g + 1));
+          wb[0] = q0[0]; wb[1] = q0[1]; wb[2] = q0[2]; wb[3] = q0[3];
+          wb[4] = q1[0]; wb[5] = q1[1]; wb[6] = q1[2]; wb[7] = q1[3];
+        } else {
+          wb = wa;
+        }
       }
-    }
-    const float sw0 = *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 64);
-    const float sw1 = kGateUp ? *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 68) : 0.0f;
+      const float sw0 = *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 64);
+      const float sw1 = kGateUp ? *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 68) : 0.0f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (t < ntb) {
+      for (int t = 0; t < NT; ++t) {
         const int r = t * 16 + m16;
         const u32x4 x0 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g));
         const u32x4 x1 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g + 1));
@@ -223,6 +234,16 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
         }
       }
     }
+  };
+  switch (ntb) {
+    case 1: kloop(IntC<1>{}); break;
+    case 2: kloop(IntC<2>{}); break;
+    case 3: kloop(IntC<3>{}); break;
+    case 4: kloop(IntC<4>{}); break;
+    case 5: kloop(IntC<5>{}); break;
+    case 6: kloop(IntC<6>{}); break;
+    case 7: kloop(IntC<7>{}); break;
+    default: kloop(IntC<8>{}); break;
   }
   __syncthreads();
   float(*red)[kF8TileM] = reinterpret_cast<float(*)[kF8TileM]>(ring);  // [8][128] amax table
