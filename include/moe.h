@@ -103,6 +103,11 @@ size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E);
  *            lower expert id; NaN ranks lowest. Exactly k distinct experts per token.
  *   topk_idx [T, k] int32 chosen expert ids in ascending order.
  *   topk_w   [T, k] f32 = route_scale * score_e / sum over chosen score (unbiased scores).
+ * With bf16 inputs, logits == NULL, H % 64 == 0 and T >= 512 the selection is first made
+ * from bf16 matrix-core dot products with a proven error bound and kept where that bound
+ * separates the chosen keys from the rest (the weights then come from exact fp64 dot
+ * products of the chosen experts); every other token goes through the fp64 path. The
+ * expert ids are the same either way; weights agree to fp32 rounding.
  * Limits: 1 <= k <= min(E, 16), E <= 1024, T >= 0, H >= 1 and H % 8 == 0. */
 moe_status moe_route(const void* x, moe_dtype x_dt, const void* w_router, const float* bias,
                      int32_t T, int32_t H, int32_t E, int32_t k, moe_score_fn fn,

@@ -17,6 +17,9 @@
 // Kernel 2 (k_topk): one wavefront per token; sums the K-split partials in a fixed order
 //   (deterministic), rounds to fp32, scores, and selects k experts by k rounds of a
 //   64-lane max over packed (key, expert) 64-bit values.
+// For bf16 inputs from 512 tokens on, when the logits are not asked for, kernels 1f and
+// 2f (below) first select from bf16 matrix-core sums with a proven error bound, and
+// kernels 1 and 2 then route only the tokens whose selection that bound leaves open.
 #include "moe_internal.h"
 
 namespace moe {
@@ -46,69 +49,100 @@ constexpr int kRouterBigT = 512;
 
 // part[s][t][e] = sum over k in split s of x[t,k] * wr[e,k], in fp64; a wavefront computes
 // kRT x kRE tiles of 16 tokens x 16 experts.
+// K splits for the n listed tokens: up to kFbMaxSplits (and H / 256), as far as the
+// partial-sum buffer (cap rows of E) allows; the partials are [splits][n][E].
+constexpr int kFbMaxSplits = 16;
+__device__ __forceinline__ int fb_splits(int n, int64_t cap, int H, int* klen) {
+  int64_t sp = H / 256 < kFbMaxSplits ? H / 256 : kFbMaxSplits;
+  if (n > 0 && sp > cap / n) sp = cap / n;
+  if (sp < 1) sp = 1;
+  int len = (int)((H + sp - 1) / sp);
+  len = (len + 31) / 32 * 32;
+  *klen = len;
+  return (H + len - 1) / len;
+}
+
+// With a token list (list, cnt): row t of the tile is token list[t], for t < *cnt, with
+// its own K splits (fb_splits; cap rows of partials).
 template <bool kBF16, int kRT, int kRE>
 __global__ void __launch_bounds__(64) k_router_gemm(const void* __restrict__ x,
                                                      const void* __restrict__ wr, int T, int H,
-                                                     int E, int klen, double* __restrict__ part) {
+                                                     int E, int klen, double* __restrict__ part,
+                                                     const int32_t* __restrict__ list,
+                                                     const int32_t* __restrict__ cnt, int64_t cap) {
   const int l = threadIdx.x;
   const int m = l & 15, kq = l >> 4;
-  const int t0 = blockIdx.y * 16 * kRT, e0 = blockIdx.x * 16 * kRE;
-  int64_t xrow[kRT], wrow[kRE];
-#pragma unroll
-  for (int i = 0; i < kRT; ++i) {
-    const int t = t0 + 16 * i + m;
-    xrow[i] = (int64_t)(t < T ? t : T - 1) * H;
+  const int e0 = blockIdx.x * 16 * kRE;
+  const int nrows = list ? *cnt : T;
+  int64_t stride = T;
+  if (list) {
+    if ((int)blockIdx.z >= fb_splits(nrows, cap, H, &klen)) return;
+    stride = nrows;
   }
+  // a grid over all tiles without a list; with one, a few rows of workgroups step through
+  // the listed tokens' tiles
+  for (int ty = blockIdx.y;; ty += gridDim.y) {
+    const int t0 = ty * 16 * kRT;
+    if (t0 >= nrows) return;
+    int64_t xrow[kRT], wrow[kRE];
 #pragma unroll
-  for (int j = 0; j < kRE; ++j) {
-    const int e = e0 + 16 * j + m;
-    wrow[j] = (int64_t)(e < E ? e : E - 1) * H;
-  }
-  const int kb = blockIdx.z * klen;
-  const int ke = min(H, kb + klen);
-  f64x4 acc[kRT][kRE];
-#pragma unroll
-  for (int i = 0; i < kRT; ++i)
-#pragma unroll
-    for (int j = 0; j < kRE; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int k0 = kb; k0 < ke; k0 += 32) {
-    const int kk = k0 + kq * 8;
-    double a[kRT][8], b[kRE][8];
-    if (kk < ke) {
-#pragma unroll
-      for (int i = 0; i < kRT; ++i) load8<kBF16>(x, xrow[i] + kk, a[i]);
-#pragma unroll
-      for (int j = 0; j < kRE; ++j) load8<kBF16>(wr, wrow[j] + kk, b[j]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-#pragma unroll
-        for (int i = 0; i < kRT; ++i) a[i][q] = 0.0;
-#pragma unroll
-        for (int j = 0; j < kRE; ++j) b[j][q] = 0.0;
-      }
+    for (int i = 0; i < kRT; ++i) {
+      const int t = t0 + 16 * i + m;
+      const int r = t < nrows ? t : nrows - 1;
+      xrow[i] = (int64_t)(list ? list[r] : r) * H;
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int i = 0; i < kRT; ++i)
-#pragma unroll
-        for (int j = 0; j < kRE; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i][q], b[j][q], acc[i][j], 0, 0, 0);
-  }
-  // the f64 16x16x4 MFMA leaves D[row kq + 4*r][column m] in lane l, register r
-  // (unlike the 16x16 f32-accumulating forms, whose rows are 4*kq + r)
-#pragma unroll
-  for (int i = 0; i < kRT; ++i)
 #pragma unroll
     for (int j = 0; j < kRE; ++j) {
-      const int eo = e0 + 16 * j + m;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int to = t0 + 16 * i + kq + 4 * r;
-        if (to < T && eo < E) part[((int64_t)blockIdx.z * T + to) * E + eo] = acc[i][j][r];
-      }
+      const int e = e0 + 16 * j + m;
+      wrow[j] = (int64_t)(e < E ? e : E - 1) * H;
     }
+    const int kb = blockIdx.z * klen;
+    const int ke = min(H, kb + klen);
+    f64x4 acc[kRT][kRE];
+#pragma unroll
+    for (int i = 0; i < kRT; ++i)
+#pragma unroll
+      for (int j = 0; j < kRE; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int k0 = kb; k0 < ke; k0 += 32) {
+      const int kk = k0 + kq * 8;
+      double a[kRT][8], b[kRE][8];
+      if (kk < ke) {
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) load8<kBF16>(x, xrow[i] + kk, a[i]);
+#pragma unroll
+        for (int j = 0; j < kRE; ++j) load8<kBF16>(wr, wrow[j] + kk, b[j]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+#pragma unroll
+          for (int i = 0; i < kRT; ++i) a[i][q] = 0.0;
+#pragma unroll
+          for (int j = 0; j < kRE; ++j) b[j][q] = 0.0;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int i = 0; i < kRT; ++i)
+#pragma unroll
+          for (int j = 0; j < kRE; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i][q], b[j][q], acc[i][j], 0, 0, 0);
+    }
+    // the f64 16x16x4 MFMA leaves D[row kq + 4*r][column m] in lane l, register r
+    // (unlike the 16x16 f32-accumulating forms, whose rows are 4*kq + r)
+#pragma unroll
+    for (int i = 0; i < kRT; ++i)
+#pragma unroll
+      for (int j = 0; j < kRE; ++j) {
+        const int eo = e0 + 16 * j + m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int to = t0 + 16 * i + kq + 4 * r;
+          if (to < nrows && eo < E) part[((int64_t)blockIdx.z * stride + to) * E + eo] = acc[i][j][r];
+        }
+      }
+    if (!list) return;
+  }
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
@@ -139,15 +173,27 @@ __device__ __forceinline__ uint32_t key_order(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// With a token list (list, cnt): wavefront p < *cnt handles token list[p], whose partials
+// are row p of part.
 __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, int S, int T, int E,
                                               int k, int fn, float scale,
                                               const float* __restrict__ bias,
                                               int32_t* __restrict__ topk_idx,
                                               float* __restrict__ topk_w,
-                                              float* __restrict__ logits) {
+                                              float* __restrict__ logits,
+                                              const int32_t* __restrict__ list,
+                                              const int32_t* __restrict__ cnt, int H, int64_t cap) {
   const int l = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int p0 = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n = list ? *cnt : T;
+  if (p0 >= n) return;
+  const int t = list ? list[p0] : p0;
+  int64_t stride = T;
+  if (list) {
+    int kl;
+    S = fb_splits(n, cap, H, &kl);
+    stride = n;
+  }
   float lg[kTopkMaxPerLane];
   double sc[kTopkMaxPerLane];
   uint64_t key[kTopkMaxPerLane];
@@ -160,7 +206,7 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
       // unrolled so that the loads of a group of partials are in flight together; the
       // sum still runs in split order
 #pragma unroll 8
-      for (int p = 0; p < S; ++p) s += part[((int64_t)p * T + t) * E + e];
+      for (int p = 0; p < S; ++p) s += part[((int64_t)p * stride + p0) * E + e];
       lg[i] = (float)s;
       if (logits) logits[(int64_t)t * E + e] = lg[i];
     }
@@ -235,6 +281,390 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
   }
 }
 
+// ------------------------------------------------------------- certified fast router
+//
+// Used for bf16 inputs when the fp32 logits themselves are not asked for.
+// Kernel 1f (k_router_fast) multiplies on the bf16 matrix cores: each 64-element K block
+// of a (token, expert) dot product is summed in fp32 by two chained
+// v_mfma_f32_16x16x32_bf16 (a product of two bf16 values is exact in fp32), and the block
+// sums are added in fp64. The wavefronts of the first expert tile (token tile) also sum
+// the squares of the x (router) rows they load, in fp64.
+// Kernel 2f (k_topk_fast) bounds the distance of every such sum from the exact dot
+// product, turns the bound into an interval for each expert's key (key and score are
+// non-decreasing in the logit: sigmoid; for softmax, in the own logit and non-increasing
+// in the others), and takes the k experts of the largest approximate keys only if every
+// chosen interval lies strictly above every other one. The exact keys then choose the
+// same k experts, and their exact fp64 dot products give the fp32 logits and the
+// weights. A token without that separation (near-ties, non-finite values) is appended
+// to a list that the exact kernels 1 and 2 then route.
+//
+// The bound. A block sum of 64 exact products formed with fp32 additions, in whatever
+// order the matrix core adds and as long as each addition errs by at most 2^-23 of its
+// result, lies within 64 * 2^-23 of the sum of the products' magnitudes from the exact
+// block sum; kCertRel doubles that. Over all blocks, and by Cauchy-Schwarz,
+// |sum - exact| <= kCertRel ||x_t|| ||w_e||. Inputs or products in the subnormal range
+// may be flushed to zero: such a product is below 2^-126 max(|x_h|, |w_h|, 1), covered
+// by H 2^-126 (||x_t|| + ||w_e|| + 1). The fp64 additions (errors near 2^-50 relative)
+// are covered by the factor 1 + 2^-30.
+constexpr double kCertRel = 0x1p-16;  // 2 * 64 * 2^-23
+constexpr int kFastTM = 2, kFastTN = 4;  // a wavefront: 32 tokens x 64 experts
+constexpr int kXcds = 8;                 // MI355X: workgroups dealt to 8 XCDs round-robin
+// rows of 16-token tiles in the grid of the exact kernel over the token list
+constexpr int kListTileRows = 64;
+
+// Work items (K split z, token tile ty, expert tile ex), ex fastest, are cut into kXcds
+// contiguous chunks; chunk c runs on the workgroups the dispatcher deals to XCD c
+// (blockIdx mod kXcds), so that the expert tiles reading one x tile share an L2.
+__global__ void __launch_bounds__(64) k_router_fast(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ wr, int T,
+                                                     int H, int E, int klen, int ntt, int net,
+                                                     int nz, double* __restrict__ part,
+                                                     double* __restrict__ pnx,
+                                                     double* __restrict__ pnw,
+                                                     int32_t* __restrict__ cnt) {
+  constexpr int TM = kFastTM, TN = kFastTN;
+  const int l = threadIdx.x;
+  const int m = l & 15, g = l >> 4;
+  const int nitems = nz * ntt * net;
+  const int chunk = (nitems + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * chunk + slot;
+  if (blockIdx.x == 0 && l == 0) *cnt = 0;
+  if (slot >= chunk || item >= nitems) return;
+  const int ex = item % net, ty = (item / net) % ntt, z = item / (net * ntt);
+  const int t0 = ty * 16 * TM, e0 = ex * 16 * TN;
+  const bool sum_x = ex == 0, sum_w = ty == 0;
+  // lane (m, g) loads elements 16 g .. 16 g + 15 of each 64-element block of row m of
+  // each tile; k-step h of the block multiplies elements 16 g + 8 h .. + 7 (the same
+  // permutation of K in both operands)
+  const uint16_t* xp[TM];
+  const uint16_t* wp[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int t = t0 + 16 * i + m;
+    xp[i] = x + (int64_t)(t < T ? t : T - 1) * H + 16 * g;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int e = e0 + 16 * j + m;
+    wp[j] = wr + (int64_t)(e < E ? e : E - 1) * H + 16 * g;
+  }
+  const int kb = z * klen;
+  const int ke = min(H, kb + klen);
+  f64x4 acc[TM][TN];
+  double sx[TM], sw[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    sx[i] = 0.0;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) sw[j] = 0.0;
+  auto sq = [](uint4 q) {
+    const double v0 = bf16_lo(q.x), v1 = bf16_hi(q.x), v2 = bf16_lo(q.y), v3 = bf16_hi(q.y);
+    const double v4 = bf16_lo(q.z), v5 = bf16_hi(q.z), v6 = bf16_lo(q.w), v7 = bf16_hi(q.w);
+    return ((v0 * v0 + v1 * v1) + (v2 * v2 + v3 * v3)) + ((v4 * v4 + v5 * v5) + (v6 * v6 + v7 * v7));
+  };
+  struct Frag {
+    uint4 a[TM][2], b[TN][2];
+  };
+  auto load = [&](int k0, Frag& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      f.a[i][0] = *reinterpret_cast<const uint4*>(xp[i] + k0);
+      f.a[i][1] = *reinterpret_cast<const uint4*>(xp[i] + k0 + 8);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      f.b[j][0] = *reinterpret_cast<const uint4*>(wp[j] + k0);
+      f.b[j][1] = *reinterpret_cast<const uint4*>(wp[j] + k0 + 8);
+    }
+  };
+  auto mult = [&](const Frag& f) {
+    // one fp32 chain per tile (both k-steps of the block), all tiles' chains independent
+    f32x4 p[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        p[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[i][0]),
+                                                          __builtin_bit_cast(bf16x8, f.b[j][0]),
+                                                          f32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        p[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[i][1]),
+                                                          __builtin_bit_cast(bf16x8, f.b[j][1]),
+                                                          p[i][j], 0, 0, 0);
+    if (sum_x) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sx[i] += sq(f.a[i][0]) + sq(f.a[i][1]);
+    }
+    if (sum_w) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sw[j] += sq(f.b[j][0]) + sq(f.b[j][1]);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] += (double)p[i][j][r];
+  };
+  // (requesting blocks one or two ahead through a register ring measured no faster: the
+  // extra registers halve the wavefronts a SIMD holds)
+  for (int k0 = kb; k0 < ke; k0 += 64) {
+    Frag f;
+    load(k0, f);
+    mult(f);
+  }
+  // the f32-accumulating 16x16 MFMA leaves D[row 4 g + r][column m] in lane l, register r
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int eo = e0 + 16 * j + m;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int to = t0 + 16 * i + 4 * g + r;
+        if (to < T && eo < E) part[((int64_t)z * T + to) * E + eo] = acc[i][j][r];
+      }
+    }
+  // the four lanes of a row (g = 0..3) hold its four 16-element quarters of every block
+  if (sum_x) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      double v = sx[i];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      const int t = t0 + 16 * i + m;
+      if (g == 0 && t < T) pnx[(int64_t)z * T + t] = v;
+    }
+  }
+  if (sum_w) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      double v = sw[j];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      const int e = e0 + 16 * j + m;
+      if (g == 0 && e < E) pnw[(int64_t)z * E + e] = v;
+    }
+  }
+}
+
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t w = __shfl_xor(v, o, 64);
+    v = w < v ? w : v;
+  }
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__global__ void __launch_bounds__(256, 3) k_topk_fast(
+    const double* __restrict__ part, const double* __restrict__ pnx,
+    const double* __restrict__ pnw, int S, int T, int H, int E, int k, int fn, float scale,
+    const float* __restrict__ bias, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ wr, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ list, int32_t* __restrict__ cnt) {
+  const int l = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  double nx2 = 0.0;
+  for (int p = 0; p < S; ++p) nx2 += pnx[(int64_t)p * T + t];
+  const double nx = sqrt(nx2);
+  const double tiny = (double)H * 0x1p-126;
+  float lo[kTopkMaxPerLane], hi[kTopkMaxPerLane], mid[kTopkMaxPerLane];
+  bool fin = true;
+#pragma unroll
+  for (int i = 0; i < kTopkMaxPerLane; ++i) {
+    const int e = i * 64 + l;
+    lo[i] = hi[i] = mid[i] = 0.0f;
+    if (e < E) {
+      double sum = 0.0, nw2 = 0.0;
+#pragma unroll 8
+      for (int p = 0; p < S; ++p) {
+        sum += part[((int64_t)p * T + t) * E + e];
+        nw2 += pnw[(int64_t)p * E + e];
+      }
+      const double nw = sqrt(nw2);
+      const double beta = (kCertRel * nx * nw + tiny * (nx + nw + 1.0)) * (1.0 + 0x1p-30);
+      fin = fin && __builtin_isfinite(sum) && __builtin_isfinite(beta);
+      // the exact logit fp32(exact sum) lies in [lo, hi] (rounding is monotone)
+      lo[i] = (float)(sum - beta);
+      hi[i] = (float)(sum + beta);
+      mid[i] = (float)sum;
+    }
+  }
+  bool certified = __all(fin);
+  uint32_t klo[kTopkMaxPerLane], khi[kTopkMaxPerLane];
+  uint64_t key[kTopkMaxPerLane];
+  if (certified) {
+    // The interval keys use fp32 exp, whose results (with the add and the division) are
+    // within 2^-20 of the exact values; kWiden moves each bound outward by more than
+    // that. exp of an fp32 difference d also carries the rounding of d, |d| 2^-24
+    // relative, which lo_exp / hi_exp add per term. The middle keys only order the
+    // candidates.
+    constexpr double kWiden = 0x1p-17;
+    auto lo_exp = [&](float d) { return (double)expf(d) * (1.0 - kWiden - fabs((double)d) * 0x1p-22); };
+    auto hi_exp = [&](float d) { return (double)expf(d) * (1.0 + kWiden + fabs((double)d) * 0x1p-22); };
+    // softmax over intervals: p_e is smallest with its own logit low and the others high,
+    // largest the other way round (sums of the exponentials first, then each key)
+    float mh = 0.0f, mm = 0.0f;
+    double Alo = 0.0, Ahi = 0.0, Am = 0.0;
+    const double rel = (double)E * 0x1p-50;  // rounding of the fp64 sums, relative
+    if (fn != MOE_SIGMOID) {
+      float fh = -INFINITY, fm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kTopkMaxPerLane; ++i)
+        if (i * 64 + l < E) { fh = fmaxf(fh, hi[i]); fm = fmaxf(fm, mid[i]); }
+      mh = wave_max_f32(fh);
+      mm = wave_max_f32(fm);
+#pragma unroll
+      for (int i = 0; i < kTopkMaxPerLane; ++i)
+        if (i * 64 + l < E) {
+          Alo += fmax(lo_exp(lo[i] - mh), 0.0);
+          Ahi += hi_exp(hi[i] - mh);
+          Am += (double)expf(mid[i] - mm);
+        }
+      Alo = wave_sum_f64(Alo);
+      Ahi = wave_sum_f64(Ahi);
+      Am = wave_sum_f64(Am);
+    }
+#pragma unroll
+    for (int i = 0; i < kTopkMaxPerLane; ++i) {
+      const int e = i * 64 + l;
+      klo[i] = khi[i] = 0u;
+      key[i] = 0ull;
+      if (e >= E) continue;
+      double slo, shi, smid;
+      if (fn == MOE_SIGMOID) {
+        slo = (double)(1.0f / (1.0f + expf(-lo[i]))) * (1.0 - kWiden);
+        shi = (double)(1.0f / (1.0f + expf(-hi[i]))) * (1.0 + kWiden);
+        smid = 1.0f / (1.0f + expf(-mid[i]));
+      } else {
+        // lo[i] <= hi[i] <= mh, so the exponentials are at most 1 (up to rounding)
+        const double alo = fmax(lo_exp(lo[i] - mh), 0.0), ahi = hi_exp(hi[i] - mh);
+        const double rest_hi = (Ahi - ahi) + Ahi * rel;
+        const double rest_lo = fmax((Alo - alo) - Alo * rel, 0.0);
+        slo = alo / (alo + rest_hi) * (1.0 - kWiden);
+        shi = ahi > 0.0 ? ahi / (ahi + rest_lo) * (1.0 + kWiden) : 0.0;
+        smid = (double)expf(mid[i] - mm) / Am;
+      }
+      float a = (float)slo, b = (float)shi, c = (float)smid;
+      if (bias) { a = a + bias[e]; b = b + bias[e]; c = c + bias[e]; }
+      klo[i] = key_order(a);
+      khi[i] = key_order(b);
+      key[i] = ((uint64_t)key_order(c) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    }
+  }
+  int sel[16];
+  if (certified) {
+    uint32_t chosen = 0u;  // bit i: expert 64 i + l is chosen
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int i = 0; i < kTopkMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
+      best = wave_max_u64(best);
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+      sel[r] = e;
+#pragma unroll
+      for (int i = 0; i < kTopkMaxPerLane; ++i)
+        if (i * 64 + l == e) { key[i] = 0ull; chosen |= 1u << i; }
+    }
+    uint32_t min_in = 0xFFFFFFFFu, max_out = 0u;
+#pragma unroll
+    for (int i = 0; i < kTopkMaxPerLane; ++i) {
+      if (i * 64 + l >= E) continue;
+      if (chosen >> i & 1u) min_in = klo[i] < min_in ? klo[i] : min_in;
+      else max_out = khi[i] > max_out ? khi[i] : max_out;
+    }
+    certified = wave_min_u32(min_in) > wave_max_u32(max_out);
+  }
+  if (!certified) {
+    if (l == 0) list[atomicAdd(cnt, 1)] = t;
+    return;
+  }
+  for (int a = 1; a < k; ++a) {
+    int v = sel[a], b = a - 1;
+    while (b >= 0 && sel[b] > v) { sel[b + 1] = sel[b]; --b; }
+    sel[b + 1] = v;
+  }
+  // exact logits of the chosen experts: fp64 dot products, rounded once to fp32. Lane l
+  // takes the 8-element chunks l, l + 64, ... of x and of the chosen router rows, eight
+  // experts at a time, whose loads of one chunk are issued together.
+  const uint16_t* xr = x + (int64_t)t * H;
+  double lg[16];
+  double mx = -INFINITY;
+  for (int r0 = 0; r0 < k; r0 += 8) {
+    int woff[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) woff[r] = (r0 + r < k ? sel[r0 + r] : sel[r0]) * H;
+    double dot[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) dot[r] = 0.0;
+    for (int h = 8 * l; h < H; h += 512) {
+      const uint4 a = *reinterpret_cast<const uint4*>(xr + h);
+      uint4 b[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) b[r] = *reinterpret_cast<const uint4*>(wr + woff[r] + h);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        double d = dot[r];
+        d += (double)bf16_lo(a.x) * (double)bf16_lo(b[r].x);
+        d += (double)bf16_hi(a.x) * (double)bf16_hi(b[r].x);
+        d += (double)bf16_lo(a.y) * (double)bf16_lo(b[r].y);
+        d += (double)bf16_hi(a.y) * (double)bf16_hi(b[r].y);
+        d += (double)bf16_lo(a.z) * (double)bf16_lo(b[r].z);
+        d += (double)bf16_hi(a.z) * (double)bf16_hi(b[r].z);
+        d += (double)bf16_lo(a.w) * (double)bf16_lo(b[r].w);
+        d += (double)bf16_hi(a.w) * (double)bf16_hi(b[r].w);
+        dot[r] = d;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const double v = (double)(float)wave_sum_f64(dot[r]);
+      if (r0 + r < k) {
+        lg[r0 + r] = v;
+        mx = fmax(mx, v);
+      }
+    }
+  }
+  // weights from the unbiased scores of the chosen experts (softmax: renormalised over
+  // the chosen, i.e. the softmax of their logits)
+  double sc[16];
+  double tot = 0.0;
+  for (int r = 0; r < k; ++r) {
+    sc[r] = fn == MOE_SIGMOID ? 1.0 / (1.0 + exp(-lg[r])) : exp(lg[r] - mx);
+    tot += sc[r];
+  }
+  if (l < k) {
+    double v = 0.0;
+    int e = 0;
+    for (int r = 0; r < k; ++r)
+      if (r == l) { v = sc[r]; e = sel[r]; }
+    topk_idx[(int64_t)t * k + l] = e;
+    topk_w[(int64_t)t * k + l] = (float)((double)scale * v / tot);
+  }
+}
+
 void router_tiles(int32_t T, int* tt, int* te) {
   *tt = T >= kRouterBigT ? 4 : 1;
   *te = T >= kRouterBigT ? 2 : 1;
@@ -256,11 +686,17 @@ int route_splits(int32_t T, int32_t H, int32_t E, int* klen) {
 
 }  // namespace
 
+namespace {
+size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+}  // namespace
+
+// part [S][T][E] f64, then (certified fast router) the squared-norm partials of the x
+// rows [S][T] and router rows [S][E] in f64, the token list [T] int32 and its count.
 size_t route_ws_bytes(int32_t T, int32_t H, int32_t E) {
   int klen;
   int S = route_splits(T, H, E, &klen);
-  size_t part = (size_t)S * T * E * sizeof(double);
-  return (part + 255) / 256 * 256;
+  return al256((size_t)S * T * E * sizeof(double)) + al256((size_t)S * T * sizeof(double)) +
+         al256((size_t)S * E * sizeof(double)) + al256((size_t)T * sizeof(int32_t)) + 256;
 }
 
 hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const float* bias,
@@ -270,21 +706,63 @@ hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const flo
   int klen;
   int S = route_splits(T, H, E, &klen);
   double* part = reinterpret_cast<double*>(ws);
+  if (x_dt == MOE_BF16 && logits == nullptr && H % 64 == 0 && T >= kRouterBigT) {
+    char* w = reinterpret_cast<char*>(ws) + al256((size_t)S * T * E * sizeof(double));
+    double* pnx = reinterpret_cast<double*>(w);
+    w += al256((size_t)S * T * sizeof(double));
+    double* pnw = reinterpret_cast<double*>(w);
+    w += al256((size_t)S * E * sizeof(double));
+    int32_t* list = reinterpret_cast<int32_t*>(w);
+    int32_t* cnt = reinterpret_cast<int32_t*>(w + al256((size_t)T * sizeof(int32_t)));
+    // K splits of the fast kernel: about kRouterWaves wavefronts, at most S (the buffers)
+    const int64_t tiles = (int64_t)((E + 16 * kFastTN - 1) / (16 * kFastTN)) *
+                          ((T + 16 * kFastTM - 1) / (16 * kFastTM));
+    int64_t sf = (kRouterWaves + tiles - 1) / tiles;
+    sf = sf < 1 ? 1 : sf > S ? S : sf;
+    int flen = (int)((H + sf - 1) / sf);
+    flen = (flen + 63) / 64 * 64;
+    const int SF = (H + flen - 1) / flen;
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    const uint16_t* wb = reinterpret_cast<const uint16_t*>(wr);
+    const int net = (E + 16 * kFastTN - 1) / (16 * kFastTN), ntt = (T + 16 * kFastTM - 1) / (16 * kFastTM);
+    const int nblk = (SF * ntt * net + kXcds - 1) / kXcds * kXcds;  // whole rounds of kXcds
+    hipLaunchKernelGGL(k_router_fast, dim3(nblk), dim3(64), 0, s, xb, wb, T, H, E, flen, ntt, net, SF,
+                       part, pnx, pnw, cnt);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_topk_fast, dim3((T + 3) / 4), dim3(256), 0, s, part, pnx, pnw, SF, T, H, E,
+                       k, (int)fn, scale, bias, xb, wb, topk_idx, topk_w, list, cnt);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // the listed tokens, exactly: the grid covers T tokens, wavefronts past the count exit
+    const int64_t cap = (int64_t)S * T;
+    const dim3 gx((E + 15) / 16, (T + 15) / 16 < kListTileRows ? (T + 15) / 16 : kListTileRows,
+                  kFbMaxSplits);
+    hipLaunchKernelGGL((k_router_gemm<true, 1, 1>), gx, dim3(64), 0, s, x, wr, T, H, E, klen, part,
+                       list, cnt, cap);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, part, S, T, E, k, (int)fn, scale,
+                       bias, topk_idx, topk_w, nullptr, list, cnt, H, cap);
+    return hipGetLastError();
+  }
   int tt, te;
   router_tiles(T, &tt, &te);
   const dim3 g1((E + 16 * te - 1) / (16 * te), (T + 16 * tt - 1) / (16 * tt), S);
   if (x_dt == MOE_BF16 && tt == 4)
-    hipLaunchKernelGGL((k_router_gemm<true, 4, 2>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
+    hipLaunchKernelGGL((k_router_gemm<true, 4, 2>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part,
+                       nullptr, nullptr, 0);
   else if (x_dt == MOE_BF16)
-    hipLaunchKernelGGL((k_router_gemm<true, 1, 1>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
+    hipLaunchKernelGGL((k_router_gemm<true, 1, 1>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part,
+                       nullptr, nullptr, 0);
   else if (tt == 4)
-    hipLaunchKernelGGL((k_router_gemm<false, 4, 2>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
+    hipLaunchKernelGGL((k_router_gemm<false, 4, 2>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part,
+                       nullptr, nullptr, 0);
   else
-    hipLaunchKernelGGL((k_router_gemm<false, 1, 1>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part);
+    hipLaunchKernelGGL((k_router_gemm<false, 1, 1>), g1, dim3(64), 0, s, x, wr, T, H, E, klen, part,
+                       nullptr, nullptr, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, part, S, T, E, k, (int)fn, scale,
-                     bias, topk_idx, topk_w, logits);
+                     bias, topk_idx, topk_w, logits, nullptr, nullptr, H, 0);
   return hipGetLastError();
 }
 
