@@ -72,6 +72,12 @@ __device__ __forceinline__ bf16x8 e2m1x8_bf16(uint32_t w, float scale) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// A compile-time int as a value, so that a generic lambda can be instantiated per count.
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 // Launchers of the kernel families (FfnArgs as set up by launch_grouped_ffn; mid_event,
 // if not null, is recorded between the gate/up and the down launches).
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event);

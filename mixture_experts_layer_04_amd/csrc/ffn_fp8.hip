@@ -83,11 +83,6 @@ __global__ void __launch_bounds__(256) k_quant_rows_fp8(const uint16_t* __restri
   }
 }
 
-template <int N>
-struct IntC {
-  static constexpr int value = N;
-};
-
 template <bool kGateUp>
 __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   // Each K block of the workgroup's operands -- its 128 (down) or 256 (gate/up) weight

@@ -206,53 +206,61 @@ __global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled
     if (p + S - 1 >= 0 && p + S - 1 < KT) issue_a(p + S - 1);
     if (p + SB - 1 >= 0 && p + SB - 1 < KT) issue_b(p + SB - 1);
   }
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + SL - 2 < KT) wait_vmcnt<AFTER>();
-    else wait_vmcnt<0>();
-    // A plain barrier, not __syncthreads(): its fence would wait for every outstanding
-    // DMA of the ring. The wait above already covers this thread's part of block kt.
-    __builtin_amdgcn_s_barrier();
-    if (kt + S - 1 < KT) issue_a(kt + S - 1);
-    if (kt + SB - 1 < KT) issue_b(kt + SB - 1);
-    // a wavefront whose rows all lie past the tile's last row has nothing to multiply (it
-    // still moves its share of the DMA and meets every barrier)
-    if (!live) continue;
-    const char* cur = smem + (kt % S) * ASTAGE;                 // activations of block kt
-    const char* curb = smem + S * ASTAGE + (kt % SB) * BSTAGE;  // weights of block kt
-    // MXFP4: this lane's 16 codes (elements 16 g .. 16 g + 15 of the K block) and scale
-    uint2 wq[kMX ? TN : 1];
-    float wsc[kMX ? TN : 1];
-    if (kMX) {
+  // The K loop, instantiated for wavefronts with rows to multiply (kLive) and for those
+  // whose rows all lie past the tile's last row, which only move their share of the DMA
+  // and meet every barrier. (Deciding this inside the loop, per K block, measured 2-7%
+  // slower; so did further instantiations per count of live 16-row sub-tiles, with the DMA
+  // of empty sub-tiles skipped.)
+  auto kloop = [&](auto live_c) {
+    constexpr bool kLive = decltype(live_c)::value != 0;
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + SL - 2 < KT) wait_vmcnt<AFTER>();
+      else wait_vmcnt<0>();
+      // A plain barrier, not __syncthreads(): its fence would wait for every outstanding
+      // DMA of the ring. The wait above already covers this thread's part of block kt.
+      __builtin_amdgcn_s_barrier();
+      if (kt + S - 1 < KT) issue_a(kt + S - 1);
+      if (kt + SB - 1 < KT) issue_b(kt + SB - 1);
+      if (!kLive) continue;
+      const char* cur = smem + (kt % S) * ASTAGE;                 // activations of block kt
+      const char* curb = smem + S * ASTAGE + (kt % SB) * BSTAGE;  // weights of block kt
+      // MXFP4: this lane's 16 codes (elements 16 g .. 16 g + 15 of the K block) and scale
+      uint2 wq[kMX ? TN : 1];
+      float wsc[kMX ? TN : 1];
+      if (kMX) {
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const char* rb = curb + brow[t] * 32;
-        // two 32-bit reads: with one 64-bit read the compiler makes it wait for all DMA
-        const char* q = rb + 8 * (g ^ (((brow[t] >> 3) & 1) << 1));
-        wq[t].x = *reinterpret_cast<const uint32_t*>(q);
-        wq[t].y = *reinterpret_cast<const uint32_t*>(q + 4);
-        wsc[t] = e8m0_f32(*reinterpret_cast<const uint8_t*>(curb + BN * 32 + 4 * brow[t] +
-                                                             (kt & 1) * 2 + (g >> 1)));
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 fa[TM], fb[TN];
-      const int c = 2 * g + ks;  // logical 16-B chunk
-#pragma unroll
-      for (int t = 0; t < TM; ++t)
-        fa[t] = *reinterpret_cast<const bf16x8*>(cur + lds_off(arow[t], c));
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        if (kMX) fb[t] = e2m1x8_bf16(ks ? wq[t].y : wq[t].x, wsc[t]);
-        else fb[t] = *reinterpret_cast<const bf16x8*>(curb + lds_off(brow[t], c));
+        for (int t = 0; t < TN; ++t) {
+          const char* rb = curb + brow[t] * 32;
+          // two 32-bit reads: with one 64-bit read the compiler makes it wait for all DMA
+          const char* q = rb + 8 * (g ^ (((brow[t] >> 3) & 1) << 1));
+          wq[t].x = *reinterpret_cast<const uint32_t*>(q);
+          wq[t].y = *reinterpret_cast<const uint32_t*>(q + 4);
+          wsc[t] = e8m0_f32(*reinterpret_cast<const uint8_t*>(curb + BN * 32 + 4 * brow[t] +
+                                                               (kt & 1) * 2 + (g >> 1)));
+        }
       }
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 fa[TM], fb[TN];
+        const int c = 2 * g + ks;  // logical 16-B chunk
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int t = 0; t < TM; ++t)
+          fa[t] = *reinterpret_cast<const bf16x8*>(cur + lds_off(arow[t], c));
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          if (kMX) fb[t] = e2m1x8_bf16(ks ? wq[t].y : wq[t].x, wsc[t]);
+          else fb[t] = *reinterpret_cast<const bf16x8*>(curb + lds_off(brow[t], c));
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
     }
-  }
+  };
+  if (live) kloop(IntC<1>{});
+  else kloop(IntC<0>{});
 #pragma unroll
   for (int mt = 0; mt < TM; ++mt) {
 #pragma unroll
