@@ -191,34 +191,42 @@ __global__ void __launch_bounds__(128 * WGN, 2) k_w4a4(FfnArgs a, int nb_per_til
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
     if (p < KT) issue(p);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * OPS>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kt + S - 1 < KT) issue(kt + S - 1);
-    if (!live) continue;
-    const char* st = ring + (kt % S) * STG;
-    i32x8 fa[TM], fb[TN];
-    int sa[TM], sb[TN];
+  // the K loop, instantiated for wavefronts with rows to multiply and for those without
+  // (which still move their share of the DMA and meet every barrier): no branch on the
+  // rows inside the loop
+  auto kloop = [&](auto live_c) {
+    constexpr bool kLive = decltype(live_c)::value != 0;
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * OPS>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kt + S - 1 < KT) issue(kt + S - 1);
+      if (!kLive) continue;
+      const char* st = ring + (kt % S) * STG;
+      i32x8 fa[TM], fb[TN];
+      int sa[TM], sb[TN];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + a4_off(arow[t], g));
-      fa[t] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-      sa[t] = (int)(*reinterpret_cast<const uint32_t*>(st + ACODES + BCODES + 4 * arow[t]) >> (8 * g));
+      for (int t = 0; t < TM; ++t) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + a4_off(arow[t], g));
+        fa[t] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        sa[t] = (int)(*reinterpret_cast<const uint32_t*>(st + ACODES + BCODES + 4 * arow[t]) >> (8 * g));
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + ACODES + a4_off(brow[t], g));
+        fb[t] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        sb[t] = (int)(*reinterpret_cast<const uint32_t*>(st + ACODES + BCODES + 4 * (BM + brow[t])) >> (8 * g));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], 4, 4,
+                                                                        0, sa[i], 0, sb[j]);
     }
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + ACODES + a4_off(brow[t], g));
-      fb[t] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-      sb[t] = (int)(*reinterpret_cast<const uint32_t*>(st + ACODES + BCODES + 4 * (BM + brow[t])) >> (8 * g));
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], 4, 4,
-                                                                      0, sa[i], 0, sb[j]);
-  }
+  };
+  if (live) kloop(IntC<1>{});
+  else kloop(IntC<0>{});
   // lane holds D[row 4 g + i of row tile mt][column m16 of weight tile nt]
 #pragma unroll
   for (int mt = 0; mt < TM; ++mt) {
