@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--overlap", action="store_true",
                     help="also time the step with the shared expert on a side stream")
-    ap.add_argument("--cpu-tokens", type=int, default=48,
+    ap.add_argument("--cpu-tokens", type=int, default=72,
                     help="tokens of the batch the CPU oracle leg computes (about 10 s of CPU work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (a known-size "
