@@ -13,6 +13,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStreamTileM = 16;   // streaming kernels (few rows per expert)
 constexpr int kTiledM = 128;       // LDS-tiled bf16 / MXFP4 kernel
 constexpr int kTiledN = 128;       // its weight rows per workgroup (gate/up: 64 features)
+constexpr int kTiledMB = 256;      // LDS-tiled bf16 kernel with 256 x 256 tiles
+constexpr int kTiledNB = 256;      // (where H % 256 == 0 and I % 128 == 0)
 constexpr int kF8TileM = 128;      // fp8 kernel
 constexpr int kF8Feat = 128;       // fp8 output features per workgroup = one scale block
 constexpr int kF8K = 128;          // fp8 K block = one scale block

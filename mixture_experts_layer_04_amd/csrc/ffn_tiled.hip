@@ -3,10 +3,14 @@
 // Token Dispatch with FP8/FP4 Grouped GEMM via CUDA Green Contexts" (key_changes, fourth
 // item), planned for gfx950.
 //
-// A workgroup computes a tile of 128 rows x 128 weight rows (gate/up: the gate and up rows
-// of 64 features, alternating by 16, so that each lane holds gate and up of the same
-// (row, feature) and SwiGLU is applied in registers) with 4 wavefronts in a 2 x 2 grid,
-// each (16 TM) x (16 TN) with v_mfma_f32_16x16x32_bf16. The K blocks (64 elements) go
+// A workgroup computes a tile of rows x weight rows (gate/up: the gate and up rows of
+// half as many features, alternating by 16, so that each lane holds gate and up of the
+// same (row, feature) and SwiGLU is applied in registers) with a WGM x WGN grid of
+// wavefronts, each (16 TM) x (16 TN) with v_mfma_f32_16x16x32_bf16: for bf16, 256 x 256
+// with 16 wavefronts of 64 x 64 (one workgroup a CU, four wavefronts a SIMD) where H and
+// I allow, else 128 x 128 with 4 wavefronts (two workgroups a CU); for MXFP4 128 x 256
+// with 4 wavefronts of 64 x 128. Per flop the 256 x 256 tile moves half the bytes from
+// L2 into LDS, which bounds these kernels. The K blocks (64 elements) go
 // from global memory straight into LDS with global_load_lds (no register staging),
 // through an S-stage ring, so that each block has S-1 blocks of MFMA work to hide
 // behind. A lane's fragment of a K block is the 32 contiguous bytes at 32 (lane / 16)
@@ -55,6 +59,19 @@ constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt to them round-robi
 #ifndef MOE_T2_WAVES_PER_SIMD
 #define MOE_T2_WAVES_PER_SIMD 2
 #endif
+// bf16 with 256 x 256 tiles: 4 x 4 wavefronts of 4 x 4 MFMA tiles; a 2-stage activation
+// ring with 2 (gate/up) or 3 (down: its weights stream from HBM) weight stages, 128 or
+// 160 KB of LDS
+#ifndef MOE_T2B_STAGES_B_GU
+#define MOE_T2B_STAGES_B_GU 2
+#endif
+#ifndef MOE_T2B_STAGES_B_DN
+#define MOE_T2B_STAGES_B_DN 3
+#endif
+static_assert(4 * 16 * 4 == kTiledMB && 4 * 16 * 4 == kTiledNB, "tile shape of the tile list");
+// waves a SIMD that the register budget must allow: a 16-wavefront workgroup puts four on
+// each SIMD of its CU
+constexpr int waves_per_simd(int nw) { return nw >= 16 ? 4 : MOE_T2_WAVES_PER_SIMD; }
 constexpr int kT2Threads = 64 * MOE_T2_WGM * MOE_T2_WGN;
 constexpr int kT2M = MOE_T2_WGM * 16 * MOE_T2_TM, kT2N = MOE_T2_WGN * 16 * MOE_T2_TN;
 static_assert(kT2M == kTiledM && kT2N == kTiledN, "tile shape of the tile list");
@@ -66,7 +83,7 @@ static_assert(kT2M == kTiledM && kT2N == kTiledN, "tile shape of the tile list")
 // all banks) and 4 scale bytes a row (those of K blocks kt & ~1 and (kt & ~1) + 1, one
 // aligned dword), and fragments are decoded to bf16 in registers as they are read.
 template <int TM, int TN, int WGM, int WGN, int S, int SB, bool kGateUp, bool kYF32, bool kMX>
-__global__ void __launch_bounds__(64 * WGM * WGN, MOE_T2_WAVES_PER_SIMD) k_tiled2(FfnArgs a, int nb_per_tile) {
+__global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_tiled2(FfnArgs a, int nb_per_tile) {
   constexpr int NW = WGM * WGN;
   constexpr int BM = WGM * 16 * TM, BN = WGN * 16 * TN;
   constexpr int BSTAGE = kMX ? BN * 32 + BN * 4 : BN * 128;  // weight bytes of a stage
@@ -317,6 +334,9 @@ hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_even
   auto fits = [&](int n) {
     return a.H % n == 0 && a.bank[0].I % (n / 2) == 0 && (!a.has_shared || a.bank[1].I % (n / 2) == 0);
   };
+  if (a.wdt != MOE_MXFP4 && a.tile_m == kTiledMB)
+    return launch_tiled_pair<4, 4, 4, 4, 2, MOE_T2B_STAGES_B_GU, MOE_T2B_STAGES_B_DN, false>(
+        a, s, mid_event);
   if (a.wdt != MOE_MXFP4)
     return launch_tiled_pair<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES,
                              MOE_T2_STAGES_B_GU, MOE_T2_STAGES_B_DN, false>(a, s, mid_event);

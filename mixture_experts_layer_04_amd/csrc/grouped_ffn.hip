@@ -40,10 +40,15 @@ int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32
                ? kStreamTileM
                : kTiledM;
   // Few rows per expert: stream the weights (each weight element read once per tile of
-  // <= 16 rows). Many rows: LDS-tiled GEMM with 128-row tiles.
-  const bool tiled_ok =
-      H % kTiledN == 0 && I_routed % (kTiledN / 2) == 0 && I_shared % (kTiledN / 2) == 0;
-  if (wdt == MOE_BF16 && tiled_ok && (int64_t)rows > 32 * (int64_t)groups) return kTiledM;
+  // <= 16 rows). Many rows: LDS-tiled GEMM with 256-row tiles (256 weight rows a
+  // workgroup) where H and I allow, else 128-row tiles.
+  auto tiled_ok = [&](int n) {
+    return H % n == 0 && I_routed % (n / 2) == 0 && I_shared % (n / 2) == 0;
+  };
+  if (wdt == MOE_BF16 && (int64_t)rows > 32 * (int64_t)groups) {
+    if (tiled_ok(kTiledNB)) return kTiledMB;
+    if (tiled_ok(kTiledN)) return kTiledM;
+  }
   return kStreamTileM;
 }
 
@@ -75,7 +80,7 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
     a.h_xs = reinterpret_cast<uint8_t*>(scratch) + ((size_t)a.rows_total * (a.I_max / 2) + 255) / 256 * 256;
     return launch_ffn_w4a4(a, s, mid_event);
   }
-  if (a.tile_m == kTiledM && (a.wdt == MOE_BF16 || a.wdt == MOE_MXFP4))
+  if ((a.tile_m == kTiledM || a.tile_m == kTiledMB) && (a.wdt == MOE_BF16 || a.wdt == MOE_MXFP4))
     return launch_ffn_tiled(a, s, mid_event);
   return launch_ffn_stream(a, s, mid_event);
 }
