@@ -20,7 +20,7 @@
 // For bf16 inputs from 512 tokens on, when the logits are not asked for, kernels 1f and
 // 2f (below) first select from bf16 matrix-core sums with a proven error bound, and
 // kernels 1 and 2 then route only the tokens whose selection that bound leaves open.
-#include "moe_internal.h"
+#include "ffn_common.h"  // LDS layout and DMA helpers of the tiled kernels
 
 namespace moe {
 namespace {
@@ -284,19 +284,20 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
 // ------------------------------------------------------------- certified fast router
 //
 // Used for bf16 inputs when the fp32 logits themselves are not asked for.
-// Kernel 1f (k_router_fast) multiplies on the bf16 matrix cores: each 64-element K block
+// Kernel 0f (k_row_norms2) sums the squares of every router row in fp64.
+// Kernel 1f (k_router_lds) multiplies on the bf16 matrix cores: each 64-element K block
 // of a (token, expert) dot product is summed in fp32 by two chained
 // v_mfma_f32_16x16x32_bf16 (a product of two bf16 values is exact in fp32), and the block
-// sums are added in fp64. The wavefronts of the first expert tile (token tile) also sum
-// the squares of the x (router) rows they load, in fp64.
-// Kernel 2f (k_topk_fast) bounds the distance of every such sum from the exact dot
-// product, turns the bound into an interval for each expert's key (key and score are
-// non-decreasing in the logit: sigmoid; for softmax, in the own logit and non-increasing
-// in the others), and takes the k experts of the largest approximate keys only if every
-// chosen interval lies strictly above every other one. The exact keys then choose the
-// same k experts, and their exact fp64 dot products give the fp32 logits and the
-// weights. A token without that separation (near-ties, non-finite values) is appended
-// to a list that the exact kernels 1 and 2 then route.
+// sums are added in fp64, one partial sum per K split.
+// Kernel 2f (k_topk_fast) adds the splits, sums the squares of the token's row in fp64,
+// bounds the distance of every sum from the exact dot product, turns the bound into an
+// interval for each expert's key (key and score are non-decreasing in the logit:
+// sigmoid; for softmax, in the own logit and non-increasing in the others), and takes the
+// k experts of the largest approximate keys only if every chosen interval lies strictly
+// above every other one. The exact keys then choose the same k experts, and their exact
+// fp64 dot products give the fp32 logits and the weights. A token without that
+// separation (near-ties, non-finite values) is appended to a list that the exact kernels
+// 1 and 2 then route.
 //
 // The bound. A block sum of 64 exact products formed with fp32 additions, in whatever
 // order the matrix core adds and as long as each addition errs by at most 2^-23 of its
@@ -307,104 +308,107 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
 // by H 2^-126 (||x_t|| + ||w_e|| + 1). The fp64 additions (errors near 2^-50 relative)
 // are covered by the factor 1 + 2^-30.
 constexpr double kCertRel = 0x1p-16;  // 2 * 64 * 2^-23
-constexpr int kFastTM = 2, kFastTN = 4;  // a wavefront: 32 tokens x 64 experts
-constexpr int kXcds = 8;                 // MI355X: workgroups dealt to 8 XCDs round-robin
+constexpr int kXcds = 8;              // MI355X: workgroups dealt to 8 XCDs round-robin
 // rows of 16-token tiles in the grid of the exact kernel over the token list
 constexpr int kListTileRows = 64;
 
-// Work items (K split z, token tile ty, expert tile ex), ex fastest, are cut into kXcds
-// contiguous chunks; chunk c runs on the workgroups the dispatcher deals to XCD c
-// (blockIdx mod kXcds), so that the expert tiles reading one x tile share an L2.
-__global__ void __launch_bounds__(64) k_router_fast(const uint16_t* __restrict__ x,
-                                                     const uint16_t* __restrict__ wr, int T,
-                                                     int H, int E, int klen, int ntt, int net,
-                                                     int nz, double* __restrict__ part,
-                                                     double* __restrict__ pnx,
-                                                     double* __restrict__ pnw,
-                                                     int32_t* __restrict__ cnt) {
-  constexpr int TM = kFastTM, TN = kFastTN;
-  const int l = threadIdx.x;
-  const int m = l & 15, g = l >> 4;
+// Kernel 1f: a workgroup of 4 x 2 wavefronts takes 128 tokens x 128 experts (a wavefront
+// 32 x 64), and each 64-element K block of the token rows and of the router rows goes
+// global -> LDS by DMA through an S-stage ring (the LDS layout and slot map of the tiled
+// expert GEMM), so every token row is fetched once per 128 experts and every router row
+// once per 128 tokens. Items (K split, token tile, expert tile), expert tile fastest, are
+// cut into kXcds contiguous chunks; chunk c runs on the workgroups the dispatcher deals to
+// XCD c (blockIdx mod kXcds), so that the expert tiles reading one token tile share an L2.
+#ifndef MOE_RT_STAGES
+#define MOE_RT_STAGES 2
+#endif
+#ifndef MOE_RT_WPS  // wavefronts a SIMD the register budget must allow
+#define MOE_RT_WPS 2
+#endif
+constexpr int kRtWgt = 4, kRtWge = 2;                          // wavefronts along tokens, experts
+constexpr int kRtTokens = kRtWgt * 32, kRtExperts = kRtWge * 64;  // 128 x 128
+
+__global__ void __launch_bounds__(64 * kRtWgt * kRtWge, MOE_RT_WPS) k_router_lds(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int E,
+    int klen, int ntt, int net, int nz, double* __restrict__ part,
+    int32_t* __restrict__ cnt) {
+  constexpr int TM = 2, TN = 4, NW = kRtWgt * kRtWge, S = MOE_RT_STAGES;
+  constexpr int XST = kRtTokens * 128, STG = XST + kRtExperts * 128;  // bytes a stage
+  constexpr int CX = kRtTokens / (NW * 8), CW = kRtExperts / (NW * 8);  // DMA ops a thread
+  constexpr int OPS = CX + CW;
+  static_assert(CX >= 1 && CW >= 1 && S >= 2 && (S - 2) * OPS < 64, "router ring");
+  __shared__ __attribute__((aligned(1024))) char smem[S * STG];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int m16 = l & 15, g = l >> 4;
   const int nitems = nz * ntt * net;
   const int chunk = (nitems + kXcds - 1) / kXcds;
   const int slot = blockIdx.x / kXcds;
   const int item = (blockIdx.x % kXcds) * chunk + slot;
-  if (blockIdx.x == 0 && l == 0) *cnt = 0;
+  if (blockIdx.x == 0 && tid == 0) *cnt = 0;
   if (slot >= chunk || item >= nitems) return;
   const int ex = item % net, ty = (item / net) % ntt, z = item / (net * ntt);
-  const int t0 = ty * 16 * TM, e0 = ex * 16 * TN;
-  const bool sum_x = ex == 0, sum_w = ty == 0;
-  // lane (m, g) loads elements 16 g .. 16 g + 15 of each 64-element block of row m of
-  // each tile; k-step h of the block multiplies elements 16 g + 8 h .. + 7 (the same
-  // permutation of K in both operands)
-  const uint16_t* xp[TM];
-  const uint16_t* wp[TN];
+  const int t0 = ty * kRtTokens, e0 = ex * kRtExperts;
+  const int wm = wave % kRtWgt, wn = wave / kRtWgt;
+  // DMA sources: 1-KB block q = NW i + wave of each tile (rows and 16-B chunks of dma_slot)
+  const char* xs[CX];
+  const char* ws[CW];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int t = t0 + 16 * i + m;
-    xp[i] = x + (int64_t)(t < T ? t : T - 1) * H + 16 * g;
+  for (int i = 0; i < CX; ++i) {
+    int r, c;
+    dma_slot(NW * i + wave, l, &r, &c);
+    const int t = t0 + r;
+    xs[i] = reinterpret_cast<const char*>(x) + (int64_t)(t < T ? t : T - 1) * H * 2 + c * 16;
   }
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int e = e0 + 16 * j + m;
-    wp[j] = wr + (int64_t)(e < E ? e : E - 1) * H + 16 * g;
+  for (int i = 0; i < CW; ++i) {
+    int r, c;
+    dma_slot(NW * i + wave, l, &r, &c);
+    const int e = e0 + r;
+    ws[i] = reinterpret_cast<const char*>(wr) + (int64_t)(e < E ? e : E - 1) * H * 2 + c * 16;
   }
-  const int kb = z * klen;
-  const int ke = min(H, kb + klen);
+  const int kb0 = z * klen / 64;
+  const int KT = (min(H, z * klen + klen) - z * klen) / 64;
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % S) * STG;
+    const int64_t o = (int64_t)(kb0 + kt) * 128;
+#pragma unroll
+    for (int i = 0; i < CX; ++i) dma16(xs[i] + o, st + (NW * i + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < CW; ++i) dma16(ws[i] + o, st + XST + (NW * i + wave) * 1024);
+  };
   f64x4 acc[TM][TN];
-  double sx[TM], sw[TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    sx[i] = 0.0;
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-  }
 #pragma unroll
-  for (int j = 0; j < TN; ++j) sw[j] = 0.0;
-  auto sq = [](uint4 q) {
-    const double v0 = bf16_lo(q.x), v1 = bf16_hi(q.x), v2 = bf16_lo(q.y), v3 = bf16_hi(q.y);
-    const double v4 = bf16_lo(q.z), v5 = bf16_hi(q.z), v6 = bf16_lo(q.w), v7 = bf16_hi(q.w);
-    return ((v0 * v0 + v1 * v1) + (v2 * v2 + v3 * v3)) + ((v4 * v4 + v5 * v5) + (v6 * v6 + v7 * v7));
-  };
-  struct Frag {
-    uint4 a[TM][2], b[TN][2];
-  };
-  auto load = [&](int k0, Frag& f) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      f.a[i][0] = *reinterpret_cast<const uint4*>(xp[i] + k0);
-      f.a[i][1] = *reinterpret_cast<const uint4*>(xp[i] + k0 + 8);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      f.b[j][0] = *reinterpret_cast<const uint4*>(wp[j] + k0);
-      f.b[j][1] = *reinterpret_cast<const uint4*>(wp[j] + k0 + 8);
-    }
-  };
-  auto mult = [&](const Frag& f) {
-    // one fp32 chain per tile (both k-steps of the block), all tiles' chains independent
+  for (int p = 0; p < S - 1; ++p)
+    if (p < KT) issue(p);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * OPS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + S - 1 < KT) issue(kt + S - 1);
+    const char* st = smem + (kt % S) * STG;
+    // one fp32 chain per 16 x 16 tile over the block's two k-steps, then added in fp64
     f32x4 p[TM][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 fa[TM], fb[TN];
+      const int c = 2 * g + ks;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        p[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[i][0]),
-                                                          __builtin_bit_cast(bf16x8, f.b[j][0]),
-                                                          f32x4{0, 0, 0, 0}, 0, 0, 0);
+      for (int t = 0; t < TM; ++t)
+        fa[t] = *reinterpret_cast<const uint4*>(st + lds_off(wm * 32 + 16 * t + m16, c));
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int t = 0; t < TN; ++t)
+        fb[t] = *reinterpret_cast<const uint4*>(st + XST + lds_off(wn * 64 + 16 * t + m16, c));
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        p[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[i][1]),
-                                                          __builtin_bit_cast(bf16x8, f.b[j][1]),
-                                                          p[i][j], 0, 0, 0);
-    if (sum_x) {
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) sx[i] += sq(f.a[i][0]) + sq(f.a[i][1]);
-    }
-    if (sum_w) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sw[j] += sq(f.b[j][0]) + sq(f.b[j][1]);
+        for (int j = 0; j < TN; ++j)
+          p[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]),
+              ks ? p[i][j] : f32x4{0, 0, 0, 0}, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -412,47 +416,36 @@ __global__ void __launch_bounds__(64) k_router_fast(const uint16_t* __restrict__
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] += (double)p[i][j][r];
-  };
-  // (requesting blocks one or two ahead through a register ring measured no faster: the
-  // extra registers halve the wavefronts a SIMD holds)
-  for (int k0 = kb; k0 < ke; k0 += 64) {
-    Frag f;
-    load(k0, f);
-    mult(f);
   }
   // the f32-accumulating 16x16 MFMA leaves D[row 4 g + r][column m] in lane l, register r
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int eo = e0 + 16 * j + m;
+      const int eo = e0 + wn * 64 + 16 * j + m16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int to = t0 + 16 * i + 4 * g + r;
+        const int to = t0 + wm * 32 + 16 * i + 4 * g + r;
         if (to < T && eo < E) part[((int64_t)z * T + to) * E + eo] = acc[i][j][r];
       }
     }
-  // the four lanes of a row (g = 0..3) hold its four 16-element quarters of every block
-  if (sum_x) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      double v = sx[i];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      const int t = t0 + 16 * i + m;
-      if (g == 0 && t < T) pnx[(int64_t)z * T + t] = v;
-    }
+}
+
+// Squared norms of the router rows, in fp64 (one wavefront a row, a fixed summation order).
+__global__ void __launch_bounds__(256) k_row_norms2(const uint16_t* __restrict__ w, int n, int H,
+                                                    double* __restrict__ out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (row >= n) return;
+  const uint16_t* p = w + (int64_t)row * H;
+  double v = 0.0;
+  for (int h = 8 * l; h < H; h += 512) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p + h);
+    const double v0 = bf16_lo(q.x), v1 = bf16_hi(q.x), v2 = bf16_lo(q.y), v3 = bf16_hi(q.y);
+    const double v4 = bf16_lo(q.z), v5 = bf16_hi(q.z), v6 = bf16_lo(q.w), v7 = bf16_hi(q.w);
+    v += ((v0 * v0 + v1 * v1) + (v2 * v2 + v3 * v3)) + ((v4 * v4 + v5 * v5) + (v6 * v6 + v7 * v7));
   }
-  if (sum_w) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      double v = sw[j];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      const int e = e0 + 16 * j + m;
-      if (g == 0 && e < E) pnw[(int64_t)z * E + e] = v;
-    }
-  }
+  v = wave_sum_f64(v);
+  if (l == 0) out[row] = v;
 }
 
 __device__ __forceinline__ double wave_max_f64(double v) {
@@ -478,17 +471,25 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 __global__ void __launch_bounds__(256, 3) k_topk_fast(
-    const double* __restrict__ part, const double* __restrict__ pnx,
-    const double* __restrict__ pnw, int S, int T, int H, int E, int k, int fn, float scale,
+    const double* __restrict__ part, const double* __restrict__ nw2s, int S, int T, int H, int E,
+    int k, int fn, float scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ wr, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ list, int32_t* __restrict__ cnt) {
   const int l = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // ||x_t||^2 in fp64 from the token's row (its chunks are read again, from cache, for the
+  // exact dot products below)
+  const uint16_t* xr = x + (int64_t)t * H;
   double nx2 = 0.0;
-  for (int p = 0; p < S; ++p) nx2 += pnx[(int64_t)p * T + t];
-  const double nx = sqrt(nx2);
+  for (int h = 8 * l; h < H; h += 512) {
+    const uint4 q = *reinterpret_cast<const uint4*>(xr + h);
+    const double v0 = bf16_lo(q.x), v1 = bf16_hi(q.x), v2 = bf16_lo(q.y), v3 = bf16_hi(q.y);
+    const double v4 = bf16_lo(q.z), v5 = bf16_hi(q.z), v6 = bf16_lo(q.w), v7 = bf16_hi(q.w);
+    nx2 += ((v0 * v0 + v1 * v1) + (v2 * v2 + v3 * v3)) + ((v4 * v4 + v5 * v5) + (v6 * v6 + v7 * v7));
+  }
+  const double nx = sqrt(wave_sum_f64(nx2));
   const double tiny = (double)H * 0x1p-126;
   float lo[kTopkMaxPerLane], hi[kTopkMaxPerLane], mid[kTopkMaxPerLane];
   bool fin = true;
@@ -497,13 +498,10 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
     const int e = i * 64 + l;
     lo[i] = hi[i] = mid[i] = 0.0f;
     if (e < E) {
-      double sum = 0.0, nw2 = 0.0;
+      double sum = 0.0;
 #pragma unroll 8
-      for (int p = 0; p < S; ++p) {
-        sum += part[((int64_t)p * T + t) * E + e];
-        nw2 += pnw[(int64_t)p * E + e];
-      }
-      const double nw = sqrt(nw2);
+      for (int p = 0; p < S; ++p) sum += part[((int64_t)p * T + t) * E + e];
+      const double nw = sqrt(nw2s[e]);
       const double beta = (kCertRel * nx * nw + tiny * (nx + nw + 1.0)) * (1.0 + 0x1p-30);
       fin = fin && __builtin_isfinite(sum) && __builtin_isfinite(beta);
       // the exact logit fp32(exact sum) lies in [lo, hi] (rounding is monotone)
@@ -609,7 +607,6 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
   // exact logits of the chosen experts: fp64 dot products, rounded once to fp32. Lane l
   // takes the 8-element chunks l, l + 64, ... of x and of the chosen router rows, eight
   // experts at a time, whose loads of one chunk are issued together.
-  const uint16_t* xr = x + (int64_t)t * H;
   double lg[16];
   double mx = -INFINITY;
   for (int r0 = 0; r0 < k; r0 += 8) {
@@ -690,13 +687,13 @@ namespace {
 size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 }  // namespace
 
-// part [S][T][E] f64, then (certified fast router) the squared-norm partials of the x
-// rows [S][T] and router rows [S][E] in f64, the token list [T] int32 and its count.
+// part [S][T][E] f64, then (certified fast router) the squared norms of the router rows
+// [E] in f64, the token list [T] int32 and its count.
 size_t route_ws_bytes(int32_t T, int32_t H, int32_t E) {
   int klen;
   int S = route_splits(T, H, E, &klen);
-  return al256((size_t)S * T * E * sizeof(double)) + al256((size_t)S * T * sizeof(double)) +
-         al256((size_t)S * E * sizeof(double)) + al256((size_t)T * sizeof(int32_t)) + 256;
+  return al256((size_t)S * T * E * sizeof(double)) + al256((size_t)E * sizeof(double)) +
+         al256((size_t)T * sizeof(int32_t)) + 256;
 }
 
 hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const float* bias,
@@ -708,15 +705,13 @@ hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const flo
   double* part = reinterpret_cast<double*>(ws);
   if (x_dt == MOE_BF16 && logits == nullptr && H % 64 == 0 && T >= kRouterBigT) {
     char* w = reinterpret_cast<char*>(ws) + al256((size_t)S * T * E * sizeof(double));
-    double* pnx = reinterpret_cast<double*>(w);
-    w += al256((size_t)S * T * sizeof(double));
-    double* pnw = reinterpret_cast<double*>(w);
-    w += al256((size_t)S * E * sizeof(double));
+    double* nw2 = reinterpret_cast<double*>(w);
+    w += al256((size_t)E * sizeof(double));
     int32_t* list = reinterpret_cast<int32_t*>(w);
     int32_t* cnt = reinterpret_cast<int32_t*>(w + al256((size_t)T * sizeof(int32_t)));
-    // K splits of the fast kernel: about kRouterWaves wavefronts, at most S (the buffers)
-    const int64_t tiles = (int64_t)((E + 16 * kFastTN - 1) / (16 * kFastTN)) *
-                          ((T + 16 * kFastTM - 1) / (16 * kFastTM));
+    // K splits of the LDS kernel: about kRouterWaves wavefronts, at most S (the buffers)
+    const int net = (E + kRtExperts - 1) / kRtExperts, ntt = (T + kRtTokens - 1) / kRtTokens;
+    const int64_t tiles = (int64_t)net * ntt * (kRtWgt * kRtWge);
     int64_t sf = (kRouterWaves + tiles - 1) / tiles;
     sf = sf < 1 ? 1 : sf > S ? S : sf;
     int flen = (int)((H + sf - 1) / sf);
@@ -724,14 +719,15 @@ hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const flo
     const int SF = (H + flen - 1) / flen;
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
     const uint16_t* wb = reinterpret_cast<const uint16_t*>(wr);
-    const int net = (E + 16 * kFastTN - 1) / (16 * kFastTN), ntt = (T + 16 * kFastTM - 1) / (16 * kFastTM);
-    const int nblk = (SF * ntt * net + kXcds - 1) / kXcds * kXcds;  // whole rounds of kXcds
-    hipLaunchKernelGGL(k_router_fast, dim3(nblk), dim3(64), 0, s, xb, wb, T, H, E, flen, ntt, net, SF,
-                       part, pnx, pnw, cnt);
+    hipLaunchKernelGGL(k_row_norms2, dim3((E + 3) / 4), dim3(256), 0, s, wb, E, H, nw2);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_topk_fast, dim3((T + 3) / 4), dim3(256), 0, s, part, pnx, pnw, SF, T, H, E,
-                       k, (int)fn, scale, bias, xb, wb, topk_idx, topk_w, list, cnt);
+    const int nblk = (SF * ntt * net + kXcds - 1) / kXcds * kXcds;  // whole rounds of kXcds
+    hipLaunchKernelGGL(k_router_lds, dim3(nblk), dim3(64 * kRtWgt * kRtWge), 0, s, xb, wb, T, H, E,
+                       flen, ntt, net, SF, part, cnt);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_topk_fast, dim3((T + 3) / 4), dim3(256), 0, s, part, nw2, SF, T, H, E, k,
+                       (int)fn, scale, bias, xb, wb, topk_idx, topk_w, list, cnt);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // the listed tokens, exactly: the grid covers T tokens, wavefronts past the count exit
     const int64_t cap = (int64_t)S * T;
