@@ -4,7 +4,7 @@
 // Shared Expert"). A gather, not an atomic scatter: each thread owns 8 consecutive
 // elements of one token, sums the k rows in slot order in fp32, adds the shared row and
 // rounds once, so the result is deterministic. Loads and stores are 16 B (bf16) or
-// 2 x 16 B (fp32) per lane.
+// 2 x 16 B (fp32) per lane, up to four rows' loads in flight per lane.
 #include "moe_internal.h"
 
 namespace moe {
@@ -49,14 +49,27 @@ __global__ void __launch_bounds__(256) k_combine(const void* __restrict__ y,
   const int h = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (h >= H) return;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; ++j) {
-    const int64_t a = (int64_t)t * k + j;
-    const int r = inv_perm[a];
-    const float wj = w[a];
-    float v[8];
-    load8f<kYF32>(y, (int64_t)r * H + h, v);
+  // slots in groups of four: the group's row loads are all issued before the first is
+  // used; the sum still runs in slot order
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    const int64_t a = (int64_t)t * k + j0;
+    const int nj = k - j0 < 4 ? k - j0 : 4;
+    int r[4];
+    float wj[4], v[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+    for (int j = 0; j < 4; ++j) {
+      r[j] = j < nj ? inv_perm[a + j] : 0;
+      wj[j] = j < nj ? w[a + j] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < nj) load8f<kYF32>(y, (int64_t)r[j] * H + h, v[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < nj) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wj[j] * v[j][i];
+      }
   }
   if (shared) {
     float v[8];
