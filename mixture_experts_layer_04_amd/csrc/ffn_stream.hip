@@ -8,6 +8,9 @@
 // v_mfma_f32_16x16x32_bf16, fp32 v_mfma_f32_16x16x4_f32. Because a dot product may be
 // summed in any order, the K index carried by lane group kq and register slot j is
 // k0 + 16*kq + j (bf16) -- the same map for A and B -- which makes every load contiguous.
+// Two wavefronts of a workgroup share one group of weight rows, each streaming half of
+// its K range; their fp32 partial sums meet in LDS and are added in K order (shorter
+// streams per wavefront measured 1-2% faster than whole rows, longer ones slower).
 #include "ffn_common.h"
 
 namespace moe {
@@ -74,6 +77,12 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
 #ifndef MOE_STREAM_UNROLL_DN
 #define MOE_STREAM_UNROLL_DN 8
 #endif
+#ifndef MOE_STREAM_KSPLIT_GU  // gate/up: wavefronts that share one row group, each a K range
+#define MOE_STREAM_KSPLIT_GU 2
+#endif
+#ifndef MOE_STREAM_KSPLIT_DN  // the same for down
+#define MOE_STREAM_KSPLIT_DN 2
+#endif
 // Weight fragment: ordinary cached loads (on MI355X they measured faster than
 // non-temporal ones for this many-rows-at-once pattern).
 __device__ __forceinline__ Frag32 load_w(const void* p) { return load_c(p); }
@@ -92,9 +101,10 @@ __device__ __forceinline__ f32x4 mma(const Frag32& w, const Frag32& x, f32x4 acc
   return kF32 ? mma_f32(w, x, acc) : mma_bf16(w, x, acc);
 }
 
-// Gate/up + SwiGLU. Workgroup = (tile, block of 64 R h features); wavefront w computes
-// features [f0, f0 + 16 R) of h: gate rows f0.. and up rows I + f0.. of W13[e], R groups of
-// 16 rows each reusing one activation fragment per K step.
+// Gate/up + SwiGLU. Workgroup = (tile, block of 64 R / KS h features); wavefronts
+// w = KS q + ks compute features [f0, f0 + 16 R) of h, f0 from q, over K range ks: gate
+// rows f0.. and up rows I + f0.. of W13[e], R groups of 16 rows each reusing one
+// activation fragment per K step.
 template <bool kF32, int R>
 __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_tile) {
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -106,8 +116,12 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
   const int64_t ge = tl.group < a.E ? tl.group : 0;
   const int I = a.bank[bank].I;
   const int H = a.H;
-  const int f0 = (fb * 4 + wave) * 16 * R;
-  if (f0 >= I) return;
+  constexpr int KS = MOE_STREAM_KSPLIT_GU;
+  static_assert(4 % KS == 0, "K split divides the workgroup");
+  const int ks = wave % KS;
+  const int f0 = (fb * (4 / KS) + wave / KS) * 16 * R;
+  if (KS == 1 && f0 >= I) return;
+  const bool active = f0 < I;
   const int m = l & 15, kq = l >> 4;
   const int esz = kF32 ? 4 : 2;
   const char* w13 = reinterpret_cast<const char*>(a.bank[bank].w13) + ge * 2 * I * (int64_t)H * esz;
@@ -129,8 +143,11 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
   f32x4 accg[R], accu[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) accg[r] = accu[r] = f32x4{0, 0, 0, 0};
-  const int kmain = H - H % (kStep * U);
-  for (int k0 = 0; k0 < kmain; k0 += kStep * U) {
+  const int nst = H / kStep;
+  const int kbeg = active ? (ks * nst / KS) * kStep : 0;
+  const int kend = active ? ((ks + 1) * nst / KS) * kStep : 0;
+  const int kmain = kend - (kend - kbeg) % (kStep * U);
+  for (int k0 = kbeg; k0 < kmain; k0 += kStep * U) {
     Frag32 fg[U][R], fu[U][R], fx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -150,7 +167,7 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
         accu[r] = mma<kF32>(fu[u][r], fx[u], accu[r]);
       }
   }
-  for (int k0 = kmain; k0 < H; k0 += kStep) {
+  for (int k0 = kmain; k0 < kend; k0 += kStep) {
     const int64_t o = (int64_t)k0 * esz;
     const Frag32 fx = load_x(xr + o, xv);
 #pragma unroll
@@ -158,6 +175,26 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
       accg[r] = mma<kF32>(load_w(wg[r] + o), fx, accg[r]);
       accu[r] = mma<kF32>(load_w(wu[r] + o), fx, accu[r]);
     }
+  }
+  if constexpr (KS > 1) {
+    // the K ranges' partial sums meet in LDS; the first wavefront of each row group adds
+    // them in K order
+    __shared__ f32x4 red[4][2 * R][64];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      red[wave][r][l] = accg[r];
+      red[wave][R + r][l] = accu[r];
+    }
+    __syncthreads();
+    if (ks != 0 || !active) return;
+#pragma unroll
+    for (int j = 1; j < KS; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const f32x4 g = red[wave + j][r][l], u = red[wave + j][R + r][l];
+        accg[r] = f32x4{accg[r][0] + g[0], accg[r][1] + g[1], accg[r][2] + g[2], accg[r][3] + g[3]};
+        accu[r] = f32x4{accu[r][0] + u[0], accu[r][1] + u[1], accu[r][2] + u[2], accu[r][3] + u[3]};
+      }
   }
   if (xv) {
 #pragma unroll
@@ -170,8 +207,9 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
   }
 }
 
-// Down projection. Workgroup = (tile, block of 64 R output features of H); wavefront w
-// computes R groups of 16 output features, reusing one h fragment per K step.
+// Down projection. Workgroup = (tile, block of 64 R / KS output features of H); wavefronts
+// w = KS q + ks compute R groups of 16 output features over K range ks, reusing one h
+// fragment per K step.
 template <bool kF32, bool kYF32, int R>
 __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile) {
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -183,14 +221,22 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
   const int64_t ge = tl.group < a.E ? tl.group : 0;
   const int I = a.bank[bank].I;
   const int H = a.H;
-  const int f0 = (fb * 4 + wave) * 16 * R;
-  if (f0 >= H) return;
+  constexpr int KS = MOE_STREAM_KSPLIT_DN;
+  static_assert(4 % KS == 0, "K split divides the workgroup");
+  const int ks = wave % KS;
+  const int f0 = (fb * (4 / KS) + wave / KS) * 16 * R;
+  if (KS == 1 && f0 >= H) return;
+  const bool active = f0 < H;
   const int m = l & 15, kq = l >> 4;
   const int esz = kF32 ? 4 : 2;
   constexpr int kStep = kF32 ? 32 : 64;
   constexpr int kLane = kStep / 4;
   constexpr int U = MOE_STREAM_UNROLL_DN;
   const int64_t lane_off = (int64_t)kq * kLane * esz;
+  // this wavefront's K range [kbeg, kend), whole K steps
+  const int nst = I / kStep;
+  const int kbeg = active ? (ks * nst / KS) * kStep : 0;
+  const int kend = active ? ((ks + 1) * nst / KS) * kStep : 0;
   const bool xv = m < tl.nrows;
   const char* w2 = reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * esz;
   const char* wr[R];
@@ -201,8 +247,8 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
   f32x4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4{0, 0, 0, 0};
-  const int kmain = I - I % (kStep * U);
-  for (int k0 = 0; k0 < kmain; k0 += kStep * U) {
+  const int kmain = kend - (kend - kbeg) % (kStep * U);
+  for (int k0 = kbeg; k0 < kmain; k0 += kStep * U) {
     Frag32 fw[U][R], fh[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -216,11 +262,27 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r] = mma<kF32>(fw[u][r], fh[u], acc[r]);
   }
-  for (int k0 = kmain; k0 < I; k0 += kStep) {
+  for (int k0 = kmain; k0 < kend; k0 += kStep) {
     const int64_t o = (int64_t)k0 * esz;
     const Frag32 fh = load_x(hr + o, xv);
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = mma<kF32>(load_w(wr[r] + o), fh, acc[r]);
+  }
+  if constexpr (KS > 1) {
+    // the K ranges' partial sums meet in LDS; the first wavefront of each row group adds
+    // them in K order and stores
+    __shared__ f32x4 red[4][R][64];
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[wave][r][l] = acc[r];
+    __syncthreads();
+    if (ks != 0 || !active) return;
+#pragma unroll
+    for (int j = 1; j < KS; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const f32x4 v = red[wave + j][r][l];
+        acc[r] = f32x4{acc[r][0] + v[0], acc[r][1] + v[1], acc[r][2] + v[2], acc[r][3] + v[3]};
+      }
   }
   if (xv) {
 #pragma unroll
@@ -413,8 +475,10 @@ bool ffn_stream_mx_ok(int32_t H, int32_t I) { return H % kMxStreamK == 0 && I % 
 
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
   constexpr int RG = MOE_STREAM_ROWS_GU, RD = MOE_STREAM_ROWS_DN;
-  const int fb_gu = (a.I_max + kFeatPerWG * RG - 1) / (kFeatPerWG * RG);
-  const int fb_dn = (a.H + kFeatPerWG * RD - 1) / (kFeatPerWG * RD);
+  constexpr int KSG = MOE_STREAM_KSPLIT_GU;
+  const int fb_gu = (a.I_max + kFeatPerWG / KSG * RG - 1) / (kFeatPerWG / KSG * RG);
+  constexpr int KSD = MOE_STREAM_KSPLIT_DN;
+  const int fb_dn = (a.H + kFeatPerWG / KSD * RD - 1) / (kFeatPerWG / KSD * RD);
   const bool f32 = a.wdt == MOE_F32;
   const bool yf32 = a.y_dt == MOE_F32;
   const dim3 blk(256);
@@ -433,13 +497,13 @@ hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_eve
     return hipGetLastError();
   }
   if (f32)
-    hipLaunchKernelGGL((k_gateup_stream<true, 1>), dim3(a.max_tiles * ((a.I_max + kFeatPerWG - 1) / kFeatPerWG)), blk, 0, s, a, (a.I_max + kFeatPerWG - 1) / kFeatPerWG);
+    hipLaunchKernelGGL((k_gateup_stream<true, 1>), dim3(a.max_tiles * ((a.I_max + kFeatPerWG / KSG - 1) / (kFeatPerWG / KSG))), blk, 0, s, a, (a.I_max + kFeatPerWG / KSG - 1) / (kFeatPerWG / KSG));
   else
     hipLaunchKernelGGL((k_gateup_stream<false, RG>), dim3(a.max_tiles * fb_gu), blk, 0, s, a, fb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
-  const int fb_dn1 = (a.H + kFeatPerWG - 1) / kFeatPerWG;
+  const int fb_dn1 = (a.H + kFeatPerWG / KSD - 1) / (kFeatPerWG / KSD);
   if (f32 && yf32)
     hipLaunchKernelGGL((k_down_stream<true, true, 1>), dim3(a.max_tiles * fb_dn1), blk, 0, s, a, fb_dn1);
   else if (f32)
