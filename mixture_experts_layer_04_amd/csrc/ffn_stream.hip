@@ -77,6 +77,9 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
 #ifndef MOE_STREAM_UNROLL_DN
 #define MOE_STREAM_UNROLL_DN 8
 #endif
+#ifndef MOE_STREAM_DN_LDS  // bf16 down with the tile's h rows staged in LDS (where I allows)
+#define MOE_STREAM_DN_LDS 1
+#endif
 #ifndef MOE_STREAM_KSPLIT_GU  // gate/up: wavefronts that share one row group, each a K range
 #define MOE_STREAM_KSPLIT_GU 2
 #endif
@@ -289,6 +292,67 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
     for (int r = 0; r < R; ++r)
       store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + 16 * r + kq * 4, acc[r]);
   }
+}
+
+// Down projection, bf16, with the tile's h rows staged in LDS: the workgroup's four
+// wavefronts (four groups of 16 output features) share each 512-element K chunk of the
+// 16 h rows, which goes global -> LDS by DMA (each wavefront one 1-KB row piece of four
+// rows) through two buffers, instead of every wavefront loading it into registers. Lane l
+// of the DMA of row p takes the 16-B piece l ^ p of the row, so that the 16 rows' reads of
+// one lane group fall in different banks. Needs I % 512 == 0.
+constexpr int kDnLdsK = 512;  // K elements per chunk (8 MFMA steps)
+template <bool kYF32>
+__global__ void __launch_bounds__(256) k_down_stream_lds(FfnArgs a, int fb_per_tile) {
+  constexpr int U = kDnLdsK / 64;
+  constexpr int CB = 16 * kDnLdsK * 2;  // bytes of a chunk
+  __shared__ __attribute__((aligned(1024))) char hs[2 * CB];
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int tile_id = blockIdx.x / fb_per_tile;
+  const int fb = blockIdx.x - tile_id * fb_per_tile;
+  if (tile_id >= *a.ntiles) return;
+  const Tile tl = a.tiles[tile_id];
+  const int bank = tl.group < a.E ? 0 : 1;
+  const int64_t ge = tl.group < a.E ? tl.group : 0;
+  const int I = a.bank[bank].I;
+  const int H = a.H;
+  const int f0 = (fb * 4 + wave) * 16;
+  const bool active = f0 < H;
+  const int m = l & 15, kq = l >> 4;
+  const bool xv = m < tl.nrows;
+  const char* wr = reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * 2 +
+                   (int64_t)(active ? f0 + m : 0) * I * 2 + kq * 32;
+  const char* hsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = 4 * wave + j;
+    const int rr = p < tl.nrows ? p : (tl.nrows > 0 ? tl.nrows - 1 : 0);  // padding rows: any valid row
+    hsrc[j] = reinterpret_cast<const char*>(a.h) + (int64_t)(tl.row0 + rr) * a.I_max * 2 + (l ^ p) * 16;
+  }
+  auto issue = [&](int c) {
+    char* dst = hs + (c & 1) * CB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(hsrc[j] + (int64_t)c * kDnLdsK * 2, dst + (4 * wave + j) * 1024);
+  };
+  const int nch = I / kDnLdsK;
+  f32x4 acc = f32x4{0, 0, 0, 0};
+  issue(0);
+  for (int c = 0; c < nch; ++c) {
+    Frag32 fw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) fw[u] = load_w(wr + (int64_t)(c * kDnLdsK + u * 64) * 2);
+    wait_vmcnt<2 * U>();  // this wavefront's DMA of chunk c (issued before the 2 U weight loads)
+    __builtin_amdgcn_s_barrier();  // ... and every other wavefront's; chunk c - 1 is read
+    if (c + 1 < nch) issue(c + 1);
+    const char* hb = hs + (c & 1) * CB + m * 1024;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      Frag32 fh;
+      fh.lo = *reinterpret_cast<const u32x4*>(hb + (((u * 8 + kq * 2) ^ m) << 4));
+      fh.hi = *reinterpret_cast<const u32x4*>(hb + (((u * 8 + kq * 2 + 1) ^ m) << 4));
+      acc = mma_bf16(fw[u], fh, acc);
+    }
+  }
+  if (xv && active) store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + kq * 4, acc);
 }
 
 // ------------------------------------------------------------------ MXFP4 weights
@@ -508,7 +572,13 @@ hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_eve
     hipLaunchKernelGGL((k_down_stream<true, true, 1>), dim3(a.max_tiles * fb_dn1), blk, 0, s, a, fb_dn1);
   else if (f32)
     hipLaunchKernelGGL((k_down_stream<true, false, 1>), dim3(a.max_tiles * fb_dn1), blk, 0, s, a, fb_dn1);
-  else if (yf32)
+  else if (MOE_STREAM_DN_LDS && a.bank[0].I % kDnLdsK == 0 && a.bank[1].I % kDnLdsK == 0) {
+    const int fbl = (a.H + kFeatPerWG - 1) / kFeatPerWG;
+    if (yf32)
+      hipLaunchKernelGGL((k_down_stream_lds<true>), dim3(a.max_tiles * fbl), blk, 0, s, a, fbl);
+    else
+      hipLaunchKernelGGL((k_down_stream_lds<false>), dim3(a.max_tiles * fbl), blk, 0, s, a, fbl);
+  } else if (yf32)
     hipLaunchKernelGGL((k_down_stream<false, true, RD>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
   else
     hipLaunchKernelGGL((k_down_stream<false, false, RD>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);

@@ -44,6 +44,12 @@ SMALL = [
               use_bias=True, scale=2.5, shared_I=128, seed=17, weight_seed=17),
     MoEConfig("bf16_tiled_softmax_f32out", T=1000, H=384, E=6, k=2, I=128, score="softmax",
               out="f32", seed=18, weight_seed=18),
+    # decode-sized groups with I a multiple of 512: the down projection stages h in LDS
+    # (ragged 16-row tiles: the shared expert's 37 rows)
+    MoEConfig("bf16_stream_lds_shared", T=37, H=320, E=12, k=3, I=1024, score="sigmoid",
+              use_bias=True, scale=2.5, shared_I=512, seed=22, weight_seed=22),
+    MoEConfig("bf16_stream_lds_f32out", T=6, H=192, E=5, k=2, I=512, score="softmax",
+              out="f32", seed=23, weight_seed=23),
     # a group of more tiles than one tile block (the shared expert's 2100 rows: nine tiles)
     MoEConfig("bf16_tile_blocks", T=2100, H=512, E=3, k=1, I=128, score="sigmoid",
               use_bias=True, scale=2.5, shared_I=128, out="f32", seed=21, weight_seed=21),
