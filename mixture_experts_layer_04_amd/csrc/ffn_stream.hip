@@ -368,6 +368,9 @@ __global__ void __launch_bounds__(256) k_down_stream_lds(FfnArgs a, int fb_per_t
 #ifndef MOE_STREAM_MX_U
 #define MOE_STREAM_MX_U 2
 #endif
+#ifndef MOE_STREAM_MX_LDS  // activation rows staged in LDS, shared by the workgroup
+#define MOE_STREAM_MX_LDS 1
+#endif
 #ifndef MOE_STREAM_MX_ROWS_GU
 #define MOE_STREAM_MX_ROWS_GU 2
 #endif
@@ -427,6 +430,21 @@ __device__ __forceinline__ void load_x_mx(const char* p, bool valid, u32x4* x) {
       x[4 * i + j] = valid ? *reinterpret_cast<const u32x4*>(p + 256 * i + 16 * j) : u32x4{0, 0, 0, 0};
 }
 
+// Activation rows staged in LDS (U == 2): an iteration's 512 elements of the tile's 16
+// rows (1 KB a row, 16 KB a chunk) go global -> LDS by DMA through two buffers shared by
+// the workgroup's four wavefronts; wavefront w stages rows 4 w .. 4 w + 3, lane l of row
+// p taking the row's 16-B piece l ^ p. Lane (m, kq) then reads pieces 4 kq + 16 i + j of
+// row m, the ones load_x_mx reads from global memory.
+constexpr int kMxChunk = 16 * 1024;
+__device__ __forceinline__ void read_x_mx_lds(const char* buf, int m, int kq, u32x4* x) {
+  const char* rb = buf + m * 1024;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[4 * i + j] = *reinterpret_cast<const u32x4*>(rb + (((4 * kq + 16 * i + j) ^ m) << 4));
+}
+
 // Gate/up + SwiGLU: wavefront w computes features [f0, f0 + 16 R) of h from the gate rows
 // f0.. and the up rows I + f0.. of W13[e].
 template <int R, int U>
@@ -441,14 +459,15 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
   const int I = a.bank[bank].I;
   const int H = a.H;
   const int f0 = (fb * 4 + wave) * 16 * R;
-  if (f0 >= I) return;
+  if (!MOE_STREAM_MX_LDS && f0 >= I) return;
+  const bool active = f0 < I;
   const int m = l & 15, kq = l >> 4;
   const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.bank[bank].w13) + ge * 2 * I * (int64_t)(H / 2);
   const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.bank[bank].w13_scale) + ge * 2 * I * (int64_t)(H / 32);
   const uint8_t *cg[R], *cu[R], *sg[R], *su[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t g = f0 + 16 * r + m, u = I + g;
+    const int64_t g = (active ? f0 : 0) + 16 * r + m, u = I + g;
     cg[r] = codes + g * (H / 2) + 16 * kq;
     cu[r] = codes + u * (H / 2) + 16 * kq;
     sg[r] = scales + g * (H / 32);
@@ -461,7 +480,25 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
   f32x4 accg[R], accu[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) accg[r] = accu[r] = f32x4{0, 0, 0, 0};
-  for (int k0 = 0; k0 < H; k0 += 256 * U) {
+#if MOE_STREAM_MX_LDS
+  static_assert(U == 2, "LDS staging of 1-KB row pieces");
+  __shared__ __attribute__((aligned(1024))) char xs[2 * kMxChunk];
+  const char* xsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = 4 * wave + j;
+    const int rp = tl.row0 + (p < tl.nrows ? p : (tl.nrows > 0 ? tl.nrows - 1 : 0));
+    const int64_t sp = a.a_rowmap ? a.a_rowmap[rp] : rp;
+    xsrc[j] = reinterpret_cast<const char*>(a.a) + sp * H * 2 + (l ^ p) * 16;
+  }
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16(xsrc[j] + (int64_t)c * 1024, xs + (c & 1) * kMxChunk + (4 * wave + j) * 1024);
+  };
+  issue(0);
+#endif
+  for (int k0 = 0, c = 0; k0 < H; k0 += 256 * U, ++c) {
     MxCodes<U> wg[R], wu[R];
     u32x4 x[8 * U];
 #pragma unroll
@@ -469,14 +506,21 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
       wg[r] = load_mx<U>(cg[r] + k0 / 2, sg[r] + k0 / 32);
       wu[r] = load_mx<U>(cu[r] + k0 / 2, su[r] + k0 / 32);
     }
+#if MOE_STREAM_MX_LDS
+    wait_vmcnt<2 * R * (2 * U + 1)>();  // this wavefront's DMA of chunk c (before the weight loads)
+    __builtin_amdgcn_s_barrier();       // ... and the others'; chunk c - 1 is read
+    if (k0 + 256 * U < H) issue(c + 1);
+    read_x_mx_lds(xs + (c & 1) * kMxChunk, m, kq, x);
+#else
     load_x_mx<U>(xr + (int64_t)k0 * 2, xv, x);
+#endif
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       accg[r] = mma_mx<U>(wg[r], x, kq, accg[r]);
       accu[r] = mma_mx<U>(wu[r], x, kq, accu[r]);
     }
   }
-  if (xv) {
+  if (xv && active) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       f32x4 hv;
@@ -500,14 +544,15 @@ __global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_ti
   const int I = a.bank[bank].I;
   const int H = a.H;
   const int f0 = (fb * 4 + wave) * 16 * R;
-  if (f0 >= H) return;
+  if (!MOE_STREAM_MX_LDS && f0 >= H) return;
+  const bool active = f0 < H;
   const int m = l & 15, kq = l >> 4;
   const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.bank[bank].w2) + ge * (int64_t)H * (I / 2);
   const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.bank[bank].w2_scale) + ge * (int64_t)H * (I / 32);
   const uint8_t *cw[R], *sw[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t o = f0 + 16 * r + m;
+    const int64_t o = (active ? f0 : 0) + 16 * r + m;
     cw[r] = codes + o * (I / 2) + 16 * kq;
     sw[r] = scales + o * (I / 32);
   }
@@ -517,16 +562,40 @@ __global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_ti
   f32x4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4{0, 0, 0, 0};
-  for (int k0 = 0; k0 < I; k0 += 256 * U) {
+#if MOE_STREAM_MX_LDS
+  static_assert(U == 2, "LDS staging of 1-KB row pieces");
+  __shared__ __attribute__((aligned(1024))) char xs[2 * kMxChunk];
+  const char* xsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = 4 * wave + j;
+    const int rp = tl.row0 + (p < tl.nrows ? p : (tl.nrows > 0 ? tl.nrows - 1 : 0));
+    xsrc[j] = reinterpret_cast<const char*>(a.h) + (int64_t)rp * a.I_max * 2 + (l ^ p) * 16;
+  }
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16(xsrc[j] + (int64_t)c * 1024, xs + (c & 1) * kMxChunk + (4 * wave + j) * 1024);
+  };
+  issue(0);
+#endif
+  for (int k0 = 0, c = 0; k0 < I; k0 += 256 * U, ++c) {
     MxCodes<U> w[R];
     u32x4 x[8 * U];
 #pragma unroll
     for (int r = 0; r < R; ++r) w[r] = load_mx<U>(cw[r] + k0 / 2, sw[r] + k0 / 32);
+#if MOE_STREAM_MX_LDS
+    wait_vmcnt<R * (2 * U + 1)>();
+    __builtin_amdgcn_s_barrier();
+    if (k0 + 256 * U < I) issue(c + 1);
+    read_x_mx_lds(xs + (c & 1) * kMxChunk, m, kq, x);
+#else
     load_x_mx<U>(hr + (int64_t)k0 * 2, xv, x);
+#endif
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = mma_mx<U>(w[r], x, kq, acc[r]);
   }
-  if (xv) {
+  if (xv && active) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
       store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + 16 * r + kq * 4, acc[r]);
