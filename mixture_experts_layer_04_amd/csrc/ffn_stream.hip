@@ -378,6 +378,11 @@ __global__ void __launch_bounds__(256) k_down_stream_lds(FfnArgs a, int fb_per_t
 #define MOE_STREAM_MX_ROWS_DN 4
 #endif
 constexpr int kMxStreamK = 256 * MOE_STREAM_MX_U;  // K elements per iteration (divides H, I)
+// The wavefronts' 16 R-row groups must tile H and I exactly (both multiples of kMxStreamK):
+// a partial group would read weight rows past its expert's.
+static_assert(kMxStreamK % (16 * MOE_STREAM_MX_ROWS_GU) == 0 &&
+                  kMxStreamK % (16 * MOE_STREAM_MX_ROWS_DN) == 0,
+              "MXFP4 streaming row groups must divide the K iteration");
 
 template <int U>
 struct MxCodes {  // this lane's 32 U bytes of E2M1 codes and the row's 8 U scale bytes
@@ -436,13 +441,24 @@ __device__ __forceinline__ void load_x_mx(const char* p, bool valid, u32x4* x) {
 // p taking the row's 16-B piece l ^ p. Lane (m, kq) then reads pieces 4 kq + 16 i + j of
 // row m, the ones load_x_mx reads from global memory.
 constexpr int kMxChunk = 16 * 1024;
-__device__ __forceinline__ void read_x_mx_lds(const char* buf, int m, int kq, u32x4* x) {
+// The four pieces of word group i (read just before use, so that only 16 registers
+// hold activations).
+__device__ __forceinline__ void read_x_mx_lds(const char* buf, int m, int kq, int i, u32x4* x4) {
   const char* rb = buf + m * 1024;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j)
+    x4[j] = *reinterpret_cast<const u32x4*>(rb + (((4 * kq + 16 * i + j) ^ m) << 4));
+}
+// acc += word group i of w (decoded with its scale) x the matching 4 activation pieces
+template <int U>
+__device__ __forceinline__ f32x4 mma_mx_part(const MxCodes<U>& w, const u32x4* x4, int i, int kq,
+                                             f32x4 acc) {
+  const float sc = e8m0_f32((w.sc[i] >> (8 * kq)) & 0xFFu);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      x[4 * i + j] = *reinterpret_cast<const u32x4*>(rb + (((4 * kq + 16 * i + j) ^ m) << 4));
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e2m1x8_bf16(w.q[i][j], sc), as_bf16x8(x4[j]), acc,
+                                                  0, 0, 0);
+  return acc;
 }
 
 // Gate/up + SwiGLU: wavefront w computes features [f0, f0 + 16 R) of h from the gate rows
@@ -500,7 +516,6 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
 #endif
   for (int k0 = 0, c = 0; k0 < H; k0 += 256 * U, ++c) {
     MxCodes<U> wg[R], wu[R];
-    u32x4 x[8 * U];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       wg[r] = load_mx<U>(cg[r] + k0 / 2, sg[r] + k0 / 32);
@@ -510,15 +525,25 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
     wait_vmcnt<2 * R * (2 * U + 1)>();  // this wavefront's DMA of chunk c (before the weight loads)
     __builtin_amdgcn_s_barrier();       // ... and the others'; chunk c - 1 is read
     if (k0 + 256 * U < H) issue(c + 1);
-    read_x_mx_lds(xs + (c & 1) * kMxChunk, m, kq, x);
+#pragma unroll
+    for (int i = 0; i < 2 * U; ++i) {
+      u32x4 x4[4];
+      read_x_mx_lds(xs + (c & 1) * kMxChunk, m, kq, i, x4);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        accg[r] = mma_mx_part<U>(wg[r], x4, i, kq, accg[r]);
+        accu[r] = mma_mx_part<U>(wu[r], x4, i, kq, accu[r]);
+      }
+    }
 #else
+    u32x4 x[8 * U];
     load_x_mx<U>(xr + (int64_t)k0 * 2, xv, x);
-#endif
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       accg[r] = mma_mx<U>(wg[r], x, kq, accg[r]);
       accu[r] = mma_mx<U>(wu[r], x, kq, accu[r]);
     }
+#endif
   }
   if (xv && active) {
 #pragma unroll
@@ -581,19 +606,25 @@ __global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_ti
 #endif
   for (int k0 = 0, c = 0; k0 < I; k0 += 256 * U, ++c) {
     MxCodes<U> w[R];
-    u32x4 x[8 * U];
 #pragma unroll
     for (int r = 0; r < R; ++r) w[r] = load_mx<U>(cw[r] + k0 / 2, sw[r] + k0 / 32);
 #if MOE_STREAM_MX_LDS
     wait_vmcnt<R * (2 * U + 1)>();
     __builtin_amdgcn_s_barrier();
     if (k0 + 256 * U < I) issue(c + 1);
-    read_x_mx_lds(xs + (c & 1) * kMxChunk, m, kq, x);
+#pragma unroll
+    for (int i = 0; i < 2 * U; ++i) {
+      u32x4 x4[4];
+      read_x_mx_lds(xs + (c & 1) * kMxChunk, m, kq, i, x4);
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = mma_mx_part<U>(w[r], x4, i, kq, acc[r]);
+    }
 #else
+    u32x4 x[8 * U];
     load_x_mx<U>(hr + (int64_t)k0 * 2, xv, x);
-#endif
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = mma_mx<U>(w[r], x, kq, acc[r]);
+#endif
   }
   if (xv && active) {
 #pragma unroll
