@@ -41,8 +41,12 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, double* v) 
   }
 }
 
-// K splits are added until about this many wavefronts run (four a SIMD).
-constexpr int kRouterWaves = 4096;
+// K splits are added until about this many wavefronts run (two a SIMD; 1024, 4096 and
+// 8192 measured slower on the route step at T = 128 and T = 8192).
+#ifndef MOE_ROUTER_WAVES
+#define MOE_ROUTER_WAVES 2048
+#endif
+constexpr int kRouterWaves = MOE_ROUTER_WAVES;
 // Tokens from which a wavefront takes 4 x 2 tiles (each token fragment feeds 2 tiles,
 // each expert fragment 4); below it, one tile.
 constexpr int kRouterBigT = 512;
