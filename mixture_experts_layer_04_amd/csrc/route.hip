@@ -26,6 +26,17 @@ namespace moe {
 namespace {
 
 constexpr int kTopkMaxPerLane = 16;  // E <= 1024
+// The top-k kernels are instantiated for 1, 2, 4, 8 and 16 experts a lane; a launch takes
+// the smallest that covers E (registers and guards scale with it).
+#define MOE_TOPK_LAUNCH(KERNEL, E_, ...)                                         \
+  do {                                                                          \
+    const int npl_ = ((E_) + 63) / 64;                                          \
+    if (npl_ <= 1) hipLaunchKernelGGL((KERNEL<1>), __VA_ARGS__);                \
+    else if (npl_ <= 2) hipLaunchKernelGGL((KERNEL<2>), __VA_ARGS__);           \
+    else if (npl_ <= 4) hipLaunchKernelGGL((KERNEL<4>), __VA_ARGS__);           \
+    else if (npl_ <= 8) hipLaunchKernelGGL((KERNEL<8>), __VA_ARGS__);           \
+    else hipLaunchKernelGGL((KERNEL<kTopkMaxPerLane>), __VA_ARGS__);            \
+  } while (0)
 
 template <bool kBF16>
 __device__ __forceinline__ void load8(const void* base, int64_t off, double* v) {
@@ -179,6 +190,7 @@ __device__ __forceinline__ uint32_t key_order(float f) {
 
 // With a token list (list, cnt): wavefront p < *cnt handles token list[p], whose partials
 // are row p of part.
+template <int NPL>  // experts per lane: E <= 64 NPL
 __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, int S, int T, int E,
                                               int k, int fn, float scale,
                                               const float* __restrict__ bias,
@@ -198,11 +210,11 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
     S = fb_splits(n, cap, H, &kl);
     stride = n;
   }
-  float lg[kTopkMaxPerLane];
-  double sc[kTopkMaxPerLane];
-  uint64_t key[kTopkMaxPerLane];
+  float lg[NPL];
+  double sc[NPL];
+  uint64_t key[NPL];
 #pragma unroll
-  for (int i = 0; i < kTopkMaxPerLane; ++i) {
+  for (int i = 0; i < NPL; ++i) {
     const int e = i * 64 + l;
     lg[i] = 0.0f;
     if (e < E) {
@@ -217,25 +229,25 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
   }
   if (fn == MOE_SIGMOID) {
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) sc[i] = 1.0 / (1.0 + exp(-(double)lg[i]));
+    for (int i = 0; i < NPL; ++i) sc[i] = 1.0 / (1.0 + exp(-(double)lg[i]));
   } else {
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i)
+    for (int i = 0; i < NPL; ++i)
       if (i * 64 + l < E) mx = fmaxf(mx, lg[i]);
     mx = wave_max_f32(mx);
     double sum = 0.0;
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) {
+    for (int i = 0; i < NPL; ++i) {
       sc[i] = (i * 64 + l < E) ? exp((double)lg[i] - (double)mx) : 0.0;
       sum += sc[i];
     }
     sum = wave_sum_f64(sum);
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) sc[i] = sc[i] / sum;
+    for (int i = 0; i < NPL; ++i) sc[i] = sc[i] / sum;
   }
 #pragma unroll
-  for (int i = 0; i < kTopkMaxPerLane; ++i) {
+  for (int i = 0; i < NPL; ++i) {
     const int e = i * 64 + l;
     if (e < E) {
       float kf = (float)sc[i];
@@ -249,12 +261,12 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
   for (int r = 0; r < k; ++r) {
     uint64_t best = 0ull;
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
+    for (int i = 0; i < NPL; ++i) best = key[i] > best ? key[i] : best;
     best = wave_max_u64(best);
     const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
     sel[r] = e;
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i)
+    for (int i = 0; i < NPL; ++i)
       if (i * 64 + l == e) key[i] = 0ull;
   }
   // ascending expert order (k <= 16: insertion sort, identical in every lane)
@@ -269,7 +281,7 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
     const int e = sel[r];
     double v = 0.0;
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i)
+    for (int i = 0; i < NPL; ++i)
       if (i == (e >> 6)) v = sc[i];
     v = __shfl(v, e & 63, 64);
     chosen[r] = v;
@@ -474,6 +486,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+template <int NPL>  // experts per lane: E <= 64 NPL
 __global__ void __launch_bounds__(256, 3) k_topk_fast(
     const double* __restrict__ part, const double* __restrict__ nw2s, int S, int T, int H, int E,
     int k, int fn, float scale,
@@ -495,10 +508,10 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
   }
   const double nx = sqrt(wave_sum_f64(nx2));
   const double tiny = (double)H * 0x1p-126;
-  float lo[kTopkMaxPerLane], hi[kTopkMaxPerLane], mid[kTopkMaxPerLane];
+  float lo[NPL], hi[NPL], mid[NPL];
   bool fin = true;
 #pragma unroll
-  for (int i = 0; i < kTopkMaxPerLane; ++i) {
+  for (int i = 0; i < NPL; ++i) {
     const int e = i * 64 + l;
     lo[i] = hi[i] = mid[i] = 0.0f;
     if (e < E) {
@@ -515,8 +528,8 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
     }
   }
   bool certified = __all(fin);
-  uint32_t klo[kTopkMaxPerLane], khi[kTopkMaxPerLane];
-  uint64_t key[kTopkMaxPerLane];
+  uint32_t klo[NPL], khi[NPL];
+  uint64_t key[NPL];
   if (certified) {
     // The interval keys use fp32 exp, whose results (with the add and the division) are
     // within 2^-20 of the exact values; kWiden moves each bound outward by more than
@@ -534,12 +547,12 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
     if (fn != MOE_SIGMOID) {
       float fh = -INFINITY, fm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kTopkMaxPerLane; ++i)
+      for (int i = 0; i < NPL; ++i)
         if (i * 64 + l < E) { fh = fmaxf(fh, hi[i]); fm = fmaxf(fm, mid[i]); }
       mh = wave_max_f32(fh);
       mm = wave_max_f32(fm);
 #pragma unroll
-      for (int i = 0; i < kTopkMaxPerLane; ++i)
+      for (int i = 0; i < NPL; ++i)
         if (i * 64 + l < E) {
           Alo += fmax(lo_exp(lo[i] - mh), 0.0);
           Ahi += hi_exp(hi[i] - mh);
@@ -550,7 +563,7 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
       Am = wave_sum_f64(Am);
     }
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) {
+    for (int i = 0; i < NPL; ++i) {
       const int e = i * 64 + l;
       klo[i] = khi[i] = 0u;
       key[i] = 0ull;
@@ -582,17 +595,17 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
     for (int r = 0; r < k; ++r) {
       uint64_t best = 0ull;
 #pragma unroll
-      for (int i = 0; i < kTopkMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
+      for (int i = 0; i < NPL; ++i) best = key[i] > best ? key[i] : best;
       best = wave_max_u64(best);
       const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
       sel[r] = e;
 #pragma unroll
-      for (int i = 0; i < kTopkMaxPerLane; ++i)
+      for (int i = 0; i < NPL; ++i)
         if (i * 64 + l == e) { key[i] = 0ull; chosen |= 1u << i; }
     }
     uint32_t min_in = 0xFFFFFFFFu, max_out = 0u;
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) {
+    for (int i = 0; i < NPL; ++i) {
       if (i * 64 + l >= E) continue;
       if (chosen >> i & 1u) min_in = klo[i] < min_in ? klo[i] : min_in;
       else max_out = khi[i] > max_out ? khi[i] : max_out;
@@ -730,7 +743,7 @@ hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const flo
     hipLaunchKernelGGL(k_router_lds, dim3(nblk), dim3(64 * kRtWgt * kRtWge), 0, s, xb, wb, T, H, E,
                        flen, ntt, net, SF, part, cnt);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_topk_fast, dim3((T + 3) / 4), dim3(256), 0, s, part, nw2, SF, T, H, E, k,
+    MOE_TOPK_LAUNCH(k_topk_fast, E, dim3((T + 3) / 4), dim3(256), 0, s, part, nw2, SF, T, H, E, k,
                        (int)fn, scale, bias, xb, wb, topk_idx, topk_w, list, cnt);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // the listed tokens, exactly: the grid covers T tokens, wavefronts past the count exit
@@ -740,7 +753,7 @@ hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const flo
     hipLaunchKernelGGL((k_router_gemm<true, 1, 1>), gx, dim3(64), 0, s, x, wr, T, H, E, klen, part,
                        list, cnt, cap);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, part, S, T, E, k, (int)fn, scale,
+    MOE_TOPK_LAUNCH(k_topk, E, dim3((T + 3) / 4), dim3(256), 0, s, part, S, T, E, k, (int)fn, scale,
                        bias, topk_idx, topk_w, nullptr, list, cnt, H, cap);
     return hipGetLastError();
   }
@@ -761,7 +774,7 @@ hipError_t launch_route(const void* x, moe_dtype x_dt, const void* wr, const flo
                        nullptr, nullptr, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, part, S, T, E, k, (int)fn, scale,
+  MOE_TOPK_LAUNCH(k_topk, E, dim3((T + 3) / 4), dim3(256), 0, s, part, S, T, E, k, (int)fn, scale,
                      bias, topk_idx, topk_w, logits, nullptr, nullptr, H, 0);
   return hipGetLastError();
 }
