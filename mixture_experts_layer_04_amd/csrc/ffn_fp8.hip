@@ -49,14 +49,17 @@ __device__ __forceinline__ float wave_max16(float v) {  // max over lanes with e
   return v;
 }
 
-// Quantise rows of a bf16 [n, H] matrix: one workgroup per row, 16 lanes per 1 x 128 block.
+// Quantise rows of a bf16 [n, H] matrix: one workgroup per (row, 16 blocks of 1 x 128), 16
+// lanes per block (a workgroup per 2048 elements, so that every row's loads are in flight
+// at once).
 __global__ void __launch_bounds__(256) k_quant_rows_fp8(const uint16_t* __restrict__ x, int H,
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ qs) {
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   const int nblk = H / 128;
-  for (int b0 = 0; b0 < nblk; b0 += 16) {
+  {
+    const int b0 = blockIdx.y * 16;
     const int b = b0 + (t >> 4);
     const int j = t & 15;
     float v[8];
@@ -300,7 +303,7 @@ hipError_t launch_ffn_fp8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event)
 hipError_t launch_quant_rows_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* qs,
                                  hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quant_rows_fp8, dim3(n), dim3(256), 0, s,
+  hipLaunchKernelGGL(k_quant_rows_fp8, dim3(n, (H / 128 + 15) / 16), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t*>(x), H, q, qs);
   return hipGetLastError();
 }
