@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(256) k_down_stream_lds(FfnArgs a, int fb_per_t
 #define MOE_STREAM_MX_LDS 1
 #endif
 #ifndef MOE_STREAM_MX_ROWS_GU
-#define MOE_STREAM_MX_ROWS_GU 2
+#define MOE_STREAM_MX_ROWS_GU 1
 #endif
 #ifndef MOE_STREAM_MX_ROWS_DN
 #define MOE_STREAM_MX_ROWS_DN 4
