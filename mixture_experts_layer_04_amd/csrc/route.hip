@@ -454,6 +454,7 @@ __global__ void __launch_bounds__(256) k_row_norms2(const uint16_t* __restrict__
   if (row >= n) return;
   const uint16_t* p = w + (int64_t)row * H;
   double v = 0.0;
+#pragma unroll 8  // the loads of eight chunks in flight together; the sum keeps its order
   for (int h = 8 * l; h < H; h += 512) {
     const uint4 q = *reinterpret_cast<const uint4*>(p + h);
     const double v0 = bf16_lo(q.x), v1 = bf16_hi(q.x), v2 = bf16_lo(q.y), v3 = bf16_hi(q.y);
