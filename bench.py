@@ -28,6 +28,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE layer tokens/s + grouped-GEMM % of HBM/MFMA peak, 256e top-8 H=7168 bf16"
+# a decode workload and the prefill-sized batch of the same layer, timed after it
+PREFILL_OF = {"r1_decode": "r1_prefill"}
 
 
 def parse():
@@ -37,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="r1_decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill-sized batch timed after a decode workload")
     ap.add_argument("--overlap", action="store_true",
                     help="also time the step with the shared expert on a side stream")
     ap.add_argument("--cpu-tokens", type=int, default=72,
@@ -179,35 +183,31 @@ def measured_traffic(workload: str):
     return rec["traffic_bytes"]
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(multi-GPU expert parallelism is not built)", file=sys.stderr)
-        sys.exit(2)
+def percentile(v, q):
+    import numpy as np
+
+    return float(np.percentile(np.asarray(v, np.float64), q))
+
+
+def run_workload(cfg, dev, args, overlap=False):
+    """Times one workload: K plain steps between two events (ms/step), then K steps of the
+    same launches with the library's stage events (per-stage means, and the median and
+    p10/p90 of the per-step times). Returns a dict of the measurements."""
     import numpy as np
     import torch
 
     import mixture_experts_layer_04_amd as moe
-    from synth.configs import CONFIGS
-    from synth.problem import device_problem, host_problem
 
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from moe_cases import experts, make_layer
-
-    cfg = CONFIGS[args.workload]
-    log(f"workload {cfg.name}: generating inputs on the device")
-    host = host_problem(cfg)
-    dev = device_problem(cfg, host=host)
-    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    T, H, E = cfg.T, cfg.H, cfg.E
     odt = torch.float32 if cfg.out == "f32" else torch.bfloat16
     out = torch.empty((T, H), dtype=odt, device="cuda")
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     ev = moe.StageEvents()
     stream = torch.cuda.current_stream()
+    layer = None
     if cfg.routed:
         # a step: the whole layer (route, permute, grouped FFN incl. shared expert, combine)
-        layer = make_layer(cfg, dev)
+        layer = moe.MoELayer.from_problem(cfg, dev)
 
         def step():
             layer.forward(dev.x, out, counts=counts)
@@ -216,7 +216,7 @@ def main():
             moe.moe_layer_forward_timed(layer.desc, dev.x, out, layer.ws, ev, counts=counts)
     else:
         # pre-routed rows (one GPU's expert-parallel share): permute, grouped FFN, combine
-        bank = experts(dev.routed)
+        bank = moe.Experts.from_bank(dev.routed)
         ws = moe.workspace(moe.moe_rows_workspace_size(bank, moe.DTYPES[cfg.act], T))
         row_e, row_w = dev.topk_idx.view(-1), dev.topk_w.view(-1)
         counts.copy_(torch.bincount(row_e.long(), minlength=E).int())
@@ -230,7 +230,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
+    log(f"{cfg.name}: warmup done ({args.warmup} steps)")
 
     # timed region: K plain steps
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -241,21 +241,24 @@ def main():
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
-    log(f"timed {args.steps} steps: {ms:.4f} ms/step")
+    log(f"{cfg.name}: timed {args.steps} steps: {ms:.4f} ms/step")
 
     # per-stage times of the same launches, from events the library records on its stream
-    stage = {s: [] for s in moe.STAGES}
+    stage = {s_: [] for s_ in moe.STAGES}
+    per_step = []
     for _ in range(args.steps):
         timed_step()
         torch.cuda.synchronize()
-        for s_, v in ev.elapsed_ms().items():
+        st = ev.elapsed_ms()
+        for s_, v in st.items():
             stage[s_].append(v)
+        per_step.append(sum(st.values()))
     stage_ms = {s_: float(np.mean(v)) for s_, v in stage.items()}
-    log("stage ms: " + ", ".join(f"{s_}={v:.4f}" for s_, v in stage_ms.items()))
+    log(f"{cfg.name}: stage ms: " + ", ".join(f"{s_}={v:.4f}" for s_, v in stage_ms.items()))
 
     # the same step with the shared expert on a side stream beside the routed experts
     ovl_ms = None
-    if args.overlap and cfg.routed and cfg.shared_I:
+    if overlap and cfg.routed and cfg.shared_I:
         fj = moe.ForkJoin()
         for _ in range(args.warmup):
             layer.forward_overlap(dev.x, out, fj, counts=counts)
@@ -266,30 +269,7 @@ def main():
         stop.record(stream)
         torch.cuda.synchronize()
         ovl_ms = start.elapsed_time(stop) / args.steps
-        log(f"overlapped shared expert: {ovl_ms:.4f} ms/step")
-
-    # the selection-bias balancing step (not part of the forward step): its own timing
-    bias_us = None
-    if cfg.routed and cfg.use_bias:
-        b = dev.bias.clone()
-        reps = 200
-        start.record(stream)
-        for _ in range(reps):
-            moe.moe_bias_update(counts, 1e-3, b)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        bias_us = start.elapsed_time(stop) / reps * 1e3
-        log(f"bias update: {bias_us:.2f} us per call")
-
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"copy probe: 3 x {args.copy_probe_mib} MiB device copies")
+        log(f"{cfg.name}: overlapped shared expert: {ovl_ms:.4f} ms/step")
 
     cnt = counts.cpu().numpy()
     touched = int((cnt > 0).sum())
@@ -302,12 +282,102 @@ def main():
         achieved, peak, unit = g["flops"] / gu_s / 1e12, g["mfma_peak"], "TFLOP/s"
     layer_bytes = acct["gate_up"]["bytes"] + acct["down"]["bytes"] + acct["other_bytes"]
     layer_flops = acct["gate_up"]["flops"] + acct["down"]["flops"] + acct["router_flops"]
+    ffn_s = (stage_ms["gate_up"] + stage_ms["down"]) / 1e3
+    ffn_flops = acct["gate_up"]["flops"] + acct["down"]["flops"]
+    return {
+        "ms": ms, "stage_ms": stage_ms, "touched": touched, "counts": counts,
+        "step_ms_p10_p50_p90": [percentile(per_step, q) for q in (10, 50, 90)],
+        "ovl_ms": ovl_ms,
+        "layer_bytes": layer_bytes, "layer_flops": layer_flops,
+        "down_frac": acct["down"]["frac_fn"](stage_ms["down"] / 1e3),
+        "ffn_tflops": ffn_flops / ffn_s / 1e12,
+        "ffn_mfma_frac": ffn_flops / ffn_s / 1e12 / acct["gate_up"]["mfma_peak"],
+        "roofline": {"bound": g["bound"], "kernel": f"grouped gate/up + SwiGLU ({g['kernel']})",
+                     "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+                     "traffic": measured_traffic(cfg.name),
+                     "algorithmic_bytes_per_launch": g["bytes"],
+                     "algorithmic_flops_per_launch": g["flops"],
+                     "avg_launch_ms": stage_ms["gate_up"]},
+    }
+
+
+def describe(cfg):
+    return (f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} top-{cfg.k} I={cfg.I} {cfg.score}"
+            f"{' + selection bias' if cfg.use_bias else ''} scale {cfg.scale}"
+            f"{', Zipf-skewed router' if cfg.zipf_s else ''}, "
+            f"{'1 shared expert, ' if cfg.shared_I else ''}{cfg.wdt}")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU expert parallelism is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_layer_04_amd as moe
+    from synth.configs import CONFIGS
+    from synth.problem import device_problem, host_problem
+
+    cfg = CONFIGS[args.workload]
+    log(f"workload {cfg.name}: generating inputs on the device")
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
+    T = cfg.T
+    r = run_workload(cfg, dev, args, overlap=args.overlap)
+
+    # the selection-bias balancing step (not part of the forward step): its own timing
+    bias_us = None
+    if cfg.routed and cfg.use_bias:
+        stream = torch.cuda.current_stream()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b = dev.bias.clone()
+        reps = 200
+        start.record(stream)
+        for _ in range(reps):
+            moe.moe_bias_update(r["counts"], 1e-3, b)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        bias_us = start.elapsed_time(stop) / reps * 1e3
+        log(f"bias update: {bias_us:.2f} us per call")
+
+    # the prefill-sized batch of the same layer (same expert banks, 64x the tokens, a skewed
+    # router): the MFMA-bound half of the metric, measured in the same process
+    prefill = None
+    pname = PREFILL_OF.get(cfg.name)
+    if pname and not args.no_prefill:
+        pcfg = CONFIGS[pname]
+        log(f"workload {pcfg.name}: generating activations and router on the device "
+            f"(expert banks shared with {cfg.name})")
+        pdev = device_problem(pcfg, banks_of=dev)
+        p = run_workload(pcfg, pdev, args)
+        prefill = {"workload": describe(pcfg), "tokens": pcfg.T, "ms_per_step": p["ms"],
+                   "tokens_per_s": pcfg.T / (p["ms"] / 1e3), "experts_touched": p["touched"],
+                   "stage_ms": {s_: round(v, 5) for s_, v in p["stage_ms"].items()},
+                   "step_ms_p10_p50_p90": p["step_ms_p10_p50_p90"],
+                   "grouped_ffn_tflops": p["ffn_tflops"],
+                   "grouped_ffn_mfma_frac": p["ffn_mfma_frac"],
+                   "down_frac": p["down_frac"],
+                   "roofline": p["roofline"]}
+        del pdev
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: 3 x {args.copy_probe_mib} MiB device copies")
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, host, args.cpu_tokens)
         log(f"cpu baseline: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
 
+    ms = r["ms"]
     line = {
         "metric": METRIC,
         "value": T / (ms / 1e3),
@@ -321,22 +391,17 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.wdt,
         "data": "synthetic (seeded Philox inputs; N(0,1) activations, N(0,0.02) weights)",
-        "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} top-{k} I={cfg.I} {cfg.score}"
-                               f"{' + selection bias' if cfg.use_bias else ''} scale {cfg.scale}, "
-                               f"{'1 shared expert, ' if cfg.shared_I else ''}{cfg.wdt}",
-                   "tokens": T, "experts_touched": touched,
-                   "stage_ms": {s_: round(v, 5) for s_, v in stage_ms.items()},
-                   "layer_algorithmic_bytes": layer_bytes, "layer_flops": layer_flops,
-                   "layer_hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                   "down_frac": acct["down"]["frac_fn"](stage_ms["down"] / 1e3),
+        "config": {"workload": describe(cfg),
+                   "tokens": T, "experts_touched": r["touched"],
+                   "stage_ms": {s_: round(v, 5) for s_, v in r["stage_ms"].items()},
+                   "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
+                   "layer_algorithmic_bytes": r["layer_bytes"], "layer_flops": r["layer_flops"],
+                   "layer_hbm_frac": r["layer_bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                   "down_frac": r["down_frac"],
                    "bias_update_us": bias_us,
-                   "ms_per_step_shared_overlapped": ovl_ms},
-        "roofline": {"bound": g["bound"], "kernel": f"grouped gate/up + SwiGLU ({g['kernel']})",
-                     "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-                     "traffic": measured_traffic(cfg.name),
-                     "algorithmic_bytes_per_launch": g["bytes"],
-                     "algorithmic_flops_per_launch": g["flops"],
-                     "avg_launch_ms": stage_ms["gate_up"]},
+                   "ms_per_step_shared_overlapped": r["ovl_ms"],
+                   "prefill": prefill},
+        "roofline": r["roofline"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -152,6 +152,13 @@ class Experts:
     w13_scale: Optional[torch.Tensor] = None
     w2_scale: Optional[torch.Tensor] = None
 
+    @classmethod
+    def from_bank(cls, bank) -> "Experts":
+        """From any object with the same fields (fmt, E, H, I, w13, w2, w13_scale, w2_scale),
+        e.g. a bank of the seeded workload generator."""
+        return cls(bank.fmt, bank.E, bank.H, bank.I, bank.w13, bank.w2, bank.w13_scale,
+                   bank.w2_scale)
+
     def c(self) -> moe_experts:
         return moe_experts(DTYPES[self.fmt], self.w13.data_ptr(),
                            self.w13_scale.data_ptr() if self.w13_scale is not None else None,
@@ -363,6 +370,14 @@ class MoELayer:
         self.desc = layer_desc(T, wr, bias, routed, shared, k, score, route_scale, DTYPES[act],
                                DTYPES[out])
         self.ws = workspace(moe_layer_workspace_size(self.desc), device)
+
+    @classmethod
+    def from_problem(cls, cfg, dev, device="cuda") -> "MoELayer":
+        """From a workload description (T, k, score, scale, act, out) and its device tensors
+        (wr, bias, routed and shared banks), e.g. those of the seeded workload generator."""
+        shared = Experts.from_bank(dev.shared) if dev.shared is not None else None
+        return cls(cfg.T, dev.wr, dev.bias, Experts.from_bank(dev.routed), shared, cfg.k,
+                   cfg.score, cfg.scale, cfg.act, cfg.out, device)
 
     def forward(self, x, out, topk_idx=None, topk_w=None, counts=None, logits=None, stream=None):
         moe_layer_forward(self.desc, x, out, self.ws, topk_idx, topk_w, counts, logits, stream)

@@ -86,7 +86,8 @@ __global__ void __launch_bounds__(256) k_quant_rows_fp8(const uint16_t* __restri
   }
 }
 
-template <bool kGateUp>
+// kYF32 (down only): expert outputs stored as fp32, else rounded once to bf16.
+template <bool kGateUp, bool kYF32>
 __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   // Each K block of the workgroup's operands -- its 128 (down) or 256 (gate/up) weight
   // rows, the tile's 128 activation rows (both in the full-rate layout of lds_off) and the
@@ -282,8 +283,15 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
       const int tok = t * 16 + m16;
       if (tok >= tl.nrows) continue;
       const int64_t o = (int64_t)(tl.row0 + tok) * H + fw + 4 * g;
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + o) =
-          make_float4(acc0[t][0], acc0[t][1], acc0[t][2], acc0[t][3]);
+      if (kYF32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + o) =
+            make_float4(acc0[t][0], acc0[t][1], acc0[t][2], acc0[t][3]);
+      } else {
+        uint2 b;
+        b.x = (uint32_t)f32_to_bf16(acc0[t][0]) | ((uint32_t)f32_to_bf16(acc0[t][1]) << 16);
+        b.y = (uint32_t)f32_to_bf16(acc0[t][2]) | ((uint32_t)f32_to_bf16(acc0[t][3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + o) = b;
+      }
     }
   }
 }
@@ -292,11 +300,14 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
 
 hipError_t launch_ffn_fp8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
   const int nb_gu = a.I_max / kF8Feat, nb_dn = a.H / kF8Feat;
-  hipLaunchKernelGGL(k_fp8<true>, dim3(a.max_tiles * nb_gu), dim3(512), 0, s, a, nb_gu);
+  hipLaunchKernelGGL((k_fp8<true, true>), dim3(a.max_tiles * nb_gu), dim3(512), 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_fp8<false>, dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
+  if (a.y_dt == MOE_F32)
+    hipLaunchKernelGGL((k_fp8<false, true>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
+  else
+    hipLaunchKernelGGL((k_fp8<false, false>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
   return hipGetLastError();
 }
 

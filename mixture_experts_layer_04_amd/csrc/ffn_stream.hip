@@ -86,6 +86,12 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
 #ifndef MOE_STREAM_KSPLIT_DN  // the same for down
 #define MOE_STREAM_KSPLIT_DN 2
 #endif
+// A wavefront's 16 R output features start at a multiple of 16 R, and ffn_shape_ok admits
+// bf16 / fp32 banks with H and I multiples of 64: so 16 R must divide 64, or the last
+// wavefront of an expert would read weight rows of the next expert (past the last one's
+// end) and write h or y past the row's end.
+static_assert(64 % (16 * MOE_STREAM_ROWS_GU) == 0, "gate/up row groups must tile I % 64");
+static_assert(64 % (16 * MOE_STREAM_ROWS_DN) == 0, "down row groups must tile H % 64");
 // Weight fragment: ordinary cached loads (on MI355X they measured faster than
 // non-temporal ones for this many-rows-at-once pattern).
 __device__ __forceinline__ Frag32 load_w(const void* p) { return load_c(p); }

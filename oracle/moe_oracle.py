@@ -49,10 +49,10 @@ def f32_to_f64(a: np.ndarray) -> np.ndarray:
     return np.asarray(a, np.float32).astype(np.float64)
 
 
-def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+def _e4m3_values(c: np.ndarray) -> np.ndarray:
     """OCP 8-bit floating point E4M3 (the 'FN' variant: bias 7, no infinities,
     S.1111.111 is NaN). Normal: (1 + m/8) * 2^(e-7); subnormal (e = 0): m/8 * 2^-6."""
-    c = np.asarray(codes, np.uint8).astype(np.int64)
+    c = np.asarray(c, np.int64)
     s = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = (c & 0x7).astype(np.float64)
@@ -61,14 +61,31 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & ((c & 7) == 7), np.nan, out)
 
 
-def e2m1_to_f64(nibbles: np.ndarray) -> np.ndarray:
+# the value of every E4M3 code, from the definition above: decoding is a table look-up
+_E4M3_VALUES = _e4m3_values(np.arange(256))
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """E4M3FN codes -> float64 values (see _e4m3_values)."""
+    return _E4M3_VALUES[np.asarray(codes, np.uint8)]
+
+
+def _e2m1_values(n: np.ndarray) -> np.ndarray:
     """OCP MX E2M1 element (bias 1): normal (1 + m/2) * 2^(e-1); subnormal m * 0.5."""
-    n = np.asarray(nibbles, np.uint8).astype(np.int64) & 0xF
+    n = np.asarray(n, np.int64) & 0xF
     s = np.where(n & 0x8, -1.0, 1.0)
     e = (n >> 1) & 0x3
     m = (n & 0x1).astype(np.float64)
     mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1))
     return s * mag
+
+
+_E2M1_VALUES = _e2m1_values(np.arange(16))
+
+
+def e2m1_to_f64(nibbles: np.ndarray) -> np.ndarray:
+    """E2M1 nibbles (the low 4 bits of each byte) -> float64 values (see _e2m1_values)."""
+    return _E2M1_VALUES[np.asarray(nibbles, np.uint8) & 0xF]
 
 
 def e8m0_to_f64(codes: np.ndarray) -> np.ndarray:
@@ -177,8 +194,9 @@ def decode_matrix(fmt: str, part: dict) -> np.ndarray:
         return bf16_to_f64(w)
     if fmt == "fp8":
         s = np.asarray(part["scale"], np.float32).astype(np.float64)
-        full = np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
-        return e4m3_to_f64(w) * full
+        R, C = w.shape
+        v = e4m3_to_f64(w).reshape(R // 128, 128, C // 128, 128)
+        return (v * s[:, None, :, None]).reshape(R, C)
     if fmt in ("mxfp4", "mxfp4a4"):
         p = np.asarray(w, np.uint8)
         R = p.shape[0]
@@ -186,8 +204,8 @@ def decode_matrix(fmt: str, part: dict) -> np.ndarray:
         el = np.empty((R, C), np.uint8)
         el[:, 0::2] = p & 0xF
         el[:, 1::2] = p >> 4
-        sc = np.repeat(e8m0_to_f64(part["scale"]), 32, axis=1)
-        return e2m1_to_f64(el) * sc
+        sc = e8m0_to_f64(part["scale"])
+        return (e2m1_to_f64(el).reshape(R, C // 32, 32) * sc[:, :, None]).reshape(R, C)
     raise ValueError(fmt)
 
 
@@ -341,7 +359,7 @@ def expert_weights(bank, e: int):
 
 # ----------------------------------------------------------------------------- layer
 
-def layer_forward(prob, tokens=None, with_routing: bool = True):
+def layer_forward(prob, tokens=None, with_routing: bool = True, workers: int = 1):
     """The whole layer on the host for the listed tokens (default: all).
 
     Routing, counts and the permutation always cover all T tokens (they are global);
@@ -349,6 +367,8 @@ def layer_forward(prob, tokens=None, with_routing: bool = True):
     a sample of a large layer only decodes the experts that sample touches.
     out[t] = sum_j w[t,j] * FFN_{e_j}(x_t) + FFN_shared(x_t); pre-routed rows
     (no router) give out[r] = w_r * FFN_{e_r}(x_r).
+    workers > 1 decodes and evaluates that many experts at once on threads; their
+    contributions are still added in ascending expert order, so the result is the same.
     """
     cfg = prob.cfg
     T = cfg.T
@@ -381,12 +401,24 @@ def layer_forward(prob, tokens=None, with_routing: bool = True):
     out = np.zeros((len(tokens), cfg.H), np.float64)
     sel = topk_idx[tokens]
     wsel = topk_w[tokens]
-    for e in np.unique(sel):
+
+    def contribution(e):
         rows, slots = np.nonzero(sel == e)
         w13, w2 = expert_weights(prob.routed, int(e))
-        y = expert_ffn(a[rows], w13, w2, requant_h=requant)
-        out[rows] += wsel[rows, slots][:, None] * y
-        del w13, w2
+        return rows, wsel[rows, slots][:, None] * expert_ffn(a[rows], w13, w2, requant_h=requant)
+
+    experts = np.unique(sel)
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        with ThreadPoolExecutor(workers) as pool:
+            parts = pool.map(contribution, experts)   # yields in ascending expert order
+            for rows, y in parts:
+                out[rows] += y
+    else:
+        for e in experts:
+            rows, y = contribution(e)
+            out[rows] += y
     if prob.shared is not None:
         w13, w2 = expert_weights(prob.shared, 0)
         out += expert_ffn(a, w13, w2, requant_h=requant)

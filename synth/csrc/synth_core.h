@@ -100,6 +100,15 @@ SYN_FN float syn_normal(uint64_t seed, uint32_t tid, uint64_t i, float std, cons
   return z * std;
 }
 
+/* Elements 4b .. 4b+3 of N(0, std^2): the four words of one Philox block, each turned into
+ * a value exactly as syn_normal does (the same values, a quarter of the Philox work). */
+SYN_FN void syn_normal4(uint64_t seed, uint32_t tid, uint64_t b, float std, const float* q,
+                        float out[4]) {
+  syn_u32x4 r = syn_philox4x32_10((uint32_t)b, (uint32_t)(b >> 32), tid, 0u, (uint32_t)seed,
+                                  (uint32_t)(seed >> 32));
+  for (int j = 0; j < 4; ++j) out[j] = syn_std_normal(r.v[j], q) * std;
+}
+
 /* U(lo, hi): 24 random bits give an exact fp32 in [0,1); then lo + (hi-lo)*f,
  * with span = hi - lo precomputed by the caller in fp32. */
 SYN_FN float syn_uniform(uint64_t seed, uint32_t tid, uint64_t i, float lo, float span) {

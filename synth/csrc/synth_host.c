@@ -41,12 +41,15 @@ static void run_fp8_block(const syn_job* j, uint64_t blk) {
   float vals[128 * 128];
   float amax = 0.0f;
   for (int r = 0; r < 128; ++r) {
+    /* cols is a multiple of 128, so base is a multiple of 4: whole Philox blocks */
     uint64_t base = (uint64_t)((ge * j->rows + rb * 128 + r) * j->cols + cb * 128);
-    for (int c = 0; c < 128; ++c) {
-      float v = syn_normal(j->seed, j->tid, base + (uint64_t)c, j->a, j->q);
-      vals[r * 128 + c] = v;
-      float av = v < 0.0f ? -v : v;
-      if (av > amax) amax = av;
+    for (int c = 0; c < 128; c += 4) {
+      syn_normal4(j->seed, j->tid, (base + (uint64_t)c) >> 2, j->a, j->q, &vals[r * 128 + c]);
+      for (int i = 0; i < 4; ++i) {
+        float v = vals[r * 128 + c + i];
+        float av = v < 0.0f ? -v : v;
+        if (av > amax) amax = av;
+      }
     }
   }
   float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
@@ -67,10 +70,10 @@ static void run_mxfp4_block(const syn_job* j, uint64_t blk) {
   uint64_t base = (uint64_t)(((j->e0 + e) * j->rows + r) * j->cols + cb * 32);
   float vals[32];
   float amax = 0.0f;
+  /* cols is a multiple of 32, so base is a multiple of 4: whole Philox blocks */
+  for (int c = 0; c < 32; c += 4) syn_normal4(j->seed, j->tid, (base + (uint64_t)c) >> 2, j->a, j->q, &vals[c]);
   for (int c = 0; c < 32; ++c) {
-    float v = syn_normal(j->seed, j->tid, base + (uint64_t)c, j->a, j->q);
-    vals[c] = v;
-    float av = v < 0.0f ? -v : v;
+    float av = vals[c] < 0.0f ? -vals[c] : vals[c];
     if (av > amax) amax = av;
   }
   uint8_t sc = syn_mx_scale_code(amax);
@@ -84,8 +87,33 @@ static void run_mxfp4_block(const syn_job* j, uint64_t blk) {
   ((uint8_t*)j->out2)[blk] = sc;
 }
 
+/* Normal fills: elements start+i for i in [lo, hi), whole Philox blocks where the element
+ * index is a multiple of 4 and single elements at the ragged ends. */
+static void run_normal(const syn_job* j, int bf16) {
+  uint64_t i = j->lo;
+  float v4[4];
+  for (; i < j->hi && ((j->start + i) & 3u); ++i) {
+    float v = syn_normal(j->seed, j->tid, j->start + i, j->a, j->q);
+    if (bf16) ((uint16_t*)j->out)[i] = syn_bf16_rne(v); else ((float*)j->out)[i] = v;
+  }
+  for (; i + 4 <= j->hi; i += 4) {
+    syn_normal4(j->seed, j->tid, (j->start + i) >> 2, j->a, j->q, v4);
+    for (int t = 0; t < 4; ++t) {
+      if (bf16) ((uint16_t*)j->out)[i + t] = syn_bf16_rne(v4[t]); else ((float*)j->out)[i + t] = v4[t];
+    }
+  }
+  for (; i < j->hi; ++i) {
+    float v = syn_normal(j->seed, j->tid, j->start + i, j->a, j->q);
+    if (bf16) ((uint16_t*)j->out)[i] = syn_bf16_rne(v); else ((float*)j->out)[i] = v;
+  }
+}
+
 static void* worker(void* arg) {
   const syn_job* j = (const syn_job*)arg;
+  if (j->kind == K_NORMAL_F32 || j->kind == K_NORMAL_BF16) {
+    run_normal(j, j->kind == K_NORMAL_BF16);
+    return NULL;
+  }
   for (uint64_t i = j->lo; i < j->hi; ++i) {
     switch (j->kind) {
       case K_WORDS:

@@ -177,14 +177,25 @@ def _to_dev(a: np.ndarray, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def device_problem(cfg: MoEConfig, device="cuda", host: Optional[HostProblem] = None) -> DevProblem:
+def device_problem(cfg: MoEConfig, device="cuda", host: Optional[HostProblem] = None,
+                   banks_of: Optional[DevProblem] = None) -> DevProblem:
     """Inputs in HBM. Large tensors are filled on the device; small ones are uploaded
-    from the host generator (same bytes either way)."""
+    from the host generator (same bytes either way). banks_of: a device problem whose
+    expert banks are the same bytes (same weight seed, format and shapes), reused instead
+    of generated again."""
     from . import dev_normal
 
     x = dev_normal(cfg.seed, TID_X, (cfg.T, cfg.H), cfg.x_std, cfg.act, device)
-    routed = _dev_bank(cfg, cfg.E, cfg.I, TID_W13, TID_W2, device)
-    shared = _dev_bank(cfg, 1, cfg.shared_I, TID_WS13, TID_WS2, device) if cfg.shared_I else None
+    if banks_of is not None:
+        o = banks_of.cfg
+        same = (o.weight_seed, o.wdt, o.E, o.H, o.I, o.shared_I, o.w_std) == \
+               (cfg.weight_seed, cfg.wdt, cfg.E, cfg.H, cfg.I, cfg.shared_I, cfg.w_std)
+        if not same:
+            raise ValueError(f"{o.name} and {cfg.name} do not share their expert banks")
+        routed, shared = banks_of.routed, banks_of.shared
+    else:
+        routed = _dev_bank(cfg, cfg.E, cfg.I, TID_W13, TID_W2, device)
+        shared = _dev_bank(cfg, 1, cfg.shared_I, TID_WS13, TID_WS2, device) if cfg.shared_I else None
     if not cfg.routed:
         idx, w = preroute(cfg) if host is None else (host.topk_idx, host.topk_w)
         return DevProblem(cfg, x, None, None, routed, shared, _to_dev(idx, device),

@@ -1,15 +1,16 @@
 """moe_layer_forward_overlap (shared expert on a side stream, forked and joined by events)
-against moe_layer_forward: the same kernels on the same rows, so every output is bit-identical;
-and the pair of streams captured into a HIP graph and replayed."""
+against the oracle, and against moe_layer_forward: the same kernels on the same rows, so every
+output is bit-identical; and the pair of streams captured into a HIP graph and replayed."""
 import numpy as np
 import pytest
 import torch
 
 import mixture_experts_layer_04_amd as moe
+import oracle as O
 from synth.configs import CONFIGS, MoEConfig
 from synth.problem import device_problem, host_problem
 
-from moe_cases import describe, make_layer
+from moe_cases import TOL, describe, make_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -54,12 +55,21 @@ def _same(a, b):
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
 def test_overlap_equals_plain_forward(cfg):
     print("case", describe(cfg), flush=True)
-    dev = device_problem(cfg, host=host_problem(cfg))
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
     layer = make_layer(cfg, dev)
     fj = moe.ForkJoin()
     plain = _outputs(cfg, layer, dev)
     for _ in range(2):  # twice: the second call reuses the workspace and the events
-        _same(_outputs(cfg, layer, dev, fj), plain)
+        ovl = _outputs(cfg, layer, dev, fj)
+        _same(ovl, plain)
+    # and against the oracle: routing bit-exact, output within the format's tolerance
+    want = O.layer_forward(host)
+    assert np.array_equal(ovl[1].numpy(), want["topk_idx"])
+    assert np.array_equal(ovl[3].numpy(), want["counts"])
+    err = O.rel_err(ovl[0].float().numpy().astype(np.float64), want["out"])
+    print(cfg.name, "overlap rel err", err, flush=True)
+    assert err <= TOL[cfg.wdt]
 
 
 def test_overlap_equals_plain_forward_r1_decode():

@@ -1,0 +1,112 @@
+"""More parity of the HIP library against the oracle, through the C ABI:
+
+  * moe_permute at the full sizes of the routed and pre-routed workloads (r1_prefill,
+    e384_fp8, ep32_mxfp4), where T * E exceeds one scan chunk: counts, offsets, perm_src
+    and inv_perm bit-exact against oracle.permutation, and every gathered row bit-exact;
+  * moe_grouped_ffn on its own for every expert format and kernel family (streaming,
+    LDS-staged streaming down, 128- and 256-row tiles, fp8, MXFP4 streaming and tiled, W4A4,
+    fp32), each with fp32 and bf16 output rows, row by row against oracle.expert_ffn on the
+    same (quantised) activations.
+The expert ids fed to moe_permute come from the oracle's routing (or the workload's
+pre-routed ids), never from the library.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_04_amd as moe
+import oracle as O
+import synth
+from synth import TID_X
+from synth.configs import CONFIGS, MoEConfig
+from synth.problem import device_problem, host_problem
+
+from moe_cases import TOL, describe
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["r1_prefill", "e384_fp8", "ep32_mxfp4"])
+def test_permute_full_size(name):
+    cfg = CONFIGS[name]
+    print("case", describe(cfg), flush=True)
+    host = host_problem(cfg)
+    if cfg.routed:
+        idx = O.route(O.decode_act(cfg.act, host.x), O.decode_act(cfg.act, host.wr), host.bias,
+                      cfg.k, cfg.score, cfg.scale)["topk_idx"]
+    else:
+        idx = host.topk_idx
+    T, k, E, H = cfg.T, cfg.k, cfg.E, cfg.H
+    assert T * E > 65536  # more than one chunk of the permutation scan
+    counts, offsets, perm_src, inv_perm = O.permutation(idx, E)
+    x = synth.dev_normal(cfg.seed, TID_X, (T, H), cfg.x_std, cfg.act)
+    d_idx = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
+    g_counts = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+    g_offsets = torch.full((E + 1,), -1, dtype=torch.int32, device="cuda")
+    g_src = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
+    g_inv = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
+    x_perm = torch.empty((T * k, H), dtype=x.dtype, device="cuda")
+    moe.moe_permute(d_idx, E, g_counts, g_offsets, g_src, g_inv, x, x_perm)
+    torch.cuda.synchronize()
+    assert np.array_equal(g_counts.cpu().numpy(), counts)
+    assert np.array_equal(g_offsets.cpu().numpy(), offsets)
+    assert np.array_equal(g_src.cpu().numpy(), perm_src)
+    assert np.array_equal(g_inv.cpu().numpy(), inv_perm)
+    want_rows = torch.from_numpy(perm_src.astype(np.int64) // k).cuda()
+    assert torch.equal(x_perm.view(torch.int16), x.view(torch.int16)[want_rows])
+
+
+# (name, weight format, H, I, E, rows): shapes chosen to reach each kernel family
+FFN_CASES = [
+    ("bf16_stream", "bf16", 256, 192, 8, 60),            # <= 32 rows per expert
+    ("bf16_stream_lds_down", "bf16", 320, 512, 5, 37),   # I % 512 == 0: h staged in LDS
+    ("bf16_tiled128", "bf16", 384, 128, 4, 700),         # H % 256 != 0: 128-row tiles
+    ("bf16_tiled256", "bf16", 512, 256, 3, 900),         # 256-row tiles
+    ("f32_stream", "f32", 128, 64, 6, 50),
+    ("fp8", "fp8", 256, 256, 5, 400),
+    ("mxfp4_stream", "mxfp4", 512, 512, 6, 40),          # H, I multiples of 512, few rows
+    ("mxfp4_tiled", "mxfp4", 256, 128, 4, 600),
+    ("w4a4", "mxfp4a4", 256, 128, 4, 500),
+]
+
+
+@pytest.mark.parametrize("y_dt", ["f32", "bf16"])
+@pytest.mark.parametrize("case", FFN_CASES, ids=lambda c: c[0])
+def test_grouped_ffn_alone(case, y_dt):
+    name, wdt, H, I, E, rows = case
+    act = "f32" if wdt == "f32" else "bf16"
+    cfg = MoEConfig(f"ffn_{name}", T=rows, H=H, E=E, k=1, I=I, score="none", act=act, wdt=wdt,
+                    out=y_dt, seed=140 + len(name), weight_seed=140 + len(name),
+                    dirichlet_alpha=0.7)
+    print("case", describe(cfg), flush=True)
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
+    counts = np.bincount(host.topk_idx[:, 0], minlength=E)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    # rows r0..r1 of x_perm belong to expert e: here, x's rows in order
+    x64 = O.decode_act(act, host.x)
+    if wdt == "fp8":
+        a = O.quantise_rows_e4m3(x64.astype(np.float32))[2]
+    elif wdt == "mxfp4a4":
+        a = O.quantise_rows_mxfp4(x64.astype(np.float32))[2]
+    else:
+        a = x64
+    requant = {"fp8": True, "mxfp4a4": "mxfp4"}.get(wdt, False)
+    want = np.zeros((rows, H))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            w13, w2 = O.expert_weights(host.routed, e)
+            want[r0:r1] = O.expert_ffn(a[r0:r1], w13, w2, requant_h=requant)
+    ydt = torch.float32 if y_dt == "f32" else torch.bfloat16
+    y = torch.full((rows + 8, H), float("nan"), dtype=ydt, device="cuda")  # 8 guard rows
+    moe.moe_grouped_ffn(moe.Experts.from_bank(dev.routed), dev.x,
+                        torch.from_numpy(offsets).cuda(), y[:rows])
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    assert np.isnan(got[rows:]).all()                # nothing written past the last row
+    err = O.rel_err(got[:rows], want)
+    tol = TOL[wdt] if not (wdt == "f32" and y_dt == "bf16") else TOL["bf16"]
+    print(name, y_dt, "rel err", err, flush=True)
+    assert err <= tol, (name, y_dt, err)

@@ -83,14 +83,18 @@ def test_w4a4_rows_match_oracle(cfg):
 
 
 def test_ep32_w4a4_full_size():
+    """ep32_w4a4 at its real size: the rows covering every expert and the first and last
+    rows of every expert's last tile against the oracle, all rows finite."""
+    from moe_cases import TILE_ROWS, cover_tokens, oracle_layer, with_device_banks
+
     cfg = CONFIGS["ep32_w4a4"]
     print("case", describe(cfg), flush=True)
     host = host_problem(cfg)
     dev = device_problem(cfg, host=host)
+    rows = cover_tokens(host.topk_idx, cfg.E, TILE_ROWS[cfg.name], False)
+    want = oracle_layer(with_device_banks(host, dev), tokens=rows)   # before the library runs
     got = run_rows(cfg, dev)
-    rows = [0, 8000, 16383]
-    want = O.layer_forward(host, tokens=rows)
     err = O.rel_err(got["out"][rows], want["out"])
-    print("ep32_w4a4 sampled rel err", err, flush=True)
+    print("ep32_w4a4 sampled rel err", len(rows), "rows", err, flush=True)
     assert err <= TOL["mxfp4"]
     assert np.isfinite(got["out"]).all()

@@ -26,6 +26,22 @@ def test_generation_is_slice_consistent():
     assert np.array_equal(a[500:800], b)
 
 
+def test_normal_fill_equals_per_element_words():
+    """The normal fills take all four words of a Philox block at once where they can; at any
+    start and length they equal the per-element definition: word i of the stream, its top
+    16 bits picking a quantile interval and its low 16 bits the point inside it (fp32)."""
+    q = synth.quantile_table()
+    std = np.float32(0.5)
+    for start in range(9):
+        for n in (1, 2, 3, 4, 5, 7, 8, 17, 64):
+            got = synth.normal_f32(7, 3, (n,), 0.5, start=start)
+            w = synth.words(7, 3, start, n)
+            a, b = q[w >> 16], q[(w >> 16) + 1]
+            f = (w & 0xFFFF).astype(np.float32) * np.float32(1.0 / 65536.0)
+            z = a + f * (b - a)
+            assert np.array_equal(got, (z * std).astype(np.float32)), (start, n)
+
+
 def test_normal_statistics():
     v = synth.normal_f32(11, 1, (2_000_000,), 1.0)
     assert abs(v.mean()) < 3e-3 and abs(v.std() - 1.0) < 3e-3
