@@ -74,6 +74,50 @@ __device__ __forceinline__ bf16x8 e2m1x8_bf16(uint32_t w, float scale) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// E2M1 code of v (already divided by the block scale): nearest of 0, .5, 1, 1.5, 2, 3, 4,
+// 6, ties to the even code, larger magnitudes to 6; the sign in bit 3 (also for zero).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                     (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
+// OCP MX shared-scale exponent e of a block from its amax (a non-negative fp32):
+// floor(log2 amax) - 2, 2 being the exponent of E2M1's largest value; 0 for a zero block,
+// clamped below at -127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const int be = (int)(__float_as_uint(amax) >> 23);  // biased exponent (amax >= 0)
+  if (amax == 0.0f) return 0;
+  if (be == 0) return -127;                            // subnormal amax: below 2^-125
+  const int e = be - 127 - 2;
+  return e < -127 ? -127 : e;
+}
+
+__device__ __forceinline__ float exp2i(int e) {  // 2^e for e in [-127, 127], exact
+  return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// ------------------------------------------------ SwiGLU output of bf16 expert banks
+// With bf16 weights, h = SiLU(g) * u goes to the down GEMM as two parts: hi = bf16(h), and
+// the residual lo = h - hi (exact in fp32) coded as MXFP4 -- E2M1 codes, two a byte
+// (element 2i in the low nibble of byte i), and an E8M0 scale per 32 features. The down
+// GEMM multiplies both parts with the same weight fragments. A bf16 h alone is off by up
+// to 2^-9 of each element; with the residual, by at most a quarter of the residual's block
+// scale unit, which keeps heavy-tailed outputs within the bf16 tolerance (a bf16 h alone
+// does not: it adds about a third to the error the bf16 output storage already makes).
+// Scratch layout, per grouped row: hi [I_max] bf16 (the h buffer), lo codes [I_max / 2]
+// bytes, lo scales [lo_sstride(I_max)] bytes (padded so rows start 16-B aligned and every
+// aligned dword of scales lies inside the row).
+__host__ __device__ inline int32_t lo_sstride(int32_t I_max) { return (I_max / 32 + 15) / 16 * 16; }
+
+// bf16 value and MXFP4 residual of h: returns hi's bits, sets *lo = h - hi (exact).
+__device__ __forceinline__ uint16_t split_bf16(float h, float* lo) {
+  const uint16_t b = f32_to_bf16(h);
+  *lo = h - bf16_to_f32(b);
+  return b;
+}
+
 // A compile-time int as a value, so that a generic lambda can be instantiated per count.
 template <int N>
 struct IntC {

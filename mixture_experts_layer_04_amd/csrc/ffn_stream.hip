@@ -105,6 +105,23 @@ __device__ __forceinline__ Frag32 load_x(const void* p, bool valid) {
   return z;
 }
 
+// h's residual for K step k0 (64 elements) of a bf16 down projection: lane group kq's 16
+// elements k0 + 16 kq .. + 15 decoded from their 8 code bytes (lr already offset by 8 kq)
+// and the E8M0 scale of their 32-element block (ls offset by kq / 2); zeros for padding rows.
+__device__ __forceinline__ Frag32 load_lo(const uint8_t* lr, const uint8_t* ls, int k0, bool valid) {
+  Frag32 f;
+  if (!valid) {
+    f.lo = u32x4{0, 0, 0, 0};
+    f.hi = u32x4{0, 0, 0, 0};
+    return f;
+  }
+  const uint2 q = *reinterpret_cast<const uint2*>(lr + k0 / 2);
+  const float sc = e8m0_f32(ls[k0 / 32]);
+  f.lo = __builtin_bit_cast(u32x4, e2m1x8_bf16(q.x, sc));
+  f.hi = __builtin_bit_cast(u32x4, e2m1x8_bf16(q.y, sc));
+  return f;
+}
+
 template <bool kF32>
 __device__ __forceinline__ f32x4 mma(const Frag32& w, const Frag32& x, f32x4 acc) {
   return kF32 ? mma_f32(w, x, acc) : mma_bf16(w, x, acc);
@@ -205,13 +222,52 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
         accu[r] = f32x4{accu[r][0] + u[0], accu[r][1] + u[1], accu[r][2] + u[2], accu[r][3] + u[3]};
       }
   }
-  if (xv) {
+  if (!xv) return;
+  if constexpr (kF32) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       f32x4 hv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) hv[i] = silu_mul(accg[r][i], accu[r][i]);
-      store4<kF32>(a.h, (int64_t)(tl.row0 + m) * a.I_max + f0 + 16 * r + kq * 4, hv);
+      store4<true>(a.h, (int64_t)(tl.row0 + m) * a.I_max + f0 + 16 * r + kq * 4, hv);
+    }
+  } else {
+    // h = hi + lo (ffn_common.h): row groups 2 j and 2 j + 1 make one 32-feature block,
+    // whose 32 values sit in this lane (8) and the lanes of the other kq (same m)
+    static_assert(R % 2 == 0, "32-feature blocks of the residual");
+    const int64_t row = tl.row0 + m;
+#pragma unroll
+    for (int r2 = 0; r2 < R; r2 += 2) {
+      float lo[2][4];
+      float am = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        uint2 p;
+        uint16_t b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b[i] = split_bf16(silu_mul(accg[r2 + d][i], accu[r2 + d][i]), &lo[d][i]);
+          am = fmaxf(am, fabsf(lo[d][i]));
+        }
+        p.x = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+        p.y = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + row * a.I_max + f0 +
+                                  16 * (r2 + d) + kq * 4) = p;
+      }
+      am = fmaxf(am, __shfl_xor(am, 16, 64));
+      am = fmaxf(am, __shfl_xor(am, 32, 64));
+      const int e = mx_exponent(am);
+      const float inv = exp2i(-e);
+      const int fblk = f0 + 16 * r2;  // first feature of the block
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        // features 16 d + 4 kq .. + 3 of the block: bytes 8 d + 2 kq, 8 d + 2 kq + 1
+        const uint32_t c0 = e2m1_code(lo[d][0] * inv), c1 = e2m1_code(lo[d][1] * inv);
+        const uint32_t c2 = e2m1_code(lo[d][2] * inv), c3 = e2m1_code(lo[d][3] * inv);
+        *reinterpret_cast<uint16_t*>(a.h_lo + row * (a.I_max / 2) + fblk / 2 + 8 * d + 2 * kq) =
+            (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+      }
+      if (kq == 0) a.h_lo_s[row * lo_sstride(a.I_max) + fblk / 32] = (uint8_t)(e + 127);
     }
   }
 }
@@ -251,31 +307,45 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
   const char* wr[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) wr[r] = w2 + (int64_t)(f0 + 16 * r + m) * I * esz + lane_off;
-  const char* hr = reinterpret_cast<const char*>(a.h) +
-                   (int64_t)(tl.row0 + (xv ? m : 0)) * a.I_max * esz + lane_off;
+  const int64_t hrow = tl.row0 + (xv ? m : 0);
+  const char* hr = reinterpret_cast<const char*>(a.h) + hrow * a.I_max * esz + lane_off;
+  // bf16: h's residual (ffn_common.h), this lane's 16 elements of each K step: 8 bytes of
+  // codes and the scale of their 32-element block
+  const uint8_t* lr = kF32 ? nullptr : a.h_lo + hrow * (a.I_max / 2) + kq * 8;
+  const uint8_t* ls = kF32 ? nullptr : a.h_lo_s + hrow * lo_sstride(a.I_max) + (kq >> 1);
   f32x4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4{0, 0, 0, 0};
   const int kmain = kend - (kend - kbeg) % (kStep * U);
   for (int k0 = kbeg; k0 < kmain; k0 += kStep * U) {
-    Frag32 fw[U][R], fh[U];
+    Frag32 fw[U][R], fh[U], fl[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t o = (int64_t)(k0 + u * kStep) * esz;
 #pragma unroll
       for (int r = 0; r < R; ++r) fw[u][r] = load_w(wr[r] + o);
       fh[u] = load_x(hr + o, xv);
+      if (!kF32) fl[u] = load_lo(lr, ls, k0 + u * kStep, xv);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = mma<kF32>(fw[u][r], fh[u], acc[r]);
+      for (int r = 0; r < R; ++r) {
+        acc[r] = mma<kF32>(fw[u][r], fh[u], acc[r]);
+        if (!kF32) acc[r] = mma<false>(fw[u][r], fl[u], acc[r]);
+      }
   }
   for (int k0 = kmain; k0 < kend; k0 += kStep) {
     const int64_t o = (int64_t)k0 * esz;
     const Frag32 fh = load_x(hr + o, xv);
+    Frag32 fl;
+    if (!kF32) fl = load_lo(lr, ls, k0, xv);
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = mma<kF32>(load_w(wr[r] + o), fh, acc[r]);
+    for (int r = 0; r < R; ++r) {
+      const Frag32 fw = load_w(wr[r] + o);
+      acc[r] = mma<kF32>(fw, fh, acc[r]);
+      if (!kF32) acc[r] = mma<false>(fw, fl, acc[r]);
+    }
   }
   if constexpr (KS > 1) {
     // the K ranges' partial sums meet in LDS; the first wavefront of each row group adds
@@ -339,14 +409,24 @@ __global__ void __launch_bounds__(256) k_down_stream_lds(FfnArgs a, int fb_per_t
 #pragma unroll
     for (int j = 0; j < 4; ++j) dma16(hsrc[j] + (int64_t)c * kDnLdsK * 2, dst + (4 * wave + j) * 1024);
   };
+  // h's residual (ffn_common.h): this lane's 8 code bytes of each K step and the scales of
+  // the chunk's 16 blocks of 32 elements, loaded from global memory (L2) per chunk
+  const int64_t hrow = tl.row0 + (xv ? m : 0);
+  const uint8_t* lr = a.h_lo + hrow * (a.I_max / 2) + kq * 8;
+  const uint8_t* ls = a.h_lo_s + hrow * lo_sstride(a.I_max);
   const int nch = I / kDnLdsK;
   f32x4 acc = f32x4{0, 0, 0, 0};
   issue(0);
   for (int c = 0; c < nch; ++c) {
     Frag32 fw[U];
+    uint2 lq[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) fw[u] = load_w(wr + (int64_t)(c * kDnLdsK + u * 64) * 2);
-    wait_vmcnt<2 * U>();  // this wavefront's DMA of chunk c (issued before the 2 U weight loads)
+#pragma unroll
+    for (int u = 0; u < U; ++u) lq[u] = *reinterpret_cast<const uint2*>(lr + (c * kDnLdsK + u * 64) / 2);
+    const u32x4 sc4 = *reinterpret_cast<const u32x4*>(ls + c * (kDnLdsK / 32));
+    // this wavefront's DMA of chunk c, issued before the 2 U weight, U code and 1 scale loads
+    wait_vmcnt<3 * U + 1>();
     __builtin_amdgcn_s_barrier();  // ... and every other wavefront's; chunk c - 1 is read
     if (c + 1 < nch) issue(c + 1);
     const char* hb = hs + (c & 1) * CB + m * 1024;
@@ -356,6 +436,13 @@ __global__ void __launch_bounds__(256) k_down_stream_lds(FfnArgs a, int fb_per_t
       fh.lo = *reinterpret_cast<const u32x4*>(hb + (((u * 8 + kq * 2) ^ m) << 4));
       fh.hi = *reinterpret_cast<const u32x4*>(hb + (((u * 8 + kq * 2 + 1) ^ m) << 4));
       acc = mma_bf16(fw[u], fh, acc);
+      // block (64 u + 16 kq) / 32 = 2 u + kq / 2 of the chunk: byte of dword u / 2
+      const uint32_t sb = (sc4[u >> 1] >> (8 * (2 * (u & 1) + (kq >> 1)))) & 0xFFu;
+      const float sc = e8m0_f32(sb);
+      Frag32 fl;
+      fl.lo = __builtin_bit_cast(u32x4, e2m1x8_bf16(lq[u].x, sc));
+      fl.hi = __builtin_bit_cast(u32x4, e2m1x8_bf16(lq[u].y, sc));
+      acc = mma_bf16(fw[u], fl, acc);
     }
   }
   if (xv && active) store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + kq * 4, acc);

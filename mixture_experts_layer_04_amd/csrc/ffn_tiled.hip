@@ -23,6 +23,12 @@
 // (~250 B/clk/CU) where padded or plainly swizzled rows reach half of it. A wavefront's
 // DMA writes 1 KB contiguously (16 B per lane, lane order), i.e. 4 + 4 rows of a group,
 // and each lane's global address absorbs the layout.
+//
+// bf16 weights: the gate/up epilogue writes h as bf16 plus its MXFP4-coded residual
+// (ffn_common.h), and the down launch stages the residual with its activation rows (32 B
+// of E2M1 codes and a scale dword a row, laid out as the MXFP4 weight rows are), decodes
+// each residual fragment as it is read and multiplies it with the same weight fragment:
+// two MFMAs per fragment pair. MXFP4 weights keep a plain bf16 h.
 #include "ffn_common.h"
 
 namespace moe {
@@ -46,8 +52,8 @@ namespace {
 #ifndef MOE_T2_STAGES_B_GU  // weight-ring stages of the bf16 gate/up launch
 #define MOE_T2_STAGES_B_GU 2
 #endif
-#ifndef MOE_T2_STAGES_B_DN  // weight-ring stages of the bf16 down launch: its h rows are
-#define MOE_T2_STAGES_B_DN 3  // L2-resident, its weights stream from HBM (80 KB: 2 WGs a CU)
+#ifndef MOE_T2_STAGES_B_DN  // weight-ring stages of the bf16 down launch (73 KB with the
+#define MOE_T2_STAGES_B_DN 2  // residual of h in the activation stages: 2 WGs a CU)
 #endif
 #ifndef MOE_T2_MX_STAGES
 #define MOE_T2_MX_STAGES 2
@@ -60,13 +66,13 @@ constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt to them round-robi
 #define MOE_T2_WAVES_PER_SIMD 2
 #endif
 // bf16 with 256 x 256 tiles: 4 x 4 wavefronts of 4 x 4 MFMA tiles; a 2-stage activation
-// ring with 2 (gate/up) or 3 (down: its weights stream from HBM) weight stages, 128 or
-// 160 KB of LDS
+// ring and a 2-stage weight ring, 128 KB (gate/up) or 146 KB (down, whose activation
+// stages also hold h's residual) of LDS
 #ifndef MOE_T2B_STAGES_B_GU
 #define MOE_T2B_STAGES_B_GU 2
 #endif
-#ifndef MOE_T2B_STAGES_B_DN
-#define MOE_T2B_STAGES_B_DN 3
+#ifndef MOE_T2B_STAGES_B_DN  // down: 2 weight stages beside 2 activation stages that also
+#define MOE_T2B_STAGES_B_DN 2  // carry h's residual (146 KB)
 #endif
 static_assert(4 * 16 * 4 == kTiledMB && 4 * 16 * 4 == kTiledNB, "tile shape of the tile list");
 // waves a SIMD that the register budget must allow: a 16-wavefront workgroup puts four on
@@ -87,7 +93,21 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
   constexpr int NW = WGM * WGN;
   constexpr int BM = WGM * 16 * TM, BN = WGN * 16 * TN;
   constexpr int BSTAGE = kMX ? BN * 32 + BN * 4 : BN * 128;  // weight bytes of a stage
-  constexpr int ASTAGE = BM * 128;                          // activation bytes of a stage
+  // bf16 weights: h carries an MXFP4 residual; the down launch stages it with the A rows
+  constexpr bool kLo = !kMX;
+  constexpr bool kALo = kLo && !kGateUp;
+  constexpr int AHI = BM * 128;                // activation (h) bytes of a stage
+  constexpr int ALO = kALo ? BM * 32 : 0;      // residual codes of a stage
+  constexpr int ASTAGE = AHI + ALO + (kALo ? BM * 4 : 0);  // + their scale dwords
+  // residual: each wavefront moves UPWA 16-B units of codes (one instruction, LPWA lanes)
+  // and the scale dwords of SPWA rows
+  constexpr int UPWA = BM * 2 / NW;
+  constexpr int LPWA = UPWA;
+  constexpr int SPWA = BM / NW;
+  constexpr int CAL = kALo ? 2 : 0;            // DMA instructions per thread: codes + scales
+  static_assert(!kALo || (BM * 2 % NW == 0 && UPWA <= 64 && UPWA % 2 == 0 && SPWA <= 64),
+                "residual DMA rounds");
+  static_assert(!kLo || TN == 4, "a lane's gate/up features span one 32-feature block");
   constexpr int RPI = NW * 8;                  // LDS rows filled per DMA instruction round
   constexpr int CA = BM / RPI;                 // DMA instructions per thread per K block: A,
   // MXFP4: each wavefront moves its UPW 16-B units of a stage's codes (CB instructions,
@@ -103,7 +123,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
   // activation ring (S stages), then weight ring (SB stages): the weights, which mostly
   // come from HBM, may be requested further ahead than the activations, mostly L2 hits
   __shared__ __attribute__((aligned(1024))) char smem[S * ASTAGE + SB * BSTAGE];
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  // the wavefront index as a uniform (scalar) value: the DMA destinations derive from it
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   // Work items (tile, weight block) are cut into kXcds equal contiguous chunks, chunk x run
   // by the workgroups that the dispatcher deals to XCD x (blockIdx = x mod kXcds), so that
   // each XCD's L2 serves the items that share data. Inside a chunk the items of a block
@@ -174,6 +195,21 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
       bg[i] = wbase + weight_row(r) * wrow_bytes + cc * 16;
     }
   }
+  // residual of h (down, bf16): lane l of wavefront w moves 16-B unit UPWA w + l of the
+  // codes (row unit / 2, physical half l % 2 swizzled as for MXFP4 weight rows) and, if
+  // l < SPWA, the scale dword of row SPWA w + l
+  const uint8_t* alg = nullptr;
+  const uint8_t* asg = nullptr;
+  if (kALo) {
+    const int u = UPWA * wave + (l < LPWA ? l : 0);
+    const int r = u >> 1;
+    const int lh = (u & 1) ^ ((r >> 3) & 1);
+    const int grow = tl.row0 + (r < tl.nrows ? r : tl.nrows - 1);
+    alg = a.h_lo + (int64_t)grow * (a.I_max / 2) + lh * 16;
+    const int rs = SPWA * wave + (l < SPWA ? l : 0);
+    const int grs = tl.row0 + (rs < tl.nrows ? rs : tl.nrows - 1);
+    asg = a.h_lo_s + (int64_t)grs * lo_sstride(a.I_max);
+  }
   if (kMX) {
     // lanes l < SPW of wavefront w fetch the scale dword of B-tile row SPW w + l
     const uint8_t* sbase = reinterpret_cast<const uint8_t*>(kGateUp ? a.bank[bank].w13_scale
@@ -185,6 +221,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
     char* st = smem + (kt % S) * ASTAGE;
 #pragma unroll
     for (int i = 0; i < CA; ++i) dma16(ag[i] + (int64_t)kt * 128, st + (NW * i + wave) * 1024);
+    if (kALo) {
+      if (l < LPWA) dma16(alg + (int64_t)kt * 32, st + AHI + UPWA * wave * 16);
+      if (l < SPWA) dma4(asg + (kt & ~1) * 2, st + AHI + ALO + wave * (SPWA * 4));
+    }
   };
   auto issue_b = [&](int kt) {
     char* st = smem + S * ASTAGE + (kt % SB) * BSTAGE;
@@ -207,15 +247,20 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
   const int KT = K / 64;  // 64-element K blocks (128 B of bf16 a row)
-  int arow[TM], brow[TN];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) arow[t] = wm * (16 * TM) + t * 16 + m16;
-#pragma unroll
-  for (int t = 0; t < TN; ++t) brow[t] = wn * (16 * TN) + t * 16 + m16;
+  // This lane's fragment rows are arow0 + 16 t (A) and brow0 + 16 t (B). Adding 16 t leaves
+  // a row's low four bits alone, so in every LDS layout here row tile t's read is the
+  // first one's plus a constant (2048 t in lds_off's, 512 t in 32-B code rows, 64 t in
+  // scale dwords): one per-lane base offset per read kind, the rest immediates.
+  const int arow0 = wm * (16 * TM) + m16, brow0 = wn * (16 * TN) + m16;
+  const int aoff[2] = {lds_off(arow0, 2 * g), lds_off(arow0, 2 * g + 1)};  // per k-step
+  const int boff[2] = {lds_off(brow0, 2 * g), lds_off(brow0, 2 * g + 1)};
+  // 32-B E2M1 code rows (MXFP4 weights; h's residual): this lane's 8-B quarter g, swizzled
+  const int bq = brow0 * 32 + 8 * (g ^ (((brow0 >> 3) & 1) << 1));
+  const int lq0 = AHI + arow0 * 32 + 8 * (g ^ (((arow0 >> 3) & 1) << 1));
   // Step i issues A(i + S - 1), then B(i + SB - 1); the steps before the loop issue the
   // blocks >= 0 of steps -(max(S, SB) - 1) .. -1. Block kt has landed once no more DMA
   // instructions are outstanding than were issued after the later of A(kt) and B(kt).
-  constexpr int OA = CA, OB = CB + CS, SL = S > SB ? S : SB;
+  constexpr int OA = CA + CAL, OB = CB + CS, SL = S > SB ? S : SB;
   constexpr int AFTER = S < SB ? OB + (S - 2) * (OA + OB) : (SB - 2) * (OA + OB);
   static_assert(S >= 2 && SB >= 2 && AFTER < 64, "ring depths");
 #pragma unroll
@@ -244,35 +289,62 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
       // MXFP4: this lane's 16 codes (elements 16 g .. 16 g + 15 of the K block) and scale
       uint2 wq[kMX ? TN : 1];
       float wsc[kMX ? TN : 1];
+      // the scale byte of this lane's 16 elements within a row's scale dword
+      const int sbyte = (kt & 1) * 2 + (g >> 1);
       if (kMX) {
+        const char* q = curb + bq;
+        const char* sc = curb + BN * 32 + 4 * brow0 + sbyte;
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
-          const char* rb = curb + brow[t] * 32;
           // two 32-bit reads: with one 64-bit read the compiler makes it wait for all DMA
-          const char* q = rb + 8 * (g ^ (((brow[t] >> 3) & 1) << 1));
-          wq[t].x = *reinterpret_cast<const uint32_t*>(q);
-          wq[t].y = *reinterpret_cast<const uint32_t*>(q + 4);
-          wsc[t] = e8m0_f32(*reinterpret_cast<const uint8_t*>(curb + BN * 32 + 4 * brow[t] +
-                                                               (kt & 1) * 2 + (g >> 1)));
+          wq[t].x = *reinterpret_cast<const uint32_t*>(q + 512 * t);
+          wq[t].y = *reinterpret_cast<const uint32_t*>(q + 512 * t + 4);
+          wsc[t] = e8m0_f32(*reinterpret_cast<const uint8_t*>(sc + 64 * t));
         }
+      }
+      // bf16 down: the block scale of this lane's 16 residual elements of each A row (the
+      // writer emits codes 0..254 only; code 0, a scale of 2^-127 for residuals below
+      // 2^-125, decodes to 0 here)
+      float lsc[kALo ? TM : 1];
+      if (kALo) {
+        const char* sc = cur + AHI + ALO + 4 * arow0 + sbyte;
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+          lsc[t] = __uint_as_float((uint32_t)*reinterpret_cast<const uint8_t*>(sc + 64 * t) << 23);
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 fa[TM], fb[TN];
-        const int c = 2 * g + ks;  // logical 16-B chunk
+        uint32_t lq[kALo ? TM : 1];  // the residual's 8 codes of k-step ks, each A row
+        const char* pa = cur + aoff[ks];
 #pragma unroll
-        for (int t = 0; t < TM; ++t)
-          fa[t] = *reinterpret_cast<const bf16x8*>(cur + lds_off(arow[t], c));
+        for (int t = 0; t < TM; ++t) fa[t] = *reinterpret_cast<const bf16x8*>(pa + 2048 * t);
+        if (kALo) {
+          const char* q = cur + lq0 + 4 * ks;
+#pragma unroll
+          for (int t = 0; t < TM; ++t) lq[t] = *reinterpret_cast<const uint32_t*>(q + 512 * t);
+        }
+        const char* pb = curb + boff[ks];
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
           if (kMX) fb[t] = e2m1x8_bf16(ks ? wq[t].y : wq[t].x, wsc[t]);
-          else fb[t] = *reinterpret_cast<const bf16x8*>(curb + lds_off(brow[t], c));
+          else fb[t] = *reinterpret_cast<const bf16x8*>(pb + 2048 * t);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        if (kALo) {
+          // then the residual: each A row tile's fragment decoded just before its MFMAs
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const bf16x8 fl = e2m1x8_bf16(lq[i], lsc[i]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, fb[j], acc[i][j], 0, 0, 0);
+          }
+        }
       }
     }
   };
@@ -285,7 +357,31 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
       const int rl = wm * (16 * TM) + mt * 16 + 4 * g + i;
       if (rl >= tl.nrows) continue;
       const int64_t row = tl.row0 + rl;
-      if (kGateUp) {
+      if (kGateUp && kLo) {
+        // h = hi + lo: hi bf16; lo as MXFP4 over the lane group's 32-feature block (the 16
+        // lanes of group g hold row rl's features fb + 16 p + m16, p = 0, 1)
+        const int fb = f0 + wn * (8 * TN);
+        float lo[TN / 2];
+        float am = 0.0f;
+#pragma unroll
+        for (int p = 0; p < TN / 2; ++p) {
+          const float hv = silu_mul(acc[mt][2 * p][i], acc[mt][2 * p + 1][i]);
+          reinterpret_cast<uint16_t*>(a.h)[row * a.I_max + fb + p * 16 + m16] = split_bf16(hv, &lo[p]);
+          am = fmaxf(am, fabsf(lo[p]));
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+        const int e = mx_exponent(am);
+        const float inv = exp2i(-e);
+#pragma unroll
+        for (int p = 0; p < TN / 2; ++p) {
+          const uint32_t cd = e2m1_code(lo[p] * inv);
+          const uint32_t nb2 = __shfl_xor(cd, 1, 64);  // the neighbouring feature's code
+          if ((m16 & 1) == 0)
+            a.h_lo[row * (a.I_max / 2) + (fb + p * 16 + m16) / 2] = (uint8_t)(cd | (nb2 << 4));
+        }
+        if (m16 == 0) a.h_lo_s[row * lo_sstride(a.I_max) + fb / 32] = (uint8_t)(e + 127);
+      } else if (kGateUp) {
 #pragma unroll
         for (int p = 0; p < TN / 2; ++p) {
           const int feat = f0 + wn * (8 * TN) + p * 16 + m16;

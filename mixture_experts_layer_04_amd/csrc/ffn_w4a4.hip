@@ -34,28 +34,6 @@ namespace {
 #endif
 constexpr int kA4Xcds = 8;
 
-// E2M1 code of v (already divided by the block scale): nearest of 0, .5, 1, 1.5, 2, 3, 4,
-// 6, ties to the even code, larger magnitudes to 6; the sign in bit 3 (also for zero).
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-                     (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 0x8u);
-}
-
-// Shared-scale exponent e of a block from its amax (a non-negative fp32).
-__device__ __forceinline__ int mx_exponent(float amax) {
-  const int be = (int)(__float_as_uint(amax) >> 23);  // biased exponent (amax >= 0)
-  if (amax == 0.0f) return 0;
-  if (be == 0) return -127;                            // subnormal amax: below 2^-125
-  const int e = be - 127 - 2;
-  return e < -127 ? -127 : e;
-}
-
-__device__ __forceinline__ float exp2i(int e) {  // 2^e for e in [-127, 127], exact
-  return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
-}
-
 // One thread per 32-element block of a bf16 row: codes [n, H/2] bytes, scales [n, H/32].
 __global__ void __launch_bounds__(256) k_quant_rows_mxfp4(const uint16_t* __restrict__ x, int n,
                                                           int H, uint8_t* __restrict__ q,

@@ -62,6 +62,11 @@ size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I
     const size_t q = ((size_t)rows_total * (I_max / 2) + 255) / 256 * 256;
     return q + ((size_t)rows_total * (I_max / 32) + 255) / 256 * 256;
   }
+  if (wdt == MOE_BF16) {  // h as bf16 plus its MXFP4-coded residual (ffn_common.h)
+    const size_t hi = ((size_t)rows_total * I_max * 2 + 255) / 256 * 256;
+    const size_t lo = ((size_t)rows_total * (I_max / 2) + 255) / 256 * 256;
+    return hi + lo + ((size_t)rows_total * lo_sstride(I_max) + 255) / 256 * 256;
+  }
   const size_t hb = (wdt == MOE_F32) ? 4 : 2;
   return ((size_t)rows_total * I_max * hb + 255) / 256 * 256;
 }
@@ -79,6 +84,11 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
   if (a.wdt == MOE_MXFP4_A4) {
     a.h_xs = reinterpret_cast<uint8_t*>(scratch) + ((size_t)a.rows_total * (a.I_max / 2) + 255) / 256 * 256;
     return launch_ffn_w4a4(a, s, mid_event);
+  }
+  if (a.wdt == MOE_BF16) {
+    char* p = reinterpret_cast<char*>(scratch) + ((size_t)a.rows_total * a.I_max * 2 + 255) / 256 * 256;
+    a.h_lo = reinterpret_cast<uint8_t*>(p);
+    a.h_lo_s = a.h_lo + ((size_t)a.rows_total * (a.I_max / 2) + 255) / 256 * 256;
   }
   if ((a.tile_m == kTiledM || a.tile_m == kTiledMB) && (a.wdt == MOE_BF16 || a.wdt == MOE_MXFP4))
     return launch_ffn_tiled(a, s, mid_event);

@@ -86,6 +86,8 @@ struct FfnArgs {
   void* h;                // [rows_total, I_max] intermediate (bf16, f32, or fp8 + scales)
   float* h_scale;         // fp8 path: [rows_total, I_max/128]
   uint8_t* h_xs;          // W4A4 path: E8M0 scales of h [rows_total, I_max/32] (codes in h)
+  uint8_t* h_lo;          // bf16 banks: MXFP4 codes of h's residual [rows_total, I_max/2]
+  uint8_t* h_lo_s;        //   and their E8M0 scales [rows_total, lo_sstride(I_max)]
   void* y;                // [rows_total, H]
   const Tile* tiles;      // tile list (row chunks of `tile_m` rows)
   const int32_t* ntiles;  // device count of valid tiles

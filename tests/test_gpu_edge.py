@@ -107,16 +107,24 @@ def _bf16(a):
     return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).double().numpy()
 
 
+def _split_h(h64):
+    """h as the bf16 kernels carry it into the down GEMM: fp32 h rounded to bf16 (hi) plus
+    the residual fp32(h) - hi coded as MXFP4 per 32 features (OCP MX rule)."""
+    h32 = h64.astype(np.float32).astype(np.float64)
+    hi = _bf16(h32)
+    return hi + O.quantise_rows_mxfp4((h32 - hi).astype(np.float32))[2]
+
+
 def _bf16_h_layer(host, want):
     """The layer as the bf16 kernels compute it, in float64: the oracle's routing and
-    weights, with h rounded to bf16 (the down GEMM's operand) -- not a reading of the
-    method, the arithmetic of this implementation."""
+    weights, with h carried as bf16 plus an MXFP4-coded residual (the down GEMM's operands)
+    -- not a reading of the method, the arithmetic of this implementation."""
     x = O.bf16_to_f64(host.x)
     idx, w = want["topk_idx"], want["topk_w"]
 
     def ffn(a, w13, w2):
         i = w2.shape[1]
-        return _bf16(O.silu(a @ w13[:i].T) * (a @ w13[i:].T)) @ w2.T
+        return _split_h(O.silu(a @ w13[:i].T) * (a @ w13[i:].T)) @ w2.T
     out = np.zeros_like(x)
     for e in np.unique(idx):
         tok, slot = np.nonzero(idx == e)
@@ -127,21 +135,17 @@ def _bf16_h_layer(host, want):
 
 
 def test_all_tokens_on_the_same_experts():
-    """Routing of the pile-up is bit-exact, and the output is the bf16 kernels' arithmetic:
+    """Routing of the pile-up is bit-exact; the output is within the bf16 tolerance of the
+    oracle (a heavy-tailed output, max/RMS 5.2: its bf16 storage alone costs 0.0150, and a
+    plain bf16 h would add enough to reach 0.0214); and it is the bf16 kernels' arithmetic:
     against a float64 simulation of it the RMS difference is at the bf16 storage level."""
     cfg, host, got, want = _pile_up()
     print("case", describe(cfg), flush=True)
     assert np.array_equal(got["topk_idx"], want["topk_idx"])
     assert got["counts"].tolist() == [cfg.T] * 8 + [0] * (cfg.E - 8)
+    err = O.rel_err(got["out"], want["out"])
+    print("pile-up max err vs oracle", err, flush=True)
+    assert err <= TOL["bf16"]
     sim = _bf16_h_layer(host, want)
     rms = np.sqrt(np.mean(want["out"] ** 2))
     assert np.sqrt(np.mean((got["out"] - sim) ** 2)) / rms <= 2e-3
-    print("pile-up max err vs oracle", O.rel_err(got["out"], want["out"]), flush=True)
-
-
-@pytest.mark.xfail(strict=True, reason="known limit of the bf16 h intermediate on a heavy-tailed "
-                   "output (max/RMS 5.2): 0.0214 against 2e-2, of which 0.0150 is the bf16 "
-                   "storage of the output itself")
-def test_all_tokens_on_the_same_experts_within_bf16_tolerance():
-    cfg, host, got, want = _pile_up()
-    assert O.rel_err(got["out"], want["out"]) <= TOL["bf16"]

@@ -101,7 +101,10 @@ def test_empty_batch():
 
 
 def test_standalone_entry_points():
-    """moe_route, moe_permute, moe_grouped_ffn and moe_combine one by one."""
+    """moe_route, moe_permute, moe_grouped_ffn and moe_combine one by one, composed as
+    moe_layer_forward composes them: the expert rows stay fp32 until the combine rounds once
+    (rows rounded to bf16 and then combined into a bf16 output are rounded twice; that is
+    covered row by row in test_gpu_parity_more)."""
     cfg = SMALL[1]
     host, dev = problems(cfg)
     T, k, E, H = cfg.T, cfg.k, cfg.E, cfg.H
@@ -116,7 +119,7 @@ def test_standalone_entry_points():
     inv_perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
     x_perm = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
     moe.moe_permute(idx, E, counts, offsets, perm_src, inv_perm, dev.x, x_perm)
-    y_perm = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
+    y_perm = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
     moe.moe_grouped_ffn(experts(dev.routed), x_perm, offsets, y_perm)
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     moe.moe_combine(y_perm, inv_perm, w, out)

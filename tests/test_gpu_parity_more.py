@@ -110,3 +110,50 @@ def test_grouped_ffn_alone(case, y_dt):
     tol = TOL[wdt] if not (wdt == "f32" and y_dt == "bf16") else TOL["bf16"]
     print(name, y_dt, "rel err", err, flush=True)
     assert err <= tol, (name, y_dt, err)
+
+
+def _split_h(h64):
+    """h as the bf16 kernels carry it into the down GEMM: fp32 h rounded to bf16 (hi) plus
+    the residual fp32(h) - hi coded as MXFP4 per 32 features (OCP MX rule)."""
+    h32 = h64.astype(np.float32).astype(np.float64)
+    hi = torch.from_numpy(h32.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    return hi + O.quantise_rows_mxfp4((h32 - hi).astype(np.float32))[2]
+
+
+@pytest.mark.parametrize("case", [c for c in FFN_CASES if c[1] == "bf16"], ids=lambda c: c[0])
+def test_bf16_down_carries_h_residual(case):
+    """The bf16 kernels' arithmetic, pinned tighter than the tolerance: with fp32 output
+    rows, every kernel family's result equals a float64 simulation of h as bf16 plus its
+    MXFP4-coded residual to 1e-4 of the RMS (without the residual the two differ by about
+    1e-3)."""
+    name, wdt, H, I, E, rows = case
+    cfg = MoEConfig(f"ffn_{name}", T=rows, H=H, E=E, k=1, I=I, score="none", act="bf16", wdt=wdt,
+                    out="f32", seed=140 + len(name), weight_seed=140 + len(name),
+                    dirichlet_alpha=0.7)
+    print("case", describe(cfg), flush=True)
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
+    counts = np.bincount(host.topk_idx[:, 0], minlength=E)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    x64 = O.bf16_to_f64(host.x)
+    sim = np.zeros((rows, H))
+    plain = np.zeros((rows, H))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            w13, w2 = O.expert_weights(host.routed, e)
+            h = O.silu(x64[r0:r1] @ w13[:I].T) * (x64[r0:r1] @ w13[I:].T)
+            sim[r0:r1] = _split_h(h) @ w2.T
+            hb = torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).double().numpy()
+            plain[r0:r1] = hb @ w2.T
+    y = torch.empty((rows, H), dtype=torch.float32, device="cuda")
+    moe.moe_grouped_ffn(moe.Experts.from_bank(dev.routed), dev.x, torch.from_numpy(offsets).cuda(), y)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    rms = np.sqrt(np.mean(sim ** 2))
+    d = np.sqrt(np.mean((got - sim) ** 2)) / rms
+    print(name, "rms diff vs simulation", d, "plain bf16 h would be",
+          np.sqrt(np.mean((plain - sim) ** 2)) / rms, flush=True)
+    assert np.sqrt(np.mean((plain - sim) ** 2)) / rms > 3e-4   # the check has teeth here
+    assert d <= 1e-4
