@@ -16,7 +16,8 @@
  *  - Tensor arguments are DEVICE pointers (HBM), row-major, the last dimension
  *    contiguous. Descriptor structs and scalars are passed from the host. The caller
  *    allocates and owns every buffer, including the workspace; the library allocates
- *    nothing and keeps no device state between calls.
+ *    nothing and keeps no device state between calls (the one exception: the static
+ *    workspace of moe_layer_forward_noalloc, which holds no result between calls).
  *  - Calls are asynchronous: they only enqueue kernels on `stream` (a hipStream_t; NULL
  *    is the default stream) and never synchronise or copy to the host, so they may be
  *    captured into a HIP graph. Group sizes stay on the device.
@@ -216,6 +217,27 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* d, const void* x, void*
                                    int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
                                    float* logits_out, void* ws, size_t ws_bytes, void* stream,
                                    void* const* events);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_layer_forward with the library's own
+ * static workspace instead of a caller's. Same descriptor, checks, kernels, launch
+ * configurations and results (bit for bit) as moe_layer_forward.
+ *   The workspace is a device array of MOE_NOALLOC_SCRATCH_BYTES held by the library on
+ *   every GPU it runs on until the process ends; its device address is looked up once per
+ *   device (on the first call there, with the stream's device made current for the lookup).
+ *   Nothing is allocated and nothing in it needs clearing between calls: the kernels write
+ *   every byte they read.
+ *   MOE_ERR_WORKSPACE (before any HIP call) if moe_layer_workspace_size(d) exceeds
+ *   MOE_NOALLOC_SCRATCH_BYTES: 64 MiB takes decode-sized batches, e.g. up to about 190
+ *   tokens of a 7168-wide, 256-expert, top-8 bf16 layer with a shared expert (128 tokens:
+ *   41 MiB); larger batches need moe_layer_forward and a workspace.
+ *   Calls on one GPU share the array: calls that may overlap in time on one GPU (different
+ *   streams, or threads without ordering) race on it and must not be issued.
+ *   MOE_ERR_HIP if the device address cannot be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* d, const void* x, void* out,
+                                     int32_t* topk_idx_out, float* topk_w_out,
+                                     int32_t* counts_out, float* logits_out, void* stream);
 
 /* Pre-routed rows (one GPU's share under expert parallelism, after the dispatch exchange):
  * each of `rows` received rows carries one local expert id and one weight.

@@ -54,7 +54,7 @@ _lib = None
 EXPORTS = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
            "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_timed",
-           "moe_layer_forward_overlap",
+           "moe_layer_forward_overlap", "moe_layer_forward_noalloc",
            "moe_rows_workspace_size",
            "moe_rows_forward", "moe_rows_forward_timed", "moe_quantize_fp8", "moe_quantize_mxfp4", "moe_bias_update",
            "moe_status_str",
@@ -87,6 +87,7 @@ def lib():
                                           P(vp)]
     L.moe_layer_forward_overlap.argtypes = [P(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                             vp, vp, vp]
+    L.moe_layer_forward_noalloc.argtypes = [P(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp]
     L.moe_rows_workspace_size.argtypes = [P(moe_experts), ci, i32]
     L.moe_rows_workspace_size.restype = sz
     L.moe_rows_forward.argtypes = [P(moe_experts), vp, ci, vp, vp, i32, vp, ci, vp, sz, vp]
@@ -94,6 +95,7 @@ def lib():
                                          P(vp)]
     for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
               "moe_layer_forward", "moe_layer_forward_timed", "moe_layer_forward_overlap",
+              "moe_layer_forward_noalloc",
               "moe_rows_forward",
               "moe_rows_forward_timed"):
         getattr(L, f).restype = ci
@@ -236,6 +238,17 @@ def moe_layer_forward(desc: moe_layer_desc, x, out, ws, topk_idx=None, topk_w=No
     st = lib().moe_layer_forward(ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(topk_idx), _ptr(topk_w),
                                  _ptr(counts), _ptr(logits), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_layer_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES of moe.h
+
+
+def moe_layer_forward_noalloc(desc: moe_layer_desc, x, out, topk_idx=None, topk_w=None,
+                              counts=None, logits=None, stream=None):
+    """moe_layer_forward on the library's static per-GPU workspace (no workspace argument)."""
+    st = lib().moe_layer_forward_noalloc(ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(topk_idx),
+                                         _ptr(topk_w), _ptr(counts), _ptr(logits), _stream(stream))
+    _check(st, "moe_layer_forward_noalloc")
 
 
 STAGE_EVENTS = 6

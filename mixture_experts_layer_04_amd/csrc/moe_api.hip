@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -494,6 +496,64 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* d, const void* x, void*
     if (!events[i]) return MOE_ERR_NULL;
   return layer_forward(d, x, out, topk_idx_out, topk_w_out, counts_out, logits_out, ws, ws_bytes,
                        stream, events);
+}
+
+// ---------------------------------------------------- no-allocation layer forward
+
+// The workspace of moe_layer_forward_noalloc: one copy on every GPU the library runs on,
+// held until the process ends. In host code this name is a host-side stand-in, not a
+// device address: the address of each GPU's copy comes from hipGetSymbolAddress, looked
+// up once per device with that device current, and only that address is ever passed on.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the stream's device (looked up on the first call there).
+hipError_t scratch_on(hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (s) {
+    hipDevice_t sd;
+    if ((e = hipStreamGetDevice(s, &sd)) != hipSuccess) return e;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (!p || ((uintptr_t)p & 255u)) return hipErrorInvalidSymbol;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* d, const void* x, void* out,
+                                     int32_t* topk_idx_out, float* topk_w_out,
+                                     int32_t* counts_out, float* logits_out, void* stream) {
+  size_t need = 0;
+  moe_status st = moe_layer_workspace_size(d, &need);
+  if (st != MOE_OK) return st;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  hipError_t e = scratch_on((hipStream_t)stream, &ws);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward_noalloc scratch address");
+  return layer_forward(d, x, out, topk_idx_out, topk_w_out, counts_out, logits_out, ws,
+                       MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 // ------------------------------------------------------------- pre-routed rows

@@ -224,3 +224,24 @@ def test_quantize_mxfp4_validation():
     b = bank("mxfp4a4", H=256, I=128, scales=True)
     assert L.moe_rows_forward(ctypes.byref(b), P, moe.MOE_F32, P, P, 16, P, moe.MOE_BF16, P,
                               1 << 30, None) == moe.MOE_ERR_DTYPE   # activations must be bf16
+
+
+def test_noalloc_rejects_layers_beyond_its_static_workspace():
+    """moe_layer_forward_noalloc refuses, before any HIP call, a layer whose workspace exceeds
+    MOE_NOALLOC_SCRATCH_BYTES (here a 8192-token prefill batch: 2.4 GB)."""
+    L = moe.lib()
+    d = moe.moe_layer_desc()
+    d.T, d.H, d.E, d.k = 8192, 7168, 256, 8
+    d.score_fn, d.route_scale = moe.MOE_SIGMOID, 2.5
+    d.act_dtype = d.out_dtype = moe.MOE_BF16
+    d.w_router = P
+    d.routed = moe.moe_experts(moe.MOE_BF16, P, None, P, None, 256, 7168, 2048)
+    d.shared = moe.moe_experts(moe.MOE_BF16, P, None, P, None, 1, 7168, 2048)
+    n = ctypes.c_size_t(0)
+    assert L.moe_layer_workspace_size(ctypes.byref(d), ctypes.byref(n)) == moe.MOE_OK
+    assert n.value > moe.NOALLOC_SCRATCH_BYTES
+    st = L.moe_layer_forward_noalloc(ctypes.byref(d), P, P, None, None, None, None, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    # and the usual argument checks come first
+    d.k = 300
+    assert L.moe_layer_forward_noalloc(ctypes.byref(d), P, P, None, None, None, None, None) == moe.MOE_ERR_SHAPE
