@@ -23,6 +23,9 @@ What is computed, and where it comes from:
     of the SwiGLU output follow the FP8/FP4 grouped GEMM with fused SwiGLU and
     re-quantisation in "GC-MoE: Overlapping Expert-Parallel Token Dispatch with
     FP8/FP4 Grouped GEMM via CUDA Green Contexts" (key_changes, fourth item).
+  * INT8 weights and activations (W8A8) follow section 3.1 of "Trillion-Parameter LLM
+    Architecture Explained and Cost-Efficient Inference in Practice"; the recipe (symmetric,
+    fp32 block scales amax/127) is a reading, see quantise_rows_int8.
   * Readings where the pages are silent (sigmoid or softmax scoring, the 2.5
     scale, fp64 accumulation of the router, tie-breaking, block-scale layouts)
     are stated at each function.
@@ -137,6 +140,29 @@ def quantise_rows_e4m3(v32: np.ndarray, block: int = 128):
     return codes, s, deq.reshape(R, C)
 
 
+def quantise_rows_int8(v32: np.ndarray, block: int = 128):
+    """Per-row, per-`block`-column INT8 quantisation of fp32 values (the W8A8 path).
+
+    Reading ("Trillion-Parameter LLM Architecture Explained and Cost-Efficient Inference in
+    Practice", section 3.1 names W8A8 -- weights and activations as INT8 on INT8 matrix
+    units -- but fixes no recipe): symmetric INT8 with the block structure of the FP8
+    path. For each 1 x 128 block, scale s = fp32(amax / 127) (s = 1 for an all-zero block)
+    and code q = round-half-to-even(fp32(v / s)), clamped to [-127, 127]; the dequantised
+    value is q * s. Decisions are taken in fp32.
+    Returns (codes int8 [R, C], scales f32 [R, C/block], dequantised f64 [R, C]).
+    """
+    v = np.asarray(v32, np.float32)
+    R, C = v.shape
+    vb = v.reshape(R, C // block, block)
+    amax = np.abs(vb).max(axis=2)
+    s = np.where(amax == 0, np.float32(1.0), (amax / np.float32(127.0)).astype(np.float32))
+    s = s.astype(np.float32)
+    scaled = (vb / s[:, :, None]).astype(np.float32)
+    codes = np.clip(np.rint(scaled), -127, 127).astype(np.int8).reshape(R, C)
+    deq = codes.astype(np.float64).reshape(R, C // block, block) * s[:, :, None].astype(np.float64)
+    return codes, s, deq.reshape(R, C)
+
+
 def _e2m1_grid() -> np.ndarray:
     """The 8 non-negative E2M1 values, indexed by their code 0..7."""
     return e2m1_to_f64(np.arange(8, dtype=np.uint8))
@@ -184,6 +210,7 @@ def decode_matrix(fmt: str, part: dict) -> np.ndarray:
     """One expert matrix [R, C] in storage format -> float64.
 
     fp8: E4M3 codes times the fp32 scale of their 128 x 128 block.
+    int8: INT8 codes times the fp32 scale of their 128 x 128 block.
     mxfp4: E2M1 nibbles (element 2i in the low nibble of byte i) times 2^(e8m0 - 127)
     of their 32-element block along C.
     """
@@ -192,10 +219,11 @@ def decode_matrix(fmt: str, part: dict) -> np.ndarray:
         return f32_to_f64(w)
     if fmt == "bf16":
         return bf16_to_f64(w)
-    if fmt == "fp8":
+    if fmt in ("fp8", "int8"):
         s = np.asarray(part["scale"], np.float32).astype(np.float64)
         R, C = w.shape
-        v = e4m3_to_f64(w).reshape(R // 128, 128, C // 128, 128)
+        codes = e4m3_to_f64(w) if fmt == "fp8" else np.asarray(w, np.int8).astype(np.float64)
+        v = codes.reshape(R // 128, 128, C // 128, 128)
         return (v * s[:, None, :, None]).reshape(R, C)
     if fmt in ("mxfp4", "mxfp4a4"):
         p = np.asarray(w, np.uint8)
@@ -340,13 +368,16 @@ def expert_ffn(a64: np.ndarray, w13_64: np.ndarray, w2_64: np.ndarray, requant_h
     first I rows are Wg and the next I rows Wu. With requant_h (True or "fp8"), h is
     re-quantised to E4M3 per 1x128 block (from its fp32 value) before the down
     projection, as the fused SwiGLU + re-quantisation of the fp8 grouped GEMM does; with
-    "mxfp4", to MXFP4 per 1x32 block (the W4A4 path)."""
+    "mxfp4", to MXFP4 per 1x32 block (the W4A4 path); with "int8", to INT8 per 1x128 block
+    (the W8A8 path)."""
     I = w13_64.shape[0] // 2
     g = a64 @ w13_64[:I].T
     u = a64 @ w13_64[I:].T
     h = silu(g) * u
     if requant_h == "mxfp4":
         _, _, h = quantise_rows_mxfp4(h.astype(np.float32))
+    elif requant_h == "int8":
+        _, _, h = quantise_rows_int8(h.astype(np.float32))
     elif requant_h:
         _, _, h = quantise_rows_e4m3(h.astype(np.float32))
     return h @ w2_64.T
@@ -388,11 +419,15 @@ def layer_forward(prob, tokens=None, with_routing: bool = True, workers: int = 1
 
     fp8 = cfg.wdt == "fp8"
     a4 = cfg.wdt == "mxfp4a4"
-    requant = "mxfp4" if a4 else fp8
+    i8 = cfg.wdt == "int8"
+    requant = "mxfp4" if a4 else ("int8" if i8 else fp8)
     xs = x64[tokens]
     if fp8:
         # activations enter the expert GEMMs quantised per 1x128 block (from bf16/fp32)
         _, _, a = quantise_rows_e4m3(xs.astype(np.float32))
+    elif i8:
+        # W8A8: activations quantised to INT8 per 1x128 block
+        _, _, a = quantise_rows_int8(xs.astype(np.float32))
     elif a4:
         # W4A4: activations quantised to MXFP4 per 1x32 block
         _, _, a = quantise_rows_mxfp4(xs.astype(np.float32))

@@ -80,9 +80,11 @@ def _host():
     lib.synth_host_uniform_f32.argtypes = [u64, u32, u64, u64, f32, f32, vp, ci]
     lib.synth_host_fp8_bank.argtypes = [u64, u32, i64, i64, i64, i64, f32, vp, vp, vp, ci]
     lib.synth_host_mxfp4_bank.argtypes = [u64, u32, i64, i64, i64, i64, f32, vp, vp, vp, ci]
+    lib.synth_host_int8_bank.argtypes = [u64, u32, i64, i64, i64, i64, f32, vp, vp, vp, ci]
     lib.synth_host_philox_block.argtypes = [vp, vp, vp]
     for f in (lib.synth_host_words, lib.synth_host_normal_f32, lib.synth_host_normal_bf16,
               lib.synth_host_uniform_f32, lib.synth_host_fp8_bank, lib.synth_host_mxfp4_bank,
+              lib.synth_host_int8_bank,
               lib.synth_host_philox_block):
         f.restype = None
     return lib
@@ -144,6 +146,16 @@ def fp8_bank(seed: int, tid: int, e0: int, ne: int, rows: int, cols: int, std: f
     return codes, scales
 
 
+def int8_bank(seed: int, tid: int, e0: int, ne: int, rows: int, cols: int, std: float):
+    """Experts [e0, e0+ne): (codes int8 [ne,rows,cols], scales f32 [ne,rows/128,cols/128])."""
+    codes = np.empty((ne, rows, cols), np.int8)
+    scales = np.empty((ne, rows // 128, cols // 128), np.float32)
+    q = quantile_table()
+    _host().synth_host_int8_bank(seed, tid, e0, ne, rows, cols, np.float32(std), _p(q), _p(codes),
+                                 _p(scales), _NTHREADS)
+    return codes, scales
+
+
 def mxfp4_bank(seed: int, tid: int, e0: int, ne: int, rows: int, cols: int, std: float):
     """Experts [e0, e0+ne): (packed uint8 [ne,rows,cols/2], e8m0 codes uint8 [ne,rows,cols/32])."""
     packed = np.empty((ne, rows, cols // 2), np.uint8)
@@ -170,8 +182,9 @@ def _dev():
     lib.synth_dev_normal_f32.argtypes = [u64, u32, u64, f32, vp, vp, vp]
     lib.synth_dev_fp8_bank.argtypes = [u64, u32, i64, i64, i64, i64, f32, vp, vp, vp, vp]
     lib.synth_dev_mxfp4_bank.argtypes = [u64, u32, i64, i64, i64, i64, f32, vp, vp, vp, vp]
+    lib.synth_dev_int8_bank.argtypes = [u64, u32, i64, i64, i64, i64, f32, vp, vp, vp, vp]
     for f in (lib.synth_dev_words, lib.synth_dev_normal_bf16, lib.synth_dev_normal_f32,
-              lib.synth_dev_fp8_bank, lib.synth_dev_mxfp4_bank):
+              lib.synth_dev_fp8_bank, lib.synth_dev_mxfp4_bank, lib.synth_dev_int8_bank):
         f.restype = ctypes.c_int
     return lib
 
@@ -229,6 +242,17 @@ def dev_fp8_bank(seed: int, tid: int, ne: int, rows: int, cols: int, std: float,
     q = _dev_table(str(device))
     _chk(_dev().synth_dev_fp8_bank(seed, tid, 0, ne, rows, cols, np.float32(std), q.data_ptr(),
                                    codes.data_ptr(), scales.data_ptr(), _stream()), "fp8_bank")
+    return codes, scales
+
+
+def dev_int8_bank(seed: int, tid: int, ne: int, rows: int, cols: int, std: float, device="cuda"):
+    import torch
+
+    codes = torch.empty((ne, rows, cols), dtype=torch.int8, device=device)
+    scales = torch.empty((ne, rows // 128, cols // 128), dtype=torch.float32, device=device)
+    q = _dev_table(str(device))
+    _chk(_dev().synth_dev_int8_bank(seed, tid, 0, ne, rows, cols, np.float32(std), q.data_ptr(),
+                                    codes.data_ptr(), scales.data_ptr(), _stream()), "int8_bank")
     return codes, scales
 
 

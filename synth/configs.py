@@ -36,7 +36,7 @@ class MoEConfig:
     scale: float = 1.0          # routed-weight scale after renormalisation
     shared_I: int = 0           # shared-expert intermediate size (0: no shared expert)
     act: str = "bf16"           # activation storage: 'f32' | 'bf16'
-    wdt: str = "bf16"           # expert weight storage: 'f32' | 'bf16' | 'fp8' | 'mxfp4'
+    wdt: str = "bf16"           # expert weight storage: 'f32' | 'bf16' | 'fp8' | 'int8' | 'mxfp4'
     out: str = "bf16"           # output storage: 'f32' | 'bf16'
     seed: int = 0               # seed of x (and of everything else unless weight_seed is set)
     weight_seed: int = 0        # seed of router / expert / shared weights
@@ -84,6 +84,16 @@ CONFIGS = {
     "r1_decode_mxfp4": MoEConfig("r1_decode_mxfp4", T=128, H=7168, E=256, k=8, I=2048,
                                  score="sigmoid", use_bias=True, scale=2.5, shared_I=2048,
                                  wdt="mxfp4", seed=2000, weight_seed=2000),
+    # W8A8: r1_decode and r1_prefill with INT8 expert weights (128 x 128 blocks, fp32
+    # scales amax/127) and INT8 activations (1 x 128 blocks) on the INT8 matrix units: same
+    # seeds, so the same router and routing as the bf16 layers
+    "r1_decode_int8": MoEConfig("r1_decode_int8", T=128, H=7168, E=256, k=8, I=2048,
+                                score="sigmoid", use_bias=True, scale=2.5, shared_I=2048,
+                                wdt="int8", seed=2000, weight_seed=2000),
+    "r1_prefill_int8": MoEConfig("r1_prefill_int8", T=8192, H=7168, E=256, k=8, I=2048,
+                                 score="sigmoid", use_bias=True, scale=2.5, shared_I=2048,
+                                 wdt="int8", seed=3000, weight_seed=2000, zipf_s=1.1,
+                                 zipf_gamma=PREFILL_ZIPF_GAMMA),
     # one GPU's expert-parallel share with both GEMM operands in MXFP4 (W4A4): ep32_mxfp4's
     # weights, rows and loads, with the activations quantised to MXFP4 inside
     "ep32_w4a4": MoEConfig("ep32_w4a4", T=16384, H=7168, E=32, k=1, I=2048, score="none",

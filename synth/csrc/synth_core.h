@@ -9,8 +9,8 @@
  *     of two 32x32->64-bit multiplies with a Weyl-sequence key schedule.
  *   - inverse-transform sampling of N(0,1) through a table of normal quantiles
  *     (filled by the caller) with linear interpolation in fp32;
- *   - round-to-nearest-even narrowing of fp32 to bf16, OCP E4M3FN and OCP MX
- *     E2M1, used to store generated weights in the layer's storage formats.
+ *   - round-to-nearest-even narrowing of fp32 to bf16, OCP E4M3FN, OCP MX E2M1 and
+ *     symmetric INT8, used to store generated weights in the layer's storage formats.
  *
  * Every floating-point step is a single IEEE-754 binary32 operation (multiply,
  * add, divide) or exact integer work, so host and device agree bit for bit as
@@ -149,6 +149,15 @@ SYN_FN uint8_t syn_e4m3_rne_sat(float x) {
   if (m == 8u) { m = 0u; e += 1; }
   if (e > 8 || (e == 8 && m == 7u)) return (uint8_t)(sign | 0x7Eu);
   return (uint8_t)(sign | (uint32_t)((e + 7) << 3) | m);
+}
+
+/* fp32 (already divided by the block scale) -> symmetric INT8 code: the nearest integer,
+ * ties to even (rintf under the default rounding mode), clamped to [-127, 127]. */
+SYN_FN int8_t syn_int8_rne_sat(float x) {
+  float r = __builtin_rintf(x);
+  if (r > 127.0f) r = 127.0f;
+  if (r < -127.0f) r = -127.0f;
+  return (int8_t)r;
 }
 
 /* |x| -> OCP MX E2M1 magnitude code (0..7), round to nearest even, saturating

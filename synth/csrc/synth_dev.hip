@@ -53,7 +53,9 @@ __global__ void __launch_bounds__(kThreads) k_normal_f32(uint64_t seed, uint32_t
   }
 }
 
-// One workgroup per 128 x 128 block; 64 elements per thread.
+// One workgroup per 128 x 128 block; 64 elements per thread. kI8: symmetric INT8 codes with
+// scale amax/127, else E4M3 codes with scale amax/448.
+template <bool kI8>
 __global__ void __launch_bounds__(kThreads) k_fp8_bank(uint64_t seed, uint32_t tid, int64_t e0,
                                                        int64_t rows, int64_t cols, float std,
                                                        const float* q, uint8_t* codes,
@@ -81,9 +83,12 @@ __global__ void __launch_bounds__(kThreads) k_fp8_bank(uint64_t seed, uint32_t t
     __syncthreads();
   }
   amax = red[0];
-  float sc = (amax == 0.0f) ? 1.0f : __fdiv_rn(amax, 448.0f);
+  float sc = (amax == 0.0f) ? 1.0f : __fdiv_rn(amax, kI8 ? 127.0f : 448.0f);
   size_t o = (size_t)((e * rows + rb * 128 + r) * cols + cb * 128 + c0);
-  for (int c = 0; c < 64; ++c) codes[o + c] = syn_e4m3_rne_sat(__fdiv_rn(v[c], sc));
+  for (int c = 0; c < 64; ++c) {
+    const float x = __fdiv_rn(v[c], sc);
+    codes[o + c] = kI8 ? (uint8_t)syn_int8_rne_sat(x) : syn_e4m3_rne_sat(x);
+  }
   if (t == 0) scales[blk] = sc;
 }
 
@@ -158,8 +163,20 @@ int synth_dev_fp8_bank(uint64_t seed, uint32_t tid, int64_t e0, int64_t ne, int6
   int64_t nblk = ne * (rows / 128) * (cols / 128);
   if (nblk == 0) return 0;
   if (nblk > 0x7FFFFFFF) return -1;
-  hipLaunchKernelGGL(k_fp8_bank, dim3((unsigned)nblk), dim3(kThreads), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(k_fp8_bank<false>, dim3((unsigned)nblk), dim3(kThreads), 0, (hipStream_t)stream,
                      seed, tid, e0, rows, cols, std, q, codes, scales);
+  return (int)hipGetLastError();
+}
+
+int synth_dev_int8_bank(uint64_t seed, uint32_t tid, int64_t e0, int64_t ne, int64_t rows,
+                        int64_t cols, float std, const float* q, int8_t* codes, float* scales,
+                        void* stream) {
+  if (rows % 128 || cols % 128) return -1;
+  int64_t nblk = ne * (rows / 128) * (cols / 128);
+  if (nblk == 0) return 0;
+  if (nblk > 0x7FFFFFFF) return -1;
+  hipLaunchKernelGGL(k_fp8_bank<true>, dim3((unsigned)nblk), dim3(kThreads), 0, (hipStream_t)stream,
+                     seed, tid, e0, rows, cols, std, q, reinterpret_cast<uint8_t*>(codes), scales);
   return (int)hipGetLastError();
 }
 

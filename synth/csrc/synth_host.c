@@ -29,8 +29,10 @@ typedef struct {
   uint64_t lo, hi; /* work range for this thread */
 } syn_job;
 
-enum { K_WORDS = 0, K_NORMAL_F32, K_NORMAL_BF16, K_UNIFORM_F32, K_FP8_BANK, K_MXFP4_BANK };
+enum { K_WORDS = 0, K_NORMAL_F32, K_NORMAL_BF16, K_UNIFORM_F32, K_FP8_BANK, K_MXFP4_BANK,
+       K_INT8_BANK };
 
+/* A 128 x 128 block of an E4M3 (scale amax/448) or INT8 (scale amax/127) bank. */
 static void run_fp8_block(const syn_job* j, uint64_t blk) {
   /* block index over (expert, row block, col block) of 128 x 128 */
   int64_t nrb = j->rows / 128, ncb = j->cols / 128;
@@ -52,11 +54,15 @@ static void run_fp8_block(const syn_job* j, uint64_t blk) {
       }
     }
   }
-  float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  const int i8 = j->kind == K_INT8_BANK;
+  float s = (amax == 0.0f) ? 1.0f : amax / (i8 ? 127.0f : 448.0f);
   uint8_t* codes = (uint8_t*)j->out;
   for (int r = 0; r < 128; ++r) {
     size_t o = (size_t)((e * j->rows + rb * 128 + r) * j->cols + cb * 128);
-    for (int c = 0; c < 128; ++c) codes[o + c] = syn_e4m3_rne_sat(vals[r * 128 + c] / s);
+    for (int c = 0; c < 128; ++c) {
+      const float v = vals[r * 128 + c] / s;
+      codes[o + c] = i8 ? (uint8_t)syn_int8_rne_sat(v) : syn_e4m3_rne_sat(v);
+    }
   }
   ((float*)j->out2)[blk] = s;
 }
@@ -129,6 +135,7 @@ static void* worker(void* arg) {
         ((float*)j->out)[i] = syn_uniform(j->seed, j->tid, j->start + i, j->a, j->b);
         break;
       case K_FP8_BANK:
+      case K_INT8_BANK:
         run_fp8_block(j, i);
         break;
       case K_MXFP4_BANK:
@@ -200,6 +207,16 @@ void synth_host_fp8_bank(uint64_t seed, uint32_t tid, int64_t e0, int64_t ne, in
                          int nthreads) {
   syn_job j; memset(&j, 0, sizeof j);
   j.kind = K_FP8_BANK; j.seed = seed; j.tid = tid; j.a = std; j.q = q; j.out = codes; j.out2 = scales;
+  j.e0 = e0; j.ne = ne; j.rows = rows; j.cols = cols;
+  run(j, (uint64_t)(ne * (rows / 128) * (cols / 128)), nthreads);
+}
+
+/* The same as symmetric INT8 codes (two's complement bytes) with fp32 scales amax/127. */
+void synth_host_int8_bank(uint64_t seed, uint32_t tid, int64_t e0, int64_t ne, int64_t rows,
+                          int64_t cols, float std, const float* q, int8_t* codes, float* scales,
+                          int nthreads) {
+  syn_job j; memset(&j, 0, sizeof j);
+  j.kind = K_INT8_BANK; j.seed = seed; j.tid = tid; j.a = std; j.q = q; j.out = codes; j.out2 = scales;
   j.e0 = e0; j.ne = ne; j.rows = rows; j.cols = cols;
   run(j, (uint64_t)(ne * (rows / 128) * (cols / 128)), nthreads);
 }

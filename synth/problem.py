@@ -19,7 +19,7 @@ from typing import Optional
 import numpy as np
 
 from . import (TID_BIAS, TID_ROWW, TID_W2, TID_W13, TID_WR, TID_WS2, TID_WS13, TID_X,
-               fp8_bank, mxfp4_bank, normal_bf16, normal_f32, uniform_f32)
+               fp8_bank, int8_bank, mxfp4_bank, normal_bf16, normal_f32, uniform_f32)
 from .configs import MoEConfig
 
 
@@ -50,6 +50,9 @@ class HostBank:
             return {"w": normal_f32(self.seed, tid, (rows, cols), self.std, start=start)}
         if self.fmt == "fp8":
             c, s = fp8_bank(self.seed, tid, e, 1, rows, cols, self.std)
+            return {"w": c[0], "scale": s[0]}
+        if self.fmt == "int8":
+            c, s = int8_bank(self.seed, tid, e, 1, rows, cols, self.std)
             return {"w": c[0], "scale": s[0]}
         if self.fmt in ("mxfp4", "mxfp4a4"):
             p, s = mxfp4_bank(self.seed, tid, e, 1, rows, cols, self.std)
@@ -152,16 +155,17 @@ class DevProblem:
 
 
 def _dev_bank(cfg: MoEConfig, E: int, I: int, tid13: int, tid2: int, device) -> DevBank:
-    from . import dev_fp8_bank, dev_mxfp4_bank, dev_normal
+    from . import dev_fp8_bank, dev_int8_bank, dev_mxfp4_bank, dev_normal
 
     s, H, std = cfg.weight_seed, cfg.H, cfg.w_std
     if cfg.wdt in ("bf16", "f32"):
         return DevBank(cfg.wdt, E, H, I, dev_normal(s, tid13, (E, 2 * I, H), std, cfg.wdt, device),
                        dev_normal(s, tid2, (E, H, I), std, cfg.wdt, device))
-    if cfg.wdt == "fp8":
-        c13, s13 = dev_fp8_bank(s, tid13, E, 2 * I, H, std, device)
-        c2, s2 = dev_fp8_bank(s, tid2, E, H, I, std, device)
-        return DevBank("fp8", E, H, I, c13, c2, s13, s2)
+    if cfg.wdt in ("fp8", "int8"):
+        gen = dev_fp8_bank if cfg.wdt == "fp8" else dev_int8_bank
+        c13, s13 = gen(s, tid13, E, 2 * I, H, std, device)
+        c2, s2 = gen(s, tid2, E, H, I, std, device)
+        return DevBank(cfg.wdt, E, H, I, c13, c2, s13, s2)
     if cfg.wdt in ("mxfp4", "mxfp4a4"):  # the same weights; mxfp4a4 also quantises activations
         p13, s13 = dev_mxfp4_bank(s, tid13, E, 2 * I, H, std, device)
         p2, s2 = dev_mxfp4_bank(s, tid2, E, H, I, std, device)
