@@ -105,11 +105,11 @@ def cpu_baseline(cfg, host, n_tokens):
 
 # bytes per stored element (block scales included) of each storage format
 ELEM_BYTES = {"f32": 4.0, "bf16": 2.0, "fp8": 1.0 + 4.0 / (128 * 128), "mxfp4": 0.5 + 1.0 / 32,
-              "mxfp4a4": 0.5 + 1.0 / 32}
+              "mxfp4a4": 0.5 + 1.0 / 32, "int8": 1.0 + 4.0 / (128 * 128)}
 # dense MFMA peak (TFLOP/s) of the product each weight format is computed with: MXFP4 weights
 # are decoded to bf16 in registers and multiplied on the bf16 MFMA
 MFMA_PEAK = {"f32": 157.3, "bf16": BF16_PEAK_TFLOPS, "fp8": 5000.0, "mxfp4": BF16_PEAK_TFLOPS,
-             "mxfp4a4": 10100.0}
+             "mxfp4a4": 10100.0, "int8": 5000.0}   # INT8: dense int8 TOP/s
 
 
 def ffn_accounting(cfg, touched):
@@ -124,9 +124,9 @@ def ffn_accounting(cfg, touched):
     wb = ELEM_BYTES[cfg.wdt]
     q8 = 1.0 + 4.0 / 128          # an E4M3 code plus its share of a 1 x 128 fp32 scale
     q4 = 0.5 + 1.0 / 32           # an E2M1 code plus its share of a 1 x 32 E8M0 scale
-    xb = q8 if cfg.wdt == "fp8" else (q4 if cfg.wdt == "mxfp4a4" else ELEM_BYTES[cfg.act])
-    hb = q8 if cfg.wdt == "fp8" else (q4 if cfg.wdt == "mxfp4a4" else
-                                      (4.0 if cfg.wdt == "f32" else 2.0))
+    q8w = cfg.wdt in ("fp8", "int8")   # 8-bit codes with a 1 x 128 fp32 scale
+    xb = q8 if q8w else (q4 if cfg.wdt == "mxfp4a4" else ELEM_BYTES[cfg.act])
+    hb = q8 if q8w else (q4 if cfg.wdt == "mxfp4a4" else (4.0 if cfg.wdt == "f32" else 2.0))
     h_elems = rows_r * I + (T * Is if Is else 0)
     w13 = (touched * 2 * I * H + (2 * Is * H if Is else 0)) * wb
     w2 = (touched * I * H + (Is * H if Is else 0)) * wb
@@ -134,6 +134,8 @@ def ffn_accounting(cfg, touched):
     fl_dn = 2.0 * (rows_r * I * H + (T * Is * H if Is else 0))
     if cfg.wdt == "fp8":
         kgu, kdn = "k_fp8<gate/up>", "k_fp8<down>"
+    elif cfg.wdt == "int8":
+        kgu, kdn = "k_fp8<gate/up, INT8>", "k_fp8<down, INT8>"
     elif cfg.wdt == "mxfp4" and rows_r <= 32 * cfg.E and H % 512 == 0 and I % 512 == 0:
         kgu, kdn = "k_gateup_stream_mx", "k_down_stream_mx"
     elif cfg.wdt == "mxfp4":

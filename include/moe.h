@@ -55,11 +55,16 @@ typedef enum {
   MOE_FP8_E4M3 = 2, /* OCP E4M3FN codes, with fp32 block scales */
   MOE_MXFP4 = 3,    /* OCP MX E2M1 pairs per byte (element 2i in the low nibble),
                        with E8M0 scales per 32 elements along the contiguous dimension */
-  MOE_MXFP4_A4 = 4  /* expert weights only: stored as MOE_MXFP4, and the layer quantises the
+  MOE_MXFP4_A4 = 4, /* expert weights only: stored as MOE_MXFP4, and the layer quantises the
                        activations (and the SwiGLU output) to MXFP4 too, per 1 x 32 block:
                        scale 2^(floor(log2 amax) - 2) (1 for a zero block), codes E2M1 with
                        round to nearest even, saturating at 6 -- both operands of the expert
                        GEMMs are then FP4 (W4A4) */
+  MOE_INT8 = 5      /* expert weights only: symmetric INT8 codes (two's complement) with fp32
+                       block scales; the layer quantises the activations (and the SwiGLU
+                       output) to INT8 per 1 x 128 block: scale amax / 127 (1 for a zero
+                       block), codes round-to-nearest-even of x / scale clamped to +-127 --
+                       both operands of the expert GEMMs are then INT8 (W8A8) */
 } moe_dtype;
 
 typedef enum {
@@ -75,6 +80,11 @@ typedef enum {
  * MXFP4:    w13 bytes [E, 2I, H/2], w2 bytes [E, H, I/2]; w13_scale u8 [E, 2I, H/32],
  *           w2_scale u8 [E, H, I/32] (value = e2m1 * 2^(scale - 127)). H, I multiples of 128.
  * MXFP4_A4: the MXFP4 layout; activations BF16 in, quantised inside. H, I multiples of 128.
+ * INT8:     w13 int8 [E, 2I, H], w2 int8 [E, H, I]; w13_scale f32 [E, 2I/128, H/128],
+ *           w2_scale f32 [E, H/128, I/128] (value = code * scale; the W8A8 weights of
+ *           section 3.1 of "Trillion-Parameter LLM Architecture Explained and
+ *           Cost-Efficient Inference in Practice"). Activations BF16 in, quantised inside.
+ *           H, I multiples of 128.
  * F32/BF16: no scales (NULL). H, I multiples of 64.
  * The fp8 and MXFP4 expert formats are the FP8/FP4 grouped GEMM inputs of "GC-MoE:
  * Overlapping Expert-Parallel Token Dispatch with FP8/FP4 Grouped GEMM via CUDA Green
@@ -143,9 +153,11 @@ size_t moe_grouped_ffn_workspace_size(const moe_experts* w, moe_dtype act_dt, in
  * grouped GEMM pair: h = SiLU(x Wg^T) * (x Wu^T), y = h W2^T (moe_ffn's e(x); SwiGLU and
  * the fused epilogue follow GC-MoE's grouped GEMM with fused SwiGLU).
  *   w        expert bank (see moe_experts), w->E groups.
- *   x_perm   [rows, H] act_dt: F32 with F32 weights; BF16 with BF16 / FP8_E4M3 / MXFP4 weights.
+ *   x_perm   [rows, H] act_dt: F32 with F32 weights; BF16 with every other format.
  *            With FP8_E4M3 weights, rows are quantised inside to E4M3 per 1 x 128 block
- *            (scale = amax/448) and h is re-quantised the same way before the down GEMM.
+ *            (scale = amax/448) and h is re-quantised the same way before the down GEMM;
+ *            with INT8 weights, to INT8 per 1 x 128 block (scale = amax/127), likewise;
+ *            with MXFP4_A4 weights, to MXFP4 per 1 x 32 block.
  *   offsets  [E+1] int32 device array, offsets[0] = 0, non-decreasing, offsets[E] = rows.
  *   y_perm   [rows, H] y_dt (F32 or BF16; F32 keeps the expert outputs unrounded until the
  *            combine, as moe_layer_forward does).
@@ -264,6 +276,14 @@ moe_status moe_rows_forward_timed(const moe_experts* w, const void* x, moe_dtype
  *   x [n, H] BF16; q [n, H] u8 codes; q_scale [n, H/128] f32. H a multiple of 128. */
 moe_status moe_quantize_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* q_scale,
                             void* stream);
+
+/* Per 1 x 128 block INT8 quantisation of activation rows, as the W8A8 expert path
+ * (MOE_INT8) applies it to its inputs and to the SwiGLU output: scale = fp32(amax / 127) per
+ * block of 128 consecutive elements of a row (1 for an all-zero block); code = round to
+ * nearest even of fp32(x / scale), clamped to [-127, 127].
+ *   x [n, H] BF16; q [n, H] int8 codes; q_scale [n, H/128] f32. H a multiple of 128. */
+moe_status moe_quantize_int8(const void* x, int32_t n, int32_t H, int8_t* q, float* q_scale,
+                             void* stream);
 
 /* ---------------------------------------------------------------- bias balancing */
 

@@ -19,11 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 # enums of moe.h
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(7)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP4_A4 = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP4_A4, MOE_INT8 = range(6)
 MOE_SOFTMAX, MOE_SIGMOID = range(2)
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4,
-          "mxfp4a4": MOE_MXFP4_A4}
+          "mxfp4a4": MOE_MXFP4_A4, "int8": MOE_INT8}
 SCORES = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}
 
 
@@ -56,7 +56,7 @@ EXPORTS = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size"
            "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_layer_forward_overlap", "moe_layer_forward_noalloc",
            "moe_rows_workspace_size",
-           "moe_rows_forward", "moe_rows_forward_timed", "moe_quantize_fp8", "moe_quantize_mxfp4", "moe_bias_update",
+           "moe_rows_forward", "moe_rows_forward_timed", "moe_quantize_fp8", "moe_quantize_mxfp4", "moe_quantize_int8", "moe_bias_update",
            "moe_status_str",
            "moe_last_hip_error"]
 
@@ -101,6 +101,8 @@ def lib():
         getattr(L, f).restype = ci
     L.moe_quantize_fp8.argtypes = [vp, i32, i32, vp, vp, vp]
     L.moe_quantize_fp8.restype = ci
+    L.moe_quantize_int8.argtypes = [vp, i32, i32, vp, vp, vp]
+    L.moe_quantize_int8.restype = ci
     L.moe_quantize_mxfp4.argtypes = [vp, i32, i32, vp, vp, vp]
     L.moe_quantize_mxfp4.restype = ci
     L.moe_bias_update.argtypes = [vp, i32, f32, vp, vp]
@@ -333,6 +335,12 @@ def moe_quantize_fp8(x, q, q_scale, stream=None):
     n, H = x.shape
     st = lib().moe_quantize_fp8(_ptr(x), n, H, _ptr(q), _ptr(q_scale), _stream(stream))
     _check(st, "moe_quantize_fp8")
+
+
+def moe_quantize_int8(x, q, q_scale, stream=None):
+    n, H = x.shape
+    st = lib().moe_quantize_int8(_ptr(x), n, H, _ptr(q), _ptr(q_scale), _stream(stream))
+    _check(st, "moe_quantize_int8")
 
 
 def moe_quantize_mxfp4(x, q, q_scale, stream=None):

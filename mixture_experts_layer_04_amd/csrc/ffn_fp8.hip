@@ -14,6 +14,13 @@
 //  - gate/up epilogue: h = SiLU(g) * u in fp32, per-token amax over the workgroup's 128
 //    features (wavefront shuffles, then LDS across wavefronts), scale = amax / 448,
 //    E4M3 codes of h / scale -- exactly one 1 x 128 quantisation block per workgroup.
+//
+// INT8 (W8A8, the weight and activation quantisation of section 3.1 of "Trillion-Parameter
+// LLM Architecture Explained and Cost-Efficient Inference in Practice"): the same kernel
+// with INT8 codes and scales amax / 127 (round to nearest even, clamped to +-127). Each
+// 128-wide K block of a 16 x 16 tile is two v_mfma_i32_16x16x64_i8 (exact int32 sums, at
+// most 128 * 127^2 < 2^24 in magnitude, so exact in fp32 as well), converted to fp32 and
+// then scaled as the fp8 partials are.
 #include "ffn_common.h"
 
 namespace moe {
@@ -43,6 +50,20 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | (code > 0x7Eu ? 0x7Eu : code);
 }
 
+// fp32 (already divided by its scale) -> symmetric INT8 code byte: nearest integer, ties to
+// even, clamped to [-127, 127].
+__device__ __forceinline__ uint32_t int8_code(float v) {
+  const float r = fminf(fmaxf(__builtin_rintf(v), -127.0f), 127.0f);
+  return (uint32_t)(int32_t)r & 0xFFu;
+}
+
+// A block code of the format: INT8 or E4M3.
+template <bool kI8>
+__device__ __forceinline__ uint32_t q8_code(float v) { return kI8 ? int8_code(v) : e4m3_code(v); }
+// The largest code magnitude of the format: the block scale is amax / this.
+template <bool kI8>
+constexpr float q8_max() { return kI8 ? 127.0f : 448.0f; }
+
 __device__ __forceinline__ float wave_max16(float v) {  // max over lanes with equal l % 16
   v = fmaxf(v, __shfl_xor(v, 16, 64));
   v = fmaxf(v, __shfl_xor(v, 32, 64));
@@ -51,7 +72,8 @@ __device__ __forceinline__ float wave_max16(float v) {  // max over lanes with e
 
 // Quantise rows of a bf16 [n, H] matrix: one workgroup per (row, 16 blocks of 1 x 128), 16
 // lanes per block (a workgroup per 2048 elements, so that every row's loads are in flight
-// at once).
+// at once). kI8: INT8 codes, else E4M3.
+template <bool kI8>
 __global__ void __launch_bounds__(256) k_quant_rows_fp8(const uint16_t* __restrict__ x, int H,
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ qs) {
@@ -74,20 +96,41 @@ __global__ void __launch_bounds__(256) k_quant_rows_fp8(const uint16_t* __restri
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 16));
     if (b < nblk) {
-      const float sc = am == 0.0f ? 1.0f : __fdiv_rn(am, 448.0f);
+      const float sc = am == 0.0f ? 1.0f : __fdiv_rn(am, q8_max<kI8>());
       uint2 c;
-      c.x = e4m3_code(__fdiv_rn(v[0], sc)) | (e4m3_code(__fdiv_rn(v[1], sc)) << 8) |
-            (e4m3_code(__fdiv_rn(v[2], sc)) << 16) | (e4m3_code(__fdiv_rn(v[3], sc)) << 24);
-      c.y = e4m3_code(__fdiv_rn(v[4], sc)) | (e4m3_code(__fdiv_rn(v[5], sc)) << 8) |
-            (e4m3_code(__fdiv_rn(v[6], sc)) << 16) | (e4m3_code(__fdiv_rn(v[7], sc)) << 24);
+      c.x = q8_code<kI8>(__fdiv_rn(v[0], sc)) | (q8_code<kI8>(__fdiv_rn(v[1], sc)) << 8) |
+            (q8_code<kI8>(__fdiv_rn(v[2], sc)) << 16) | (q8_code<kI8>(__fdiv_rn(v[3], sc)) << 24);
+      c.y = q8_code<kI8>(__fdiv_rn(v[4], sc)) | (q8_code<kI8>(__fdiv_rn(v[5], sc)) << 8) |
+            (q8_code<kI8>(__fdiv_rn(v[6], sc)) << 16) | (q8_code<kI8>(__fdiv_rn(v[7], sc)) << 24);
       *reinterpret_cast<uint2*>(q + row * H + b * 128 + j * 8) = c;
       if (j == 0) qs[row * nblk + b] = sc;
     }
   }
 }
 
-// kYF32 (down only): expert outputs stored as fp32, else rounded once to bf16.
-template <bool kGateUp, bool kYF32>
+// The unscaled product of one 128-wide K block of a 16 x 16 tile: each lane holds 32 bytes
+// of codes of both operands. E4M3: one scaled MFMA with unit E8M0 scales (exact). INT8: two
+// int32 MFMAs over the lane's first and second 16 bytes (the same K slots in both
+// operands), summed exactly in int32 and converted to fp32 exactly.
+template <bool kI8>
+__device__ __forceinline__ f32x4 block_product(const i32x8& w, const i32x8& x) {
+  if constexpr (kI8) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 w0 = {w[0], w[1], w[2], w[3]}, w1 = {w[4], w[5], w[6], w[7]};
+    const i32x4 x0 = {x[0], x[1], x[2], x[3]}, x1 = {x[4], x[5], x[6], x[7]};
+    i32x4 p = {0, 0, 0, 0};
+    p = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, x0, p, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, x1, p, 0, 0, 0);
+    return f32x4{(float)p[0], (float)p[1], (float)p[2], (float)p[3]};
+  } else {
+    const f32x4 z = {0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, z, 0, 0, 0, 127, 0, 127);
+  }
+}
+
+// kYF32 (down only): expert outputs stored as fp32, else rounded once to bf16. kI8: INT8
+// weights and activations (W8A8), else E4M3.
+template <bool kGateUp, bool kYF32, bool kI8>
 __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   // Each K block of the workgroup's operands -- its 128 (down) or 256 (gate/up) weight
   // rows, the tile's 128 activation rows (both in the full-rate layout of lds_off) and the
@@ -220,13 +263,12 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
         xb[0] = x0[0]; xb[1] = x0[1]; xb[2] = x0[2]; xb[3] = x0[3];
         xb[4] = x1[0]; xb[5] = x1[1]; xb[6] = x1[2]; xb[7] = x1[3];
         const float sx = *reinterpret_cast<const float*>(st + WB + ACT + t * 128 + m16 * 4);
-        const f32x4 z = {0, 0, 0, 0};
-        f32x4 p0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, z, 0, 0, 0, 127, 0, 127);
+        const f32x4 p0 = block_product<kI8>(wa, xb);
         const float c0 = sw0 * sx;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc0[t][i] += p0[i] * c0;
         if (kGateUp) {
-          f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb, xb, z, 0, 0, 0, 127, 0, 127);
+          const f32x4 p1 = block_product<kI8>(wb, xb);
           const float c1 = sw1 * sx;
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc1[t][i] += p1[i] * c1;
@@ -269,10 +311,10 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
       float am = 0.0f;
 #pragma unroll
       for (int w = 0; w < 8; ++w) am = fmaxf(am, red[w][tok]);
-      const float sc = am == 0.0f ? 1.0f : __fdiv_rn(am, 448.0f);
+      const float sc = am == 0.0f ? 1.0f : __fdiv_rn(am, q8_max<kI8>());
       uint32_t c = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c |= e4m3_code(__fdiv_rn(acc0[t][i], sc)) << (8 * i);
+      for (int i = 0; i < 4; ++i) c |= q8_code<kI8>(__fdiv_rn(acc0[t][i], sc)) << (8 * i);
       const int64_t row = tl.row0 + tok;
       *reinterpret_cast<uint32_t*>(hq + row * a.I_max + fw + 4 * g) = c;
       if (wave == 0 && g == 0) a.h_scale[row * (a.I_max / kF8K) + f0 / kF8K] = sc;
@@ -298,24 +340,39 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
 
 }  // namespace
 
-hipError_t launch_ffn_fp8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
+namespace {
+template <bool kI8>
+hipError_t launch_q8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
   const int nb_gu = a.I_max / kF8Feat, nb_dn = a.H / kF8Feat;
-  hipLaunchKernelGGL((k_fp8<true, true>), dim3(a.max_tiles * nb_gu), dim3(512), 0, s, a, nb_gu);
+  hipLaunchKernelGGL((k_fp8<true, true, kI8>), dim3(a.max_tiles * nb_gu), dim3(512), 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
   if (a.y_dt == MOE_F32)
-    hipLaunchKernelGGL((k_fp8<false, true>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_fp8<false, true, kI8>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
   else
-    hipLaunchKernelGGL((k_fp8<false, false>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_fp8<false, false, kI8>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_ffn_fp8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
+  return a.wdt == MOE_INT8 ? launch_q8<true>(a, s, mid_event) : launch_q8<false>(a, s, mid_event);
 }
 
 hipError_t launch_quant_rows_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* qs,
                                  hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quant_rows_fp8, dim3(n, (H / 128 + 15) / 16), dim3(256), 0, s,
+  hipLaunchKernelGGL(k_quant_rows_fp8<false>, dim3(n, (H / 128 + 15) / 16), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t*>(x), H, q, qs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_int8(const void* x, int32_t n, int32_t H, int8_t* q, float* qs,
+                                  hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_rows_fp8<true>, dim3(n, (H / 128 + 15) / 16), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(x), H, reinterpret_cast<uint8_t*>(q), qs);
   return hipGetLastError();
 }
 

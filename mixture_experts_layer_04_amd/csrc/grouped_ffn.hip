@@ -10,8 +10,9 @@
 // rows of one group. Launch grids use a host-side upper bound on the tile count; surplus
 // workgroups exit at once, so no host synchronisation is needed.
 //
-// Three kernel families, chosen per call: streaming kernels (ffn_stream.hip), the
-// LDS-tiled bf16 / MXFP4 kernel (ffn_tiled.hip) and the fp8 kernel (ffn_fp8.hip).
+// Kernel families, chosen per call: streaming kernels (ffn_stream.hip), the LDS-tiled bf16 /
+// MXFP4 kernel (ffn_tiled.hip), the fp8 / INT8 kernel (ffn_fp8.hip) and the W4A4 kernel
+// (ffn_w4a4.hip).
 #include "ffn_common.h"
 
 namespace moe {
@@ -20,7 +21,8 @@ bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I) {
   switch (wdt) {
     case MOE_F32:
     case MOE_BF16: return H % 64 == 0 && I % 64 == 0;
-    case MOE_FP8_E4M3: return H % kF8Feat == 0 && I % kF8Feat == 0;
+    case MOE_FP8_E4M3:
+    case MOE_INT8: return H % kF8Feat == 0 && I % kF8Feat == 0;
     // the tiled kernel's weight-row blocks, and dword-aligned scale bytes of every row
     case MOE_MXFP4: return H % kTiledN == 0 && I % 128 == 0;
     // 128-element K blocks of the FP4 instruction
@@ -31,7 +33,7 @@ bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I) {
 
 int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32_t I_routed,
                    int32_t I_shared) {
-  if (wdt == MOE_FP8_E4M3) return kF8TileM;
+  if (wdt == MOE_FP8_E4M3 || wdt == MOE_INT8) return kF8TileM;
   if (wdt == MOE_MXFP4_A4) return kTiledM;
   // MXFP4: streaming kernels for few rows per expert where the shapes allow, else tiled
   if (wdt == MOE_MXFP4)
@@ -54,7 +56,7 @@ int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32
 
 size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_max) {
   (void)H;
-  if (wdt == MOE_FP8_E4M3) {
+  if (wdt == MOE_FP8_E4M3 || wdt == MOE_INT8) {
     const size_t q = ((size_t)rows_total * I_max + 255) / 256 * 256;
     return q + ((size_t)rows_total * (I_max / kF8K) * sizeof(float) + 255) / 256 * 256;
   }
@@ -76,7 +78,7 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
     return mid_event ? hipEventRecord(mid_event, s) : hipSuccess;
   }
   a.h = scratch;
-  if (a.wdt == MOE_FP8_E4M3) {
+  if (a.wdt == MOE_FP8_E4M3 || a.wdt == MOE_INT8) {
     a.h_scale = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) +
                                          ((size_t)a.rows_total * a.I_max + 255) / 256 * 256);
     return launch_ffn_fp8(a, s, mid_event);

@@ -34,6 +34,7 @@ moe_status check_bank(const moe_experts* w, int32_t H, bool need_scales) {
     case MOE_BF16:
       break;
     case MOE_FP8_E4M3:
+    case MOE_INT8:
     case MOE_MXFP4:
     case MOE_MXFP4_A4:
       if (need_scales && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_NULL;
@@ -51,7 +52,8 @@ moe_status check_bank(const moe_experts* w, int32_t H, bool need_scales) {
 // Activation dtype that goes with a weight dtype.
 bool act_ok(moe_dtype act, moe_dtype wdt) {
   if (wdt == MOE_F32) return act == MOE_F32;
-  if (wdt == MOE_BF16 || wdt == MOE_FP8_E4M3 || wdt == MOE_MXFP4 || wdt == MOE_MXFP4_A4)
+  if (wdt == MOE_BF16 || wdt == MOE_FP8_E4M3 || wdt == MOE_MXFP4 || wdt == MOE_MXFP4_A4 ||
+      wdt == MOE_INT8)
     return act == MOE_BF16;
   return false;
 }
@@ -93,13 +95,13 @@ void plan_ffn(Carve& c, FfnPlan& p, moe_dtype wdt, moe_dtype act, int32_t H, int
   if (need_y) p.o_y = c.take((size_t)p.rows_total * H * dt_bytes(p.y_dt));
 }
 
-// Staging of quantised activations: fp8 (E4M3 codes [rows, H], fp32 scales [rows, H/128])
-// or W4A4 (E2M1 codes [rows, H/2], E8M0 scales [rows, H/32]).
+// Staging of quantised activations: fp8 or INT8 (codes [rows, H], fp32 scales
+// [rows, H/128]) or W4A4 (E2M1 codes [rows, H/2], E8M0 scales [rows, H/32]).
 struct QPlan {
   size_t o_q = 0, o_qs = 0;
 };
 void plan_quant(Carve& c, QPlan& q, moe_dtype wdt, int32_t rows, int32_t H) {
-  if (wdt == MOE_FP8_E4M3) {
+  if (wdt == MOE_FP8_E4M3 || wdt == MOE_INT8) {
     q.o_q = c.take((size_t)rows * H);
     q.o_qs = c.take((size_t)rows * (H / 128) * sizeof(float));
   } else if (wdt == MOE_MXFP4_A4) {
@@ -110,9 +112,12 @@ void plan_quant(Carve& c, QPlan& q, moe_dtype wdt, int32_t rows, int32_t H) {
 // Quantises the rows of x for the expert GEMMs (if the format needs it) and points f at them.
 hipError_t quantise_acts(moe_dtype wdt, const void* x, int32_t rows, int32_t H, char* base,
                          const QPlan& q, FfnArgs& f, hipStream_t s) {
-  if (wdt == MOE_FP8_E4M3) {
+  if (wdt == MOE_FP8_E4M3 || wdt == MOE_INT8) {
     f.a_q = reinterpret_cast<const uint8_t*>(base + q.o_q);
     f.a_qscale = reinterpret_cast<const float*>(base + q.o_qs);
+    if (wdt == MOE_INT8)
+      return launch_quant_rows_int8(x, rows, H, reinterpret_cast<int8_t*>(base + q.o_q),
+                                    reinterpret_cast<float*>(base + q.o_qs), s);
     return launch_quant_rows_fp8(x, rows, H, reinterpret_cast<uint8_t*>(base + q.o_q),
                                  reinterpret_cast<float*>(base + q.o_qs), s);
   }
@@ -659,6 +664,18 @@ moe_status moe_quantize_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, flo
   if (!al16(x) || !al16(q) || !al16(q_scale)) return MOE_ERR_ALIGN;
   hipError_t e = launch_quant_rows_fp8(x, n, H, q, q_scale, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_fp8");
+}
+
+// ------------------------------------------------------------- INT8 quantiser
+
+moe_status moe_quantize_int8(const void* x, int32_t n, int32_t H, int8_t* q, float* q_scale,
+                             void* stream) {
+  if (n < 0 || H < 128 || H % 128) return MOE_ERR_SHAPE;
+  if (n == 0) return MOE_OK;
+  if (!x || !q || !q_scale) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(q) || !al16(q_scale)) return MOE_ERR_ALIGN;
+  hipError_t e = launch_quant_rows_int8(x, n, H, q, q_scale, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_int8");
 }
 
 // ------------------------------------------------------------- bias balancing

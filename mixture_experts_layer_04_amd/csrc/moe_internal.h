@@ -78,13 +78,14 @@ struct FfnArgs {
   // map(r) = a_rowmap ? a_rowmap[r] : r
   const void* a;
   const int32_t* a_rowmap;
-  // fp8 path: activations pre-quantised to E4M3 (a_q, [*, H]) with fp32 scales [*, H/128]
+  // fp8 / INT8 paths: activations pre-quantised to E4M3 or INT8 (a_q, [*, H]) with fp32
+  // scales [*, H/128]
   const uint8_t* a_q;
   const float* a_qscale;
   // W4A4 path: activations as E2M1 codes (a_q, [*, H/2]) with E8M0 scales [*, H/32]
   const uint8_t* a_xs;
-  void* h;                // [rows_total, I_max] intermediate (bf16, f32, or fp8 + scales)
-  float* h_scale;         // fp8 path: [rows_total, I_max/128]
+  void* h;                // [rows_total, I_max] intermediate (bf16, f32, or fp8/int8 + scales)
+  float* h_scale;         // fp8 / INT8 paths: [rows_total, I_max/128]
   uint8_t* h_xs;          // W4A4 path: E8M0 scales of h [rows_total, I_max/32] (codes in h)
   uint8_t* h_lo;          // bf16 banks: MXFP4 codes of h's residual [rows_total, I_max/2]
   uint8_t* h_lo_s;        //   and their E8M0 scales [rows_total, lo_sstride(I_max)]
@@ -140,6 +141,9 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s,
 // fp8 path: per 1 x 128 block E4M3 quantisation of rows of a [n, H] bf16 matrix.
 hipError_t launch_quant_rows_fp8(const void* x, int32_t n, int32_t H, uint8_t* q, float* qs,
                                  hipStream_t s);
+// W8A8 path: per 1 x 128 block INT8 quantisation of rows of a [n, H] bf16 matrix.
+hipError_t launch_quant_rows_int8(const void* x, int32_t n, int32_t H, int8_t* q, float* qs,
+                                  hipStream_t s);
 // W4A4 path: per 1 x 32 block MXFP4 quantisation of rows of a [n, H] bf16 matrix.
 hipError_t launch_quant_rows_mxfp4(const void* x, int32_t n, int32_t H, uint8_t* q, uint8_t* qs,
                                    hipStream_t s);

@@ -12,11 +12,13 @@ import mixture_experts_layer_04_amd as moe
 from synth.configs import MoEConfig
 from synth.problem import DevProblem, device_problem, host_problem
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2, "mxfp4": 6e-2, "mxfp4a4": 6e-2}
+# the stated tolerances; INT8 (W8A8) takes the low-precision one of fp8 / MXFP4
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2, "mxfp4": 6e-2, "mxfp4a4": 6e-2, "int8": 6e-2}
 
 # rows per tile of the grouped FFN kernels the library picks at each full-size workload
 TILE_ROWS = {"r1_decode": 16, "r1_decode_fp8": 128, "r1_decode_mxfp4": 16, "r1_prefill": 256,
-             "e384_fp8": 128, "ep32_mxfp4": 128, "ep32_w4a4": 128}
+             "e384_fp8": 128, "ep32_mxfp4": 128, "ep32_w4a4": 128, "r1_decode_int8": 128,
+             "r1_prefill_int8": 128}
 
 
 def experts(bank) -> moe.Experts:

@@ -64,6 +64,7 @@ FFN_CASES = [
     ("bf16_tiled256", "bf16", 512, 256, 3, 900),         # 256-row tiles
     ("f32_stream", "f32", 128, 64, 6, 50),
     ("fp8", "fp8", 256, 256, 5, 400),
+    ("int8", "int8", 384, 256, 5, 400),
     ("mxfp4_stream", "mxfp4", 512, 512, 6, 40),          # H, I multiples of 512, few rows
     ("mxfp4_tiled", "mxfp4", 256, 128, 4, 600),
     ("w4a4", "mxfp4a4", 256, 128, 4, 500),
@@ -88,11 +89,13 @@ def test_grouped_ffn_alone(case, y_dt):
     x64 = O.decode_act(act, host.x)
     if wdt == "fp8":
         a = O.quantise_rows_e4m3(x64.astype(np.float32))[2]
+    elif wdt == "int8":
+        a = O.quantise_rows_int8(x64.astype(np.float32))[2]
     elif wdt == "mxfp4a4":
         a = O.quantise_rows_mxfp4(x64.astype(np.float32))[2]
     else:
         a = x64
-    requant = {"fp8": True, "mxfp4a4": "mxfp4"}.get(wdt, False)
+    requant = {"fp8": True, "int8": "int8", "mxfp4a4": "mxfp4"}.get(wdt, False)
     want = np.zeros((rows, H))
     for e in range(E):
         r0, r1 = offsets[e], offsets[e + 1]
