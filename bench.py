@@ -43,6 +43,10 @@ def parse():
                     help="skip the prefill-sized batch timed after a decode workload")
     ap.add_argument("--overlap", action="store_true",
                     help="also time the step with the shared expert on a side stream")
+    ap.add_argument("--split", action="store_true",
+                    help="also time moe_layer_forward_split (groups of few rows on a second "
+                         "stream), with and without disjoint CU masks, on the named workload "
+                         "(the prefill batch timed after a decode workload always gets it)")
     ap.add_argument("--cpu-tokens", type=int, default=72,
                     help="tokens of the batch the CPU oracle leg computes (about 10 s of CPU work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -303,6 +307,36 @@ def run_workload(cfg, dev, args, overlap=False):
     }
 
 
+def time_split(cfg, dev, args):
+    """ms/step of moe_layer_forward_split for a few cold-row thresholds, on two plain streams
+    and on streams with disjoint CU masks (a quarter of the CUs for the cold groups); host
+    clock around K steps on the split streams, which torch's events do not see."""
+    import torch
+
+    import mixture_experts_layer_04_amd as moe
+
+    layer = moe.MoELayer.from_problem(cfg, dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {}
+    for masked in (False, True):
+        ss = moe.SplitStreams(*moe.cu_masks(n_cu)) if masked else moe.SplitStreams()
+        for cold_max in (32, 64, 128):
+            for _ in range(args.warmup):
+                moe.moe_layer_forward_split(layer.desc, dev.x, out, layer.ws, ss, cold_max)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                moe.moe_layer_forward_split(layer.desc, dev.x, out, layer.ws, ss, cold_max)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) / args.steps * 1e3
+            key = f"{'cu_masked' if masked else 'shared_cus'}_cold_le_{cold_max}"
+            res[key] = ms
+            log(f"{cfg.name}: split {key}: {ms:.4f} ms/step")
+        del ss
+    return res
+
+
 def describe(cfg):
     return (f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} top-{cfg.k} I={cfg.I} {cfg.score}"
             f"{' + selection bias' if cfg.use_bias else ''} scale {cfg.scale}"
@@ -328,6 +362,7 @@ def main():
     dev = device_problem(cfg, host=host)
     T = cfg.T
     r = run_workload(cfg, dev, args, overlap=args.overlap)
+    split = time_split(cfg, dev, args) if args.split and cfg.routed and cfg.wdt == "bf16" else None
 
     # the selection-bias balancing step (not part of the forward step): its own timing
     bias_us = None
@@ -354,7 +389,9 @@ def main():
             f"(expert banks shared with {cfg.name})")
         pdev = device_problem(pcfg, banks_of=dev)
         p = run_workload(pcfg, pdev, args)
+        psplit = time_split(pcfg, pdev, args)
         prefill = {"workload": describe(pcfg), "tokens": pcfg.T, "ms_per_step": p["ms"],
+                   "ms_per_step_split": psplit,
                    "tokens_per_s": pcfg.T / (p["ms"] / 1e3), "experts_touched": p["touched"],
                    "stage_ms": {s_: round(v, 5) for s_, v in p["stage_ms"].items()},
                    "step_ms_p10_p50_p90": p["step_ms_p10_p50_p90"],
@@ -402,6 +439,7 @@ def main():
                    "down_frac": r["down_frac"],
                    "bias_update_us": bias_us,
                    "ms_per_step_shared_overlapped": r["ovl_ms"],
+                   "ms_per_step_split": split,
                    "prefill": prefill},
         "roofline": r["roofline"],
         "cpu_baseline": cpu,

@@ -219,6 +219,30 @@ moe_status moe_layer_forward_overlap(const moe_layer_desc* d, const void* x, voi
                                      float* logits_out, void* ws, size_t ws_bytes, void* stream,
                                      void* side_stream, void* fork_event, void* join_event);
 
+/* moe_layer_forward with the routed and shared groups split by size over two streams: groups
+ * with at most cold_rows_max rows in this batch (expert weights to stream, few rows to
+ * multiply: HBM-bound work) run the grouped FFN's streaming kernels on cold_stream, the others
+ * (many rows: MFMA-bound work) the kernels moe_layer_forward picks for the batch, on `stream`
+ * -- so that the two kinds of tiles overlap, each on the compute units its stream may use
+ * (the single-GPU counterpart of the green-context partition and the concurrent
+ * dispatch/GEMM graph of "GC-MoE: Overlapping Expert-Parallel Token Dispatch with FP8/FP4
+ * Grouped GEMM via CUDA Green Contexts", key_changes, first and second items; a caller can
+ * create the two streams with disjoint CU masks, hipExtStreamCreateWithCUMask).
+ * Same arguments, checks and workspace size as moe_layer_forward, plus:
+ *   cold_stream  a hipStream_t other than `stream`;
+ *   fork_event, join_event  caller hipEvent_t (MOE_ERR_NULL if NULL): cold_stream waits for
+ *                `stream` after the permutation, `stream` for cold_stream before the combine;
+ *   cold_rows_max  >= 0 (MOE_ERR_SHAPE otherwise); 0 sends nothing to cold_stream.
+ * BF16 expert banks only (MOE_ERR_DTYPE otherwise). Routing is identical to
+ * moe_layer_forward's; the cold groups' outputs come from the streaming kernels instead of
+ * the tiled ones (the same arithmetic in another summation order). Only events are recorded
+ * and waited on, so the pair of streams can be captured into a HIP graph. */
+moe_status moe_layer_forward_split(const moe_layer_desc* d, const void* x, void* out,
+                                   int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                                   float* logits_out, void* ws, size_t ws_bytes, void* stream,
+                                   void* cold_stream, void* fork_event, void* join_event,
+                                   int32_t cold_rows_max);
+
 /* moe_layer_forward with stage timing: `events` points to MOE_STAGE_EVENTS hipEvent_t
  * handles created by the caller (hipEventCreate); they are recorded on `stream` at the
  * stage boundaries  [0] route [1] permute [2] gate/up+SwiGLU [3] down [4] combine [5],

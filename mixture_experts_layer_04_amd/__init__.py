@@ -54,7 +54,7 @@ _lib = None
 EXPORTS = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
            "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_timed",
-           "moe_layer_forward_overlap", "moe_layer_forward_noalloc",
+           "moe_layer_forward_overlap", "moe_layer_forward_noalloc", "moe_layer_forward_split",
            "moe_rows_workspace_size",
            "moe_rows_forward", "moe_rows_forward_timed", "moe_quantize_fp8", "moe_quantize_mxfp4", "moe_quantize_int8", "moe_bias_update",
            "moe_status_str",
@@ -88,6 +88,8 @@ def lib():
     L.moe_layer_forward_overlap.argtypes = [P(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                             vp, vp, vp]
     L.moe_layer_forward_noalloc.argtypes = [P(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp]
+    L.moe_layer_forward_split.argtypes = [P(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                          vp, vp, vp, i32]
     L.moe_rows_workspace_size.argtypes = [P(moe_experts), ci, i32]
     L.moe_rows_workspace_size.restype = sz
     L.moe_rows_forward.argtypes = [P(moe_experts), vp, ci, vp, vp, i32, vp, ci, vp, sz, vp]
@@ -95,7 +97,7 @@ def lib():
                                          P(vp)]
     for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
               "moe_layer_forward", "moe_layer_forward_timed", "moe_layer_forward_overlap",
-              "moe_layer_forward_noalloc",
+              "moe_layer_forward_noalloc", "moe_layer_forward_split",
               "moe_rows_forward",
               "moe_rows_forward_timed"):
         getattr(L, f).restype = ci
@@ -329,6 +331,73 @@ def moe_layer_forward_overlap(desc: moe_layer_desc, x, out, ws, fj: ForkJoin, to
                                          ws.numel(), _stream(stream), _stream(fj.side), fj.ev[0],
                                          fj.ev[1])
     _check(st, "moe_layer_forward_overlap")
+
+
+class SplitStreams:
+    """Two HIP streams and a fork/join event pair for moe_layer_forward_split. With CU masks
+    (lists of 32-bit words, bit i = compute unit i) the streams are created with
+    hipExtStreamCreateWithCUMask, so the hot and cold groups run on disjoint compute units;
+    without, they share all of them. Both streams keep the default priority."""
+
+    def __init__(self, hot_mask=None, cold_mask=None):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        vpp = ctypes.POINTER(ctypes.c_void_p)
+        self.hip.hipStreamCreate.argtypes = [vpp]
+        self.hip.hipExtStreamCreateWithCUMask.argtypes = [vpp, ctypes.c_uint32,
+                                                          ctypes.POINTER(ctypes.c_uint32)]
+        self.hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventCreateWithFlags.argtypes = [vpp, ctypes.c_uint]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.streams, self.ev = [], []
+        for mask in (hot_mask, cold_mask):
+            h = ctypes.c_void_p()
+            if mask is None:
+                rc = self.hip.hipStreamCreate(ctypes.byref(h))
+            else:
+                words = (ctypes.c_uint32 * len(mask))(*mask)
+                rc = self.hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), len(mask), words)
+            if rc != 0:
+                raise RuntimeError(f"stream creation failed ({rc})")
+            self.streams.append(h)
+        for _ in range(2):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(h), 0x2) != 0:  # timing disabled
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(h)
+        self.hot, self.cold = self.streams
+
+    def __del__(self):
+        try:
+            for h in self.ev:
+                self.hip.hipEventDestroy(h)
+            for h in self.streams:
+                self.hip.hipStreamDestroy(h)
+        except Exception:
+            pass
+
+
+def cu_masks(n_cu: int, cold_share: int = 4):
+    """Disjoint CU masks: every cold_share-th group of 8 consecutive CUs for the cold stream,
+    the rest for the hot one (whichever way CU numbers map to XCDs -- interleaved or in
+    blocks of 32 -- each XCD gets the same split)."""
+    hot = [0] * ((n_cu + 31) // 32)
+    cold = list(hot)
+    for i in range(n_cu):
+        m = cold if (i // 8) % cold_share == cold_share - 1 else hot
+        m[i // 32] |= 1 << (i % 32)
+    return hot, cold
+
+
+def moe_layer_forward_split(desc: moe_layer_desc, x, out, ws, ss: SplitStreams, cold_rows_max: int,
+                            topk_idx=None, topk_w=None, counts=None, logits=None):
+    """The layer on ss.hot (route, permute, hot groups, combine) and ss.cold (groups of at most
+    cold_rows_max rows). The caller orders ss.hot after the producers of x and before the
+    consumers of out (e.g. by synchronising)."""
+    st = lib().moe_layer_forward_split(ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(topk_idx),
+                                       _ptr(topk_w), _ptr(counts), _ptr(logits), _ptr(ws),
+                                       ws.numel(), ss.hot, ss.cold, ss.ev[0], ss.ev[1],
+                                       int(cold_rows_max))
+    _check(st, "moe_layer_forward_split")
 
 
 def moe_quantize_fp8(x, q, q_scale, stream=None):

@@ -54,6 +54,8 @@ int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32
   return kStreamTileM;
 }
 
+int32_t ffn_stream_tile_rows() { return kStreamTileM; }
+
 size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_max) {
   (void)H;
   if (wdt == MOE_FP8_E4M3 || wdt == MOE_INT8) {

@@ -137,6 +137,9 @@ struct LayerPlan {
   // the shared group's own tile list, for the launch that runs beside the routed experts
   size_t o_sh_tiles = 0, o_sh_ntiles = 0;
   int32_t sh_max_tiles = 0;
+  // the streaming kernels' tile list of the groups moe_layer_forward_split runs beside the rest
+  size_t o_cold_tiles = 0, o_cold_ntiles = 0;
+  int32_t cold_max_tiles = 0;
   FfnPlan ffn;
   size_t total = 0;
 };
@@ -164,6 +167,9 @@ LayerPlan plan_layer(const moe_layer_desc* d) {
     p.o_sh_tiles = c.take((size_t)(p.sh_max_tiles > 0 ? p.sh_max_tiles : 1) * sizeof(Tile));
     p.o_sh_ntiles = c.take(sizeof(int32_t));
   }
+  p.cold_max_tiles = (int32_t)max_tiles(rows + (shared ? T : 0), E + 1, ffn_stream_tile_rows());
+  p.o_cold_tiles = c.take((size_t)p.cold_max_tiles * sizeof(Tile));
+  p.o_cold_ntiles = c.take(sizeof(int32_t));
   p.total = c.off;
   return p;
 }
@@ -490,6 +496,77 @@ moe_status moe_layer_forward_overlap(const moe_layer_desc* d, const void* x, voi
   const SideStream side{(hipStream_t)side_stream, (hipEvent_t)fork_event, (hipEvent_t)join_event};
   return layer_forward(d, x, out, topk_idx_out, topk_w_out, counts_out, logits_out, ws, ws_bytes,
                        stream, nullptr, &side);
+}
+
+moe_status moe_layer_forward_split(const moe_layer_desc* d, const void* x, void* out,
+                                   int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                                   float* logits_out, void* ws, size_t ws_bytes, void* stream,
+                                   void* cold_stream, void* fork_event, void* join_event,
+                                   int32_t cold_rows_max) {
+  moe_status st = check_layer(d);
+  if (st != MOE_OK) return st;
+  if (d->routed.dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (cold_rows_max < 0) return MOE_ERR_SHAPE;
+  if (!fork_event || !join_event || !ws || (d->T > 0 && (!x || !out))) return MOE_ERR_NULL;
+  if ((x && !al16(x)) || (out && !al16(out)) || !al256(ws)) return MOE_ERR_ALIGN;
+  if ((topk_idx_out && !al16(topk_idx_out)) || (topk_w_out && !al16(topk_w_out)) ||
+      (counts_out && !al16(counts_out)) || (logits_out && !al16(logits_out)))
+    return MOE_ERR_ALIGN;
+  const LayerPlan p = plan_layer(d);
+  if (ws_bytes < p.total) return MOE_ERR_WORKSPACE;
+  const int32_t T = d->T, k = d->k, E = d->E, H = d->H;
+  if (T == 0) return MOE_OK;
+  char* base = reinterpret_cast<char*>(ws);
+  hipStream_t s = (hipStream_t)stream, sc = (hipStream_t)cold_stream;
+  hipEvent_t fork = (hipEvent_t)fork_event, join = (hipEvent_t)join_event;
+  const bool shared = d->shared.w13 != nullptr;
+  int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(base + p.o_idx);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + p.o_w);
+  int32_t* counts = counts_out ? counts_out : reinterpret_cast<int32_t*>(base + p.o_counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + p.o_offsets);
+  int32_t* inv_perm = reinterpret_cast<int32_t*>(base + p.o_inv_perm);
+  int32_t* row_token = reinterpret_cast<int32_t*>(base + p.o_row_token);
+  hipError_t e = launch_route(x, d->act_dtype, d->w_router, d->bias, T, H, E, k, d->score_fn,
+                              d->route_scale, idx, w, logits_out, base + p.o_route, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward_split route");
+  e = launch_permute_maps(idx, T, k, E, counts, offsets,
+                          reinterpret_cast<int32_t*>(base + p.o_perm_src), inv_perm, row_token,
+                          nullptr, nullptr, p.ffn.tile_m, shared ? 1 : 0, base + p.o_perm_ws, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward_split permute");
+  const int32_t tm_cold = ffn_stream_tile_rows();
+  Tile* hot_tiles = reinterpret_cast<Tile*>(base + p.ffn.o_tiles);
+  int32_t* hot_n = reinterpret_cast<int32_t*>(base + p.ffn.o_ntiles);
+  Tile* cold_tiles = reinterpret_cast<Tile*>(base + p.o_cold_tiles);
+  int32_t* cold_n = reinterpret_cast<int32_t*>(base + p.o_cold_ntiles);
+  e = launch_split_tiles(offsets, E, T, k, shared ? 1 : 0, cold_rows_max, p.ffn.tile_m, hot_tiles,
+                         hot_n, tm_cold, cold_tiles, cold_n, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward_split tiles");
+  void* y = base + p.ffn.o_y;
+  FfnArgs f = ffn_args(p.ffn, base, d->routed, shared ? &d->shared : nullptr, d->act_dtype, H, x,
+                       row_token, y);
+  // cold groups: streaming kernels on the side stream, between the fork and join events; at
+  // most ceil(cold_rows_max / tm_cold) tiles a group
+  FfnArgs fc = f;
+  fc.tiles = cold_tiles;
+  fc.ntiles = cold_n;
+  fc.tile_m = tm_cold;
+  const int64_t per_group = ((int64_t)cold_rows_max + tm_cold - 1) / tm_cold;
+  const int64_t cold_bound = per_group * (E + (shared ? 1 : 0));
+  fc.max_tiles = (int32_t)(cold_bound < p.cold_max_tiles ? cold_bound : p.cold_max_tiles);
+  if ((e = hipEventRecord(fork, s)) != hipSuccess || (e = hipStreamWaitEvent(sc, fork, 0)) != hipSuccess)
+    return hip_fail(e, "moe_layer_forward_split fork");
+  e = launch_grouped_ffn(fc, base + p.ffn.o_scratch, sc);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward_split cold ffn");
+  if ((e = hipEventRecord(join, sc)) != hipSuccess) return hip_fail(e, "moe_layer_forward_split join");
+  // hot groups: the kernels the layer picks for this batch, on the main stream
+  e = launch_grouped_ffn(f, base + p.ffn.o_scratch, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward_split hot ffn");
+  if ((e = hipStreamWaitEvent(s, join, 0)) != hipSuccess)
+    return hip_fail(e, "moe_layer_forward_split join");
+  const void* ysh = shared ? reinterpret_cast<const char*>(y) + (size_t)T * k * H * dt_bytes(p.ffn.y_dt)
+                           : nullptr;
+  e = launch_combine(y, p.ffn.y_dt, inv_perm, w, T, k, H, ysh, out, d->out_dtype, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_layer_forward_split combine");
 }
 
 moe_status moe_layer_forward_timed(const moe_layer_desc* d, const void* x, void* out,

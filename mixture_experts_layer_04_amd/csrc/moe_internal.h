@@ -123,6 +123,12 @@ hipError_t launch_gather_rows(const void* x, int32_t elem_bytes, int32_t H,
 // Row map and tile list of the shared group alone (rows T*k .. T*k + T - 1, group E).
 hipError_t launch_shared_group(int32_t T, int32_t k, int32_t E, int32_t tile_m, int32_t* row_token,
                                Tile* tiles, int32_t* ntiles, hipStream_t s);
+// Hot and cold tile lists from the offsets (and the shared group E of T rows at row T*k):
+// groups of more than cold_max rows in tm_hot-row tiles, the rest in tm_cold-row tiles.
+hipError_t launch_split_tiles(const int32_t* offsets, int32_t E, int32_t T, int32_t k,
+                              int32_t with_shared, int32_t cold_max, int32_t tm_hot, Tile* hot,
+                              int32_t* n_hot, int32_t tm_cold, Tile* cold, int32_t* n_cold,
+                              hipStream_t s);
 // Tile list straight from a device offsets array (grouped FFN called on its own).
 hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* tiles,
                                      int32_t* ntiles, int32_t tile_m, hipStream_t s);
@@ -134,6 +140,8 @@ bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I);
 int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32_t I_routed,
                    int32_t I_shared);
 size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_max);
+// Rows per tile of the streaming kernels (the tile_m that selects them).
+int32_t ffn_stream_tile_rows();
 // Runs gate/up + SwiGLU and down for all tiles. `scratch` holds h (and fp8 staging).
 // If mid_event is non-NULL it is recorded between the gate/up and the down launches.
 hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s,

@@ -209,6 +209,41 @@ __global__ void __launch_bounds__(kScanThreads) k_tiles_from_offsets(const int32
   if (e == 0) *ntiles = ntot;
 }
 
+// Two tile lists from the offsets: groups with more than cold_max rows ("hot": many rows
+// per expert, the tiled kernels' work) in tm_hot-row tiles, groups with 1..cold_max rows
+// ("cold": their weights stream, few rows to multiply) in tm_cold-row tiles. The shared
+// group E (T rows at row T*k), when present, is classified the same way.
+__global__ void __launch_bounds__(kScanThreads) k_split_tiles(const int32_t* __restrict__ offsets,
+                                                              int E, int T, int k, int with_shared,
+                                                              int cold_max, int tm_hot,
+                                                              Tile* __restrict__ hot,
+                                                              int32_t* __restrict__ n_hot,
+                                                              int tm_cold, Tile* __restrict__ cold,
+                                                              int32_t* __restrict__ n_cold) {
+  __shared__ int sh[kScanThreads];
+  const int e = threadIdx.x;
+  int rows = 0, row0 = 0;
+  if (e < E) {
+    row0 = offsets[e];
+    rows = offsets[e + 1] - row0;
+  } else if (e == E && with_shared) {
+    row0 = T * k;
+    rows = T;
+  }
+  const bool is_cold = rows <= cold_max;
+  const int nh = is_cold ? 0 : (rows + tm_hot - 1) / tm_hot;
+  const int nc = is_cold ? (rows + tm_cold - 1) / tm_cold : 0;
+  int th, tc;
+  const int oh = block_exclusive_scan(nh, sh, &th);
+  const int oc = block_exclusive_scan(nc, sh, &tc);
+  for (int i = 0; i < nh; ++i) hot[oh + i] = make_tile(e, row0, rows, i, nh, oh, tm_hot);
+  for (int i = 0; i < nc; ++i) cold[oc + i] = make_tile(e, row0, rows, i, nc, oc, tm_cold);
+  if (e == 0) {
+    *n_hot = th;
+    *n_cold = tc;
+  }
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int32_t T, int32_t E) {
@@ -265,6 +300,15 @@ hipError_t launch_shared_group(int32_t T, int32_t k, int32_t E, int32_t tile_m, 
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_shared_group, dim3((T + 255) / 256), dim3(256), 0, s, row_token, T, k, E,
                      tile_m, tiles, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_tiles(const int32_t* offsets, int32_t E, int32_t T, int32_t k,
+                              int32_t with_shared, int32_t cold_max, int32_t tm_hot, Tile* hot,
+                              int32_t* n_hot, int32_t tm_cold, Tile* cold, int32_t* n_cold,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_split_tiles, dim3(1), dim3(kScanThreads), 0, s, offsets, E, T, k,
+                     with_shared, cold_max, tm_hot, hot, n_hot, tm_cold, cold, n_cold);
   return hipGetLastError();
 }
 
