@@ -122,19 +122,21 @@ def test_combine_matches_layer_accumulation(with_shared):
 
 
 def _silu_at(target: float, lo: float, hi: float) -> float:
-    """A float64 z in [lo, hi] with torch's float64 SiLU(z) just above `target`, within
-    2^-27 relative: above the tie in float64, on it after rounding to fp32."""
+    """A float64 z in [lo, hi] whose float64 SiLU lies about 2^-33 relative above `target`
+    (torch's SiLU and the oracle's both: far above float64's last bit, far below half an
+    fp32 step), so h is above the tie in float64 and on it after rounding to fp32."""
     f = lambda z: F.silu(torch.tensor([z], dtype=torch.float64)).item()
+    goal = target * (1 + 2.0 ** -33)
     a, b = lo, hi
     for _ in range(200):
         m = 0.5 * (a + b)
-        if f(m) > target:
+        if f(m) > goal:
             b = m
         else:
             a = m
     z = b
-    v = f(z)
-    assert target < v < target * (1 + 2.0 ** -27), (v, target)
+    for v in (f(z), float(O.silu(np.array([z]))[0])):
+        assert target < v < target * (1 + 2.0 ** -27) and np.float32(v) == np.float32(target), (v, target)
     return z
 
 

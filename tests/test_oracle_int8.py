@@ -102,15 +102,19 @@ def test_int8_products_match_integer_accumulation():
 
 
 def _silu_at(target, lo, hi):
+    """A float64 z whose float64 SiLU (torch's and the oracle's) lies about 2^-33 relative
+    above `target`: above the tie in float64, on it after rounding to fp32."""
     f = lambda z: F.silu(torch.tensor([z], dtype=torch.float64)).item()
+    goal = target * (1 + 2.0 ** -33)
     a, b = lo, hi
     for _ in range(200):
         m = 0.5 * (a + b)
-        if f(m) > target:
+        if f(m) > goal:
             b = m
         else:
             a = m
-    assert target < f(b) < target * (1 + 2.0 ** -27)
+    for v in (f(b), float(O.silu(np.array([b]))[0])):
+        assert target < v < target * (1 + 2.0 ** -27) and np.float32(v) == np.float32(target)
     return b
 
 
