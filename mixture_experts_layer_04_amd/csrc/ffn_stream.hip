@@ -2,12 +2,13 @@
 // streaming the weights of the touched experts ("GC-MoE: Overlapping Expert-Parallel
 // Token Dispatch with FP8/FP4 Grouped GEMM via CUDA Green Contexts", why_it_matters).
 // The weights are the MFMA A operand (16 output features per wavefront), the <= 16 rows
-// of the tile the B operand. Each lane loads 32 contiguous bytes of its weight row per
-// step (a full 128-B line per 4 lanes) straight from HBM into registers: a weight element
+// of the tile the B operand. Weights go straight from HBM into registers: a weight element
 // is read exactly once per tile and never staged in LDS. bf16 uses
 // v_mfma_f32_16x16x32_bf16, fp32 v_mfma_f32_16x16x4_f32. Because a dot product may be
-// summed in any order, the K index carried by lane group kq and register slot j is
-// k0 + 16*kq + j (bf16) -- the same map for A and B -- which makes every load contiguous.
+// summed in any order, the K index that a lane group and register slot carry is chosen
+// per kernel -- the same map for A and B -- to suit the loads: the bf16 gate/up kernel
+// loads whole 128-B lines of 8 rows per instruction and rearranges them across lanes
+// (load_w_lines), the others load 32 contiguous bytes of a row per lane (k0 + 16 kq + j).
 // Two wavefronts of a workgroup share one group of weight rows, each streaming half of
 // its K range; their fp32 partial sums meet in LDS and are added in K order (shorter
 // streams per wavefront measured 1-2% faster than whole rows, longer ones slower).
@@ -68,6 +69,9 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
 #ifndef MOE_STREAM_UNROLL_GU
 #define MOE_STREAM_UNROLL_GU 2
 #endif
+#ifndef MOE_STREAM_UNROLL_GU_BF16  // the same for bf16 weights in whole lines (load_w_lines)
+#define MOE_STREAM_UNROLL_GU_BF16 1
+#endif
 #ifndef MOE_STREAM_ROWS_GU  // 16-row weight groups per wavefront (bf16)
 #define MOE_STREAM_ROWS_GU 4
 #endif
@@ -95,6 +99,58 @@ static_assert(64 % (16 * MOE_STREAM_ROWS_DN) == 0, "down row groups must tile H 
 // Weight fragment: ordinary cached loads (on MI355X they measured faster than
 // non-temporal ones for this many-rows-at-once pattern).
 __device__ __forceinline__ Frag32 load_w(const void* p) { return load_c(p); }
+
+// bf16 weight rows in whole 128-B lines. A load instruction whose 64 lanes take 16 rows x
+// 64 B (lane (m, kq) its MFMA fragment) streamed at 5.5 TB/s non-temporal and 6.2 TB/s
+// cached in a probe on MI355X; one whose lanes take 8 rows x 128 B streamed at 6.7-6.8
+// TB/s non-temporal. So a 16-row group's 64-element K step (16 rows x 128 B) is two such
+// loads, G0 (rows 0..7) and G1 (rows 8..15): lane (m, kq) takes 16-B chunk kq + 4 (m / 8)
+// of row m % 8 in G0 and chunk kq + 4 (1 - m / 8) of row 8 + m % 8 in G1. Then row m's
+// chunk kq sits in lane (m, kq) of G0 (m < 8) or G1 (m >= 8), and its chunk kq + 4 in lane
+// (m ^ 8, kq) of the other one: a select and a DPP rotation by 8 lanes within each row of
+// 16 give the MFMA operand, .lo = K elements 8 kq .. 8 kq + 7 and .hi = 32 + 8 kq .. of
+// the step. The B operand takes the same K map (load_x_perm).
+struct WRaw {
+  u32x4 g0, g1;
+};
+struct WLane {  // this lane's byte offsets of G0 and G1 from a group's first row
+  uint32_t o0, o1;
+  bool lo8;
+};
+__device__ __forceinline__ WLane wlane(int m, int kq, uint32_t row_bytes) {
+  return WLane{(uint32_t)(m & 7) * row_bytes + (uint32_t)(kq + 4 * (m >> 3)) * 16,
+               (uint32_t)(8 + (m & 7)) * row_bytes + (uint32_t)(kq + 4 * (1 - (m >> 3))) * 16, m < 8};
+}
+__device__ __forceinline__ WRaw load_w_lines(const char* group, const WLane& w) {
+  WRaw r;
+  r.g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(group + w.o0));
+  r.g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(group + w.o1));
+  return r;
+}
+__device__ __forceinline__ Frag32 w_frag(const WRaw& r, bool lo8) {
+  Frag32 f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f.lo[j] = lo8 ? r.g0[j] : r.g1[j];
+    const uint32_t y = lo8 ? r.g1[j] : r.g0[j];
+    // row_ror:8 -- lane i of each 16-lane row takes lane (i + 8) % 16
+    f.hi[j] = (uint32_t)__builtin_amdgcn_mov_dpp((int)y, 0x128, 0xF, 0xF, false);
+  }
+  return f;
+}
+// The matching B-operand fragment of a row: K elements 8 kq .. + 7 and 32 + 8 kq .. + 7 of
+// the step (p already offset by 16 kq bytes); zeros for padding rows.
+__device__ __forceinline__ Frag32 load_x_perm(const char* p, bool valid) {
+  Frag32 f;
+  if (valid) {
+    f.lo = *reinterpret_cast<const u32x4*>(p);
+    f.hi = *reinterpret_cast<const u32x4*>(p + 64);
+  } else {
+    f.lo = u32x4{0, 0, 0, 0};
+    f.hi = u32x4{0, 0, 0, 0};
+  }
+  return f;
+}
 // Activation fragment of a row; lanes of padding rows (beyond the tile's rows) load
 // nothing and contribute zeros to columns that are never stored.
 __device__ __forceinline__ Frag32 load_x(const void* p, bool valid) {
@@ -157,15 +213,6 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
   constexpr int kStep = kF32 ? 32 : 64;          // K elements per MFMA step
   constexpr int kLane = kStep / 4;               // contiguous elements per lane per step
   constexpr int U = MOE_STREAM_UNROLL_GU;
-  const int64_t lane_off = (int64_t)kq * kLane * esz;
-  const char* wg[R];
-  const char* wu[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    wg[r] = w13 + (int64_t)(f0 + 16 * r + m) * H * esz + lane_off;
-    wu[r] = w13 + (int64_t)(I + f0 + 16 * r + m) * H * esz + lane_off;
-  }
-  const char* xr = reinterpret_cast<const char*>(a.a) + src * H * esz + lane_off;
   f32x4 accg[R], accu[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) accg[r] = accu[r] = f32x4{0, 0, 0, 0};
@@ -173,33 +220,78 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
   const int kbeg = active ? (ks * nst / KS) * kStep : 0;
   const int kend = active ? ((ks + 1) * nst / KS) * kStep : 0;
   const int kmain = kend - (kend - kbeg) % (kStep * U);
-  for (int k0 = kbeg; k0 < kmain; k0 += kStep * U) {
-    Frag32 fg[U][R], fu[U][R], fx[U];
+  if constexpr (!kF32) {
+    // whole 128-B lines of 8 rows per load (load_w_lines): the group's first row is uniform
+    const WLane wl = wlane(m, kq, (uint32_t)H * 2);
+    const char* xq = reinterpret_cast<const char*>(a.a) + src * H * 2 + kq * 16;
+    const char* g0 = w13 + (int64_t)f0 * H * 2;
+    const char* u0 = w13 + (int64_t)(I + f0) * H * 2;
+    auto step = [&](int k0, auto uc) {
+      constexpr int UU = decltype(uc)::value;
+      WRaw rg[UU][R], ru[UU][R];
+      Frag32 fx[UU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t o = (int64_t)(k0 + u * kStep) * esz;
+      for (int u = 0; u < UU; ++u) {
+        const int64_t o = (int64_t)(k0 + u * 64) * 2;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        fg[u][r] = load_w(wg[r] + o);
-        fu[u][r] = load_w(wu[r] + o);
+        for (int r = 0; r < R; ++r) {
+          rg[u][r] = load_w_lines(g0 + (int64_t)16 * r * H * 2 + o, wl);
+          ru[u][r] = load_w_lines(u0 + (int64_t)16 * r * H * 2 + o, wl);
+        }
+        fx[u] = load_x_perm(xq + o, xv);
       }
-      fx[u] = load_x(xr + o, xv);
-    }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < UU; ++u)
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        accg[r] = mma<kF32>(fg[u][r], fx[u], accg[r]);
-        accu[r] = mma<kF32>(fu[u][r], fx[u], accu[r]);
-      }
-  }
-  for (int k0 = kmain; k0 < kend; k0 += kStep) {
-    const int64_t o = (int64_t)k0 * esz;
-    const Frag32 fx = load_x(xr + o, xv);
+        for (int r = 0; r < R; ++r) {
+          accg[r] = mma_bf16(w_frag(rg[u][r], wl.lo8), fx[u], accg[r]);
+          accu[r] = mma_bf16(w_frag(ru[u][r], wl.lo8), fx[u], accu[r]);
+        }
+    };
+    constexpr int UB = MOE_STREAM_UNROLL_GU_BF16;
+    const int kmb = kend - (kend - kbeg) % (64 * UB);
+    for (int k0 = kbeg; k0 < kmb; k0 += 64 * UB) step(k0, IntC<UB>{});
+    for (int k0 = kmb; k0 < kend; k0 += 64) step(k0, IntC<1>{});
+  } else {
+    // fp32: each lane's 32 contiguous bytes of its row per step (cached loads), K index
+    // k0 + 8 kq + j in both operands
+    const int64_t lane_off = (int64_t)kq * kLane * esz;
+    const char* wg[R];
+    const char* wu[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      accg[r] = mma<kF32>(load_w(wg[r] + o), fx, accg[r]);
-      accu[r] = mma<kF32>(load_w(wu[r] + o), fx, accu[r]);
+      wg[r] = w13 + (int64_t)(f0 + 16 * r + m) * H * esz + lane_off;
+      wu[r] = w13 + (int64_t)(I + f0 + 16 * r + m) * H * esz + lane_off;
+    }
+    const char* xr = reinterpret_cast<const char*>(a.a) + src * H * esz + lane_off;
+    for (int k0 = kbeg; k0 < kmain; k0 += kStep * U) {
+      Frag32 fg[U][R], fu[U][R], fx[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t o = (int64_t)(k0 + u * kStep) * esz;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          fg[u][r] = load_w(wg[r] + o);
+          fu[u][r] = load_w(wu[r] + o);
+        }
+        fx[u] = load_x(xr + o, xv);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          accg[r] = mma<kF32>(fg[u][r], fx[u], accg[r]);
+          accu[r] = mma<kF32>(fu[u][r], fx[u], accu[r]);
+        }
+    }
+    for (int k0 = kmain; k0 < kend; k0 += kStep) {
+      const int64_t o = (int64_t)k0 * esz;
+      const Frag32 fx = load_x(xr + o, xv);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        accg[r] = mma<kF32>(load_w(wg[r] + o), fx, accg[r]);
+        accu[r] = mma<kF32>(load_w(wu[r] + o), fx, accu[r]);
+      }
     }
   }
   if constexpr (KS > 1) {
@@ -583,9 +675,11 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
     su[r] = scales + u * (H / 32);
   }
   const bool xv = m < tl.nrows;
+#if !MOE_STREAM_MX_LDS
   const int row = tl.row0 + (xv ? m : 0);
   const int64_t src = a.a_rowmap ? a.a_rowmap[row] : row;
   const char* xr = reinterpret_cast<const char*>(a.a) + src * H * 2 + 64 * kq;
+#endif
   f32x4 accg[R], accu[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) accg[r] = accu[r] = f32x4{0, 0, 0, 0};
@@ -675,8 +769,10 @@ __global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_ti
     sw[r] = scales + o * (I / 32);
   }
   const bool xv = m < tl.nrows;
+#if !MOE_STREAM_MX_LDS
   const char* hr = reinterpret_cast<const char*>(a.h) +
                    (int64_t)(tl.row0 + (xv ? m : 0)) * a.I_max * 2 + 64 * kq;
+#endif
   f32x4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4{0, 0, 0, 0};

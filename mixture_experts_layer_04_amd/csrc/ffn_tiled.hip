@@ -78,7 +78,6 @@ static_assert(4 * 16 * 4 == kTiledMB && 4 * 16 * 4 == kTiledNB, "tile shape of t
 // waves a SIMD that the register budget must allow: a 16-wavefront workgroup puts four on
 // each SIMD of its CU
 constexpr int waves_per_simd(int nw) { return nw >= 16 ? 4 : MOE_T2_WAVES_PER_SIMD; }
-constexpr int kT2Threads = 64 * MOE_T2_WGM * MOE_T2_WGN;
 constexpr int kT2M = MOE_T2_WGM * 16 * MOE_T2_TM, kT2N = MOE_T2_WGN * 16 * MOE_T2_TN;
 static_assert(kT2M == kTiledM && kT2N == kTiledN, "tile shape of the tile list");
 
