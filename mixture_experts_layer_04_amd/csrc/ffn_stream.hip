@@ -6,12 +6,13 @@
 // is read exactly once per tile and never staged in LDS. bf16 uses
 // v_mfma_f32_16x16x32_bf16, fp32 v_mfma_f32_16x16x4_f32. Because a dot product may be
 // summed in any order, the K index that a lane group and register slot carry is chosen
-// per kernel -- the same map for A and B -- to suit the loads: the bf16 gate/up kernel
-// loads whole 128-B lines of 8 rows per instruction and rearranges them across lanes
-// (load_w_lines), the others load 32 contiguous bytes of a row per lane (k0 + 16 kq + j).
-// Two wavefronts of a workgroup share one group of weight rows, each streaming half of
-// its K range; their fp32 partial sums meet in LDS and are added in K order (shorter
-// streams per wavefront measured 1-2% faster than whole rows, longer ones slower).
+// per kernel -- the same map for A and B -- to suit the loads: the bf16 kernels load whole
+// 128-B lines of 8 rows per instruction and rearrange them across lanes (load_w_lines),
+// the fp32 ones load 32 contiguous bytes of a row per lane (k0 + 8 kq + j).
+// The four wavefronts of a workgroup share one block of weight rows (bf16: 4 groups of
+// 16), each streaming a quarter of its K range; their fp32 partial sums meet in LDS and are
+// added in K order. On r1_decode's shapes this beat halves (1%) and whole rows, and beat
+// staging the down launch's h rows in LDS (0.747 against 0.769 ms).
 #include "ffn_common.h"
 
 namespace moe {
@@ -75,20 +76,20 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
 #ifndef MOE_STREAM_ROWS_GU  // 16-row weight groups per wavefront (bf16)
 #define MOE_STREAM_ROWS_GU 4
 #endif
-#ifndef MOE_STREAM_ROWS_DN
-#define MOE_STREAM_ROWS_DN 1
+#ifndef MOE_STREAM_ROWS_DN  // 16-row weight groups per wavefront (bf16 down)
+#define MOE_STREAM_ROWS_DN 4
 #endif
 #ifndef MOE_STREAM_UNROLL_DN
 #define MOE_STREAM_UNROLL_DN 8
 #endif
-#ifndef MOE_STREAM_DN_LDS  // bf16 down with the tile's h rows staged in LDS (where I allows)
-#define MOE_STREAM_DN_LDS 1
+#ifndef MOE_STREAM_UNROLL_DN_LINES  // K steps per iteration of the bf16 down kernel
+#define MOE_STREAM_UNROLL_DN_LINES 1
 #endif
 #ifndef MOE_STREAM_KSPLIT_GU  // gate/up: wavefronts that share one row group, each a K range
-#define MOE_STREAM_KSPLIT_GU 2
+#define MOE_STREAM_KSPLIT_GU 4
 #endif
 #ifndef MOE_STREAM_KSPLIT_DN  // the same for down
-#define MOE_STREAM_KSPLIT_DN 2
+#define MOE_STREAM_KSPLIT_DN 4
 #endif
 // A wavefront's 16 R output features start at a multiple of 16 R, and ffn_shape_ok admits
 // bf16 / fp32 banks with H and I multiples of 64: so 16 R must divide 64, or the last
@@ -161,20 +162,23 @@ __device__ __forceinline__ Frag32 load_x(const void* p, bool valid) {
   return z;
 }
 
-// h's residual for K step k0 (64 elements) of a bf16 down projection: lane group kq's 16
-// elements k0 + 16 kq .. + 15 decoded from their 8 code bytes (lr already offset by 8 kq)
-// and the E8M0 scale of their 32-element block (ls offset by kq / 2); zeros for padding rows.
-__device__ __forceinline__ Frag32 load_lo(const uint8_t* lr, const uint8_t* ls, int k0, bool valid) {
+// h's residual for K step k0 (64 elements) of the bf16 down projection, in load_w_lines' K
+// map: elements k0 + 8 kq .. + 7 (.lo) and k0 + 32 + 8 kq .. + 7 (.hi), i.e. the code words
+// 4 kq and 16 + 4 kq bytes into the step (lr already offset by 4 kq), decoded with the
+// E8M0 scales of the step's two 32-element blocks; zeros for padding rows.
+__device__ __forceinline__ Frag32 load_lo_perm(const uint8_t* lr, const uint8_t* ls, int k0,
+                                               bool valid) {
   Frag32 f;
   if (!valid) {
     f.lo = u32x4{0, 0, 0, 0};
     f.hi = u32x4{0, 0, 0, 0};
     return f;
   }
-  const uint2 q = *reinterpret_cast<const uint2*>(lr + k0 / 2);
-  const float sc = e8m0_f32(ls[k0 / 32]);
-  f.lo = __builtin_bit_cast(u32x4, e2m1x8_bf16(q.x, sc));
-  f.hi = __builtin_bit_cast(u32x4, e2m1x8_bf16(q.y, sc));
+  const uint32_t q0 = *reinterpret_cast<const uint32_t*>(lr + k0 / 2);
+  const uint32_t q1 = *reinterpret_cast<const uint32_t*>(lr + k0 / 2 + 16);
+  const uint32_t sc = *reinterpret_cast<const uint16_t*>(ls + k0 / 32);
+  f.lo = __builtin_bit_cast(u32x4, e2m1x8_bf16(q0, e8m0_f32(sc & 0xFFu)));
+  f.hi = __builtin_bit_cast(u32x4, e2m1x8_bf16(q1, e8m0_f32(sc >> 8)));
   return f;
 }
 
@@ -385,58 +389,80 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
   if (KS == 1 && f0 >= H) return;
   const bool active = f0 < H;
   const int m = l & 15, kq = l >> 4;
-  const int esz = kF32 ? 4 : 2;
-  constexpr int kStep = kF32 ? 32 : 64;
-  constexpr int kLane = kStep / 4;
-  constexpr int U = MOE_STREAM_UNROLL_DN;
-  const int64_t lane_off = (int64_t)kq * kLane * esz;
+  constexpr int kStep = kF32 ? 32 : 64;  // K elements per MFMA step
   // this wavefront's K range [kbeg, kend), whole K steps
   const int nst = I / kStep;
   const int kbeg = active ? (ks * nst / KS) * kStep : 0;
   const int kend = active ? ((ks + 1) * nst / KS) * kStep : 0;
   const bool xv = m < tl.nrows;
-  const char* w2 = reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * esz;
-  const char* wr[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) wr[r] = w2 + (int64_t)(f0 + 16 * r + m) * I * esz + lane_off;
   const int64_t hrow = tl.row0 + (xv ? m : 0);
-  const char* hr = reinterpret_cast<const char*>(a.h) + hrow * a.I_max * esz + lane_off;
-  // bf16: h's residual (ffn_common.h), this lane's 16 elements of each K step: 8 bytes of
-  // codes and the scale of their 32-element block
-  const uint8_t* lr = kF32 ? nullptr : a.h_lo + hrow * (a.I_max / 2) + kq * 8;
-  const uint8_t* ls = kF32 ? nullptr : a.h_lo_s + hrow * lo_sstride(a.I_max) + (kq >> 1);
   f32x4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4{0, 0, 0, 0};
-  const int kmain = kend - (kend - kbeg) % (kStep * U);
-  for (int k0 = kbeg; k0 < kmain; k0 += kStep * U) {
-    Frag32 fw[U][R], fh[U], fl[U];
+  if constexpr (!kF32) {
+    // bf16: weights in whole 128-B lines (load_w_lines); h and its residual (ffn_common.h)
+    // in that K map
+    const char* w2 = reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * 2;
+    const WLane wl = wlane(m, kq, (uint32_t)I * 2);
+    const char* hq = reinterpret_cast<const char*>(a.h) + hrow * a.I_max * 2 + kq * 16;
+    const uint8_t* lq = a.h_lo + hrow * (a.I_max / 2) + kq * 4;
+    const uint8_t* lsb = a.h_lo_s + hrow * lo_sstride(a.I_max);
+    auto step = [&](int k0, auto uc) {
+      constexpr int UU = decltype(uc)::value;
+      WRaw rw[UU][R];
+      Frag32 fh[UU], fl[UU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t o = (int64_t)(k0 + u * kStep) * esz;
+      for (int u = 0; u < UU; ++u) {
+        const int64_t o = (int64_t)(k0 + u * 64) * 2;
 #pragma unroll
-      for (int r = 0; r < R; ++r) fw[u][r] = load_w(wr[r] + o);
-      fh[u] = load_x(hr + o, xv);
-      if (!kF32) fl[u] = load_lo(lr, ls, k0 + u * kStep, xv);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        acc[r] = mma<kF32>(fw[u][r], fh[u], acc[r]);
-        if (!kF32) acc[r] = mma<false>(fw[u][r], fl[u], acc[r]);
+        for (int r = 0; r < R; ++r)
+          rw[u][r] = load_w_lines(w2 + (int64_t)(f0 + 16 * r) * I * 2 + o, wl);
+        fh[u] = load_x_perm(hq + o, xv);
+        fl[u] = load_lo_perm(lq, lsb, k0 + u * 64, xv);
       }
-  }
-  for (int k0 = kmain; k0 < kend; k0 += kStep) {
-    const int64_t o = (int64_t)k0 * esz;
-    const Frag32 fh = load_x(hr + o, xv);
-    Frag32 fl;
-    if (!kF32) fl = load_lo(lr, ls, k0, xv);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const Frag32 fw = load_w(wr[r] + o);
-      acc[r] = mma<kF32>(fw, fh, acc[r]);
-      if (!kF32) acc[r] = mma<false>(fw, fl, acc[r]);
+      for (int u = 0; u < UU; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const Frag32 fw = w_frag(rw[u][r], wl.lo8);
+          acc[r] = mma_bf16(fw, fh[u], acc[r]);
+          acc[r] = mma_bf16(fw, fl[u], acc[r]);
+        }
+    };
+    constexpr int UB = MOE_STREAM_UNROLL_DN_LINES;
+    const int kmb = kend - (kend - kbeg) % (64 * UB);
+    for (int k0 = kbeg; k0 < kmb; k0 += 64 * UB) step(k0, IntC<UB>{});
+    for (int k0 = kmb; k0 < kend; k0 += 64) step(k0, IntC<1>{});
+  } else {
+    // fp32: each lane's 32 contiguous bytes of its row per step (cached loads), K index
+    // k0 + 8 kq + j in both operands
+    constexpr int U = MOE_STREAM_UNROLL_DN;
+    const int64_t lane_off = (int64_t)kq * 8 * 4;
+    const char* w2 = reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * 4;
+    const char* wr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wr[r] = w2 + (int64_t)(f0 + 16 * r + m) * I * 4 + lane_off;
+    const char* hr = reinterpret_cast<const char*>(a.h) + hrow * a.I_max * 4 + lane_off;
+    const int kmain = kend - (kend - kbeg) % (kStep * U);
+    for (int k0 = kbeg; k0 < kmain; k0 += kStep * U) {
+      Frag32 fw[U][R], fh[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t o = (int64_t)(k0 + u * kStep) * 4;
+#pragma unroll
+        for (int r = 0; r < R; ++r) fw[u][r] = load_w(wr[r] + o);
+        fh[u] = load_x(hr + o, xv);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = mma_f32(fw[u][r], fh[u], acc[r]);
+    }
+    for (int k0 = kmain; k0 < kend; k0 += kStep) {
+      const int64_t o = (int64_t)k0 * 4;
+      const Frag32 fh = load_x(hr + o, xv);
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = mma_f32(load_w(wr[r] + o), fh, acc[r]);
     }
   }
   if constexpr (KS > 1) {
@@ -460,84 +486,6 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
     for (int r = 0; r < R; ++r)
       store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + 16 * r + kq * 4, acc[r]);
   }
-}
-
-// Down projection, bf16, with the tile's h rows staged in LDS: the workgroup's four
-// wavefronts (four groups of 16 output features) share each 512-element K chunk of the
-// 16 h rows, which goes global -> LDS by DMA (each wavefront one 1-KB row piece of four
-// rows) through two buffers, instead of every wavefront loading it into registers. Lane l
-// of the DMA of row p takes the 16-B piece l ^ p of the row, so that the 16 rows' reads of
-// one lane group fall in different banks. Needs I % 512 == 0.
-constexpr int kDnLdsK = 512;  // K elements per chunk (8 MFMA steps)
-template <bool kYF32>
-__global__ void __launch_bounds__(256) k_down_stream_lds(FfnArgs a, int fb_per_tile) {
-  constexpr int U = kDnLdsK / 64;
-  constexpr int CB = 16 * kDnLdsK * 2;  // bytes of a chunk
-  __shared__ __attribute__((aligned(1024))) char hs[2 * CB];
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int tile_id = blockIdx.x / fb_per_tile;
-  const int fb = blockIdx.x - tile_id * fb_per_tile;
-  if (tile_id >= *a.ntiles) return;
-  const Tile tl = a.tiles[tile_id];
-  const int bank = tl.group < a.E ? 0 : 1;
-  const int64_t ge = tl.group < a.E ? tl.group : 0;
-  const int I = a.bank[bank].I;
-  const int H = a.H;
-  const int f0 = (fb * 4 + wave) * 16;
-  const bool active = f0 < H;
-  const int m = l & 15, kq = l >> 4;
-  const bool xv = m < tl.nrows;
-  const char* wr = reinterpret_cast<const char*>(a.bank[bank].w2) + ge * (int64_t)H * I * 2 +
-                   (int64_t)(active ? f0 + m : 0) * I * 2 + kq * 32;
-  const char* hsrc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = 4 * wave + j;
-    const int rr = p < tl.nrows ? p : (tl.nrows > 0 ? tl.nrows - 1 : 0);  // padding rows: any valid row
-    hsrc[j] = reinterpret_cast<const char*>(a.h) + (int64_t)(tl.row0 + rr) * a.I_max * 2 + (l ^ p) * 16;
-  }
-  auto issue = [&](int c) {
-    char* dst = hs + (c & 1) * CB;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(hsrc[j] + (int64_t)c * kDnLdsK * 2, dst + (4 * wave + j) * 1024);
-  };
-  // h's residual (ffn_common.h): this lane's 8 code bytes of each K step and the scales of
-  // the chunk's 16 blocks of 32 elements, loaded from global memory (L2) per chunk
-  const int64_t hrow = tl.row0 + (xv ? m : 0);
-  const uint8_t* lr = a.h_lo + hrow * (a.I_max / 2) + kq * 8;
-  const uint8_t* ls = a.h_lo_s + hrow * lo_sstride(a.I_max);
-  const int nch = I / kDnLdsK;
-  f32x4 acc = f32x4{0, 0, 0, 0};
-  issue(0);
-  for (int c = 0; c < nch; ++c) {
-    Frag32 fw[U];
-    uint2 lq[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) fw[u] = load_w(wr + (int64_t)(c * kDnLdsK + u * 64) * 2);
-#pragma unroll
-    for (int u = 0; u < U; ++u) lq[u] = *reinterpret_cast<const uint2*>(lr + (c * kDnLdsK + u * 64) / 2);
-    const u32x4 sc4 = *reinterpret_cast<const u32x4*>(ls + c * (kDnLdsK / 32));
-    // this wavefront's DMA of chunk c, issued before the 2 U weight, U code and 1 scale loads
-    wait_vmcnt<3 * U + 1>();
-    __builtin_amdgcn_s_barrier();  // ... and every other wavefront's; chunk c - 1 is read
-    if (c + 1 < nch) issue(c + 1);
-    const char* hb = hs + (c & 1) * CB + m * 1024;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      Frag32 fh;
-      fh.lo = *reinterpret_cast<const u32x4*>(hb + (((u * 8 + kq * 2) ^ m) << 4));
-      fh.hi = *reinterpret_cast<const u32x4*>(hb + (((u * 8 + kq * 2 + 1) ^ m) << 4));
-      acc = mma_bf16(fw[u], fh, acc);
-      // block (64 u + 16 kq) / 32 = 2 u + kq / 2 of the chunk: byte of dword u / 2
-      const uint32_t sb = (sc4[u >> 1] >> (8 * (2 * (u & 1) + (kq >> 1)))) & 0xFFu;
-      const float sc = e8m0_f32(sb);
-      Frag32 fl;
-      fl.lo = __builtin_bit_cast(u32x4, e2m1x8_bf16(lq[u].x, sc));
-      fl.hi = __builtin_bit_cast(u32x4, e2m1x8_bf16(lq[u].y, sc));
-      acc = mma_bf16(fw[u], fl, acc);
-    }
-  }
-  if (xv && active) store4<kYF32>(a.y, (int64_t)(tl.row0 + m) * H + f0 + kq * 4, acc);
 }
 
 // ------------------------------------------------------------------ MXFP4 weights
@@ -861,13 +809,7 @@ hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_eve
     hipLaunchKernelGGL((k_down_stream<true, true, 1>), dim3(a.max_tiles * fb_dn1), blk, 0, s, a, fb_dn1);
   else if (f32)
     hipLaunchKernelGGL((k_down_stream<true, false, 1>), dim3(a.max_tiles * fb_dn1), blk, 0, s, a, fb_dn1);
-  else if (MOE_STREAM_DN_LDS && a.bank[0].I % kDnLdsK == 0 && a.bank[1].I % kDnLdsK == 0) {
-    const int fbl = (a.H + kFeatPerWG - 1) / kFeatPerWG;
-    if (yf32)
-      hipLaunchKernelGGL((k_down_stream_lds<true>), dim3(a.max_tiles * fbl), blk, 0, s, a, fbl);
-    else
-      hipLaunchKernelGGL((k_down_stream_lds<false>), dim3(a.max_tiles * fbl), blk, 0, s, a, fbl);
-  } else if (yf32)
+  else if (yf32)
     hipLaunchKernelGGL((k_down_stream<false, true, RD>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
   else
     hipLaunchKernelGGL((k_down_stream<false, false, RD>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
