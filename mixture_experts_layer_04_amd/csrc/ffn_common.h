@@ -41,6 +41,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
+// The same with the non-temporal hint (nt): for data read once (weights streamed past
+// every other user), which streams from HBM faster than a cached request when a
+// wavefront's lanes cover whole 128-B lines.
+__device__ __forceinline__ void dma16nt(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 2);
+}
 // 4 B per lane from global memory into LDS at lds + 4 * lane (device-only wrapper).
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);

@@ -32,6 +32,9 @@ namespace {
 #ifndef MOE_F8_STAGES_DN
 #define MOE_F8_STAGES_DN 2
 #endif
+#ifndef MOE_F8_W_NT  // weight DMA of single-tile groups with the non-temporal hint
+#define MOE_F8_W_NT 1
+#endif
 
 // fp32 -> E4M3FN code, round to nearest even, saturating at +-448 (NaN -> 0x7F).
 // Written from the format: magnitudes below 2^-6 lie on the subnormal grid m * 2^-9;
@@ -209,11 +212,18 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
     const float* sb = reinterpret_cast<const float*>(a.bank[bank].w2_scale) + ge * (H / 128) * (int64_t)KB;
     sp = sb + (int64_t)(f0 / 128) * KB;
   }
+  // A group that fits in one tile reads its weights once: stream them with the
+  // non-temporal hint (r1_decode_fp8 gate/up 0.72 -> 0.66 ms). Where row tiles of a group
+  // share the weights through L2, the hint made the prefill-sized INT8 layer 12% slower.
+  const bool wnt = MOE_F8_W_NT && tl.nblk == 1;
   auto issue = [&](int kb) {
     char* st = ring + (kb % S) * STG;
     const int64_t o = (int64_t)kb * kF8K;
 #pragma unroll
-    for (int i = 0; i < NWD; ++i) dma16(wp[i] + o, st + (8 * i + wave) * 1024);
+    for (int i = 0; i < NWD; ++i) {
+      if (wnt) dma16nt(wp[i] + o, st + (8 * i + wave) * 1024);
+      else dma16(wp[i] + o, st + (8 * i + wave) * 1024);
+    }
     dma16(ap[0] + o, st + WB + wave * 1024);
     dma16(ap[1] + o, st + WB + (8 + wave) * 1024);
     if (l < (kGateUp ? 18 : 17)) dma4(sp + kb, st + WB + ACT + wave * 128);
