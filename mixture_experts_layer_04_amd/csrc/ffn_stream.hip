@@ -507,6 +507,9 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
 #ifndef MOE_STREAM_MX_ROWS_GU
 #define MOE_STREAM_MX_ROWS_GU 1
 #endif
+#ifndef MOE_STREAM_MX_LINES  // MXFP4 codes in whole 128-B lines (load_mx_lines)
+#define MOE_STREAM_MX_LINES 1
+#endif
 #ifndef MOE_STREAM_MX_ROWS_DN
 #define MOE_STREAM_MX_ROWS_DN 4
 #endif
@@ -582,6 +585,62 @@ __device__ __forceinline__ void read_x_mx_lds(const char* buf, int m, int kq, in
   for (int j = 0; j < 4; ++j)
     x4[j] = *reinterpret_cast<const u32x4*>(rb + (((4 * kq + 16 * i + j) ^ m) << 4));
 }
+// The same codes in whole 128-B lines (load_w_lines, non-temporal): line pair p of a
+// 16-row group and iteration covers the row's bytes 128 p .. 128 p + 127, whose chunk kq
+// (elements 256 p + 32 kq ..) is this lane's word group 2 p and chunk kq + 4 (elements
+// 256 p + 128 + 32 kq ..) its word group 2 p + 1 -- the K map of load_mx. The lines stay
+// as loaded until a word group is used (mx_words), so that the loads stay in flight.
+template <int U>
+struct MxLines {
+  WRaw p[U];
+  uint32_t sc[2 * U];
+};
+// grp: the group's first row's codes at the iteration's start; scales: this lane's row's
+template <int U>
+__device__ __forceinline__ MxLines<U> load_mx_lines(const uint8_t* grp, const WLane& wl,
+                                                    const uint8_t* scales) {
+  MxLines<U> c;
+#pragma unroll
+  for (int p = 0; p < U; ++p) c.p[p] = load_w_lines(reinterpret_cast<const char*>(grp) + 128 * p, wl);
+  if (U == 2) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(scales);
+#pragma unroll
+    for (int i = 0; i < 2 * U; ++i) c.sc[i] = v[i];
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(scales);
+    c.sc[0] = v.x;
+    c.sc[1 % (2 * U)] = v.y;
+  }
+  return c;
+}
+// word group i of the lines, as load_mx would hold it
+template <int U>
+__device__ __forceinline__ u32x4 mx_words(const MxLines<U>& w, int i, bool lo8) {
+  const WRaw& r = w.p[i >> 1];
+  u32x4 q;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if ((i & 1) == 0) {
+      q[j] = lo8 ? r.g0[j] : r.g1[j];
+    } else {
+      const uint32_t y = lo8 ? r.g1[j] : r.g0[j];
+      q[j] = (uint32_t)__builtin_amdgcn_mov_dpp((int)y, 0x128, 0xF, 0xF, false);  // row_ror:8
+    }
+  }
+  return q;
+}
+template <int U>
+__device__ __forceinline__ f32x4 mma_mx_part(const MxLines<U>& w, bool lo8, const u32x4* x4, int i,
+                                             int kq, f32x4 acc) {
+  const float sc = e8m0_f32((w.sc[i] >> (8 * kq)) & 0xFFu);
+  const u32x4 q = mx_words<U>(w, i, lo8);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e2m1x8_bf16(q[j], sc), as_bf16x8(x4[j]), acc,
+                                                  0, 0, 0);
+  return acc;
+}
+
 // acc += word group i of w (decoded with its scale) x the matching 4 activation pieces
 template <int U>
 __device__ __forceinline__ f32x4 mma_mx_part(const MxCodes<U>& w, const u32x4* x4, int i, int kq,
@@ -649,13 +708,27 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
   };
   issue(0);
 #endif
+#if MOE_STREAM_MX_LDS && MOE_STREAM_MX_LINES
+  const WLane wl = wlane(m, kq, (uint32_t)(H / 2));
+  const uint8_t* glg = codes + (int64_t)(active ? f0 : 0) * (H / 2);
+  const uint8_t* glu = codes + (int64_t)(I + (active ? f0 : 0)) * (H / 2);
+#endif
   for (int k0 = 0, c = 0; k0 < H; k0 += 256 * U, ++c) {
+#if MOE_STREAM_MX_LDS && MOE_STREAM_MX_LINES
+    MxLines<U> wg[R], wu[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      wg[r] = load_mx_lines<U>(glg + (int64_t)16 * r * (H / 2) + k0 / 2, wl, sg[r] + k0 / 32);
+      wu[r] = load_mx_lines<U>(glu + (int64_t)16 * r * (H / 2) + k0 / 2, wl, su[r] + k0 / 32);
+    }
+#else
     MxCodes<U> wg[R], wu[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       wg[r] = load_mx<U>(cg[r] + k0 / 2, sg[r] + k0 / 32);
       wu[r] = load_mx<U>(cu[r] + k0 / 2, su[r] + k0 / 32);
     }
+#endif
 #if MOE_STREAM_MX_LDS
     wait_vmcnt<2 * R * (2 * U + 1)>();  // this wavefront's DMA of chunk c (before the weight loads)
     __builtin_amdgcn_s_barrier();       // ... and the others'; chunk c - 1 is read
@@ -666,8 +739,13 @@ __global__ void __launch_bounds__(256) k_gateup_stream_mx(FfnArgs a, int fb_per_
       read_x_mx_lds(xs + (c & 1) * kMxChunk, m, kq, i, x4);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
+#if MOE_STREAM_MX_LINES
+        accg[r] = mma_mx_part<U>(wg[r], wl.lo8, x4, i, kq, accg[r]);
+        accu[r] = mma_mx_part<U>(wu[r], wl.lo8, x4, i, kq, accu[r]);
+#else
         accg[r] = mma_mx_part<U>(wg[r], x4, i, kq, accg[r]);
         accu[r] = mma_mx_part<U>(wu[r], x4, i, kq, accu[r]);
+#endif
       }
     }
 #else
@@ -741,10 +819,21 @@ __global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_ti
   };
   issue(0);
 #endif
+#if MOE_STREAM_MX_LDS && MOE_STREAM_MX_LINES
+  const WLane wl = wlane(m, kq, (uint32_t)(I / 2));
+  const uint8_t* gl = codes + (int64_t)(active ? f0 : 0) * (I / 2);
+#endif
   for (int k0 = 0, c = 0; k0 < I; k0 += 256 * U, ++c) {
+#if MOE_STREAM_MX_LDS && MOE_STREAM_MX_LINES
+    MxLines<U> w[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      w[r] = load_mx_lines<U>(gl + (int64_t)16 * r * (I / 2) + k0 / 2, wl, sw[r] + k0 / 32);
+#else
     MxCodes<U> w[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) w[r] = load_mx<U>(cw[r] + k0 / 2, sw[r] + k0 / 32);
+#endif
 #if MOE_STREAM_MX_LDS
     wait_vmcnt<R * (2 * U + 1)>();
     __builtin_amdgcn_s_barrier();
@@ -754,7 +843,13 @@ __global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_ti
       u32x4 x4[4];
       read_x_mx_lds(xs + (c & 1) * kMxChunk, m, kq, i, x4);
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = mma_mx_part<U>(w[r], x4, i, kq, acc[r]);
+      for (int r = 0; r < R; ++r) {
+#if MOE_STREAM_MX_LINES
+        acc[r] = mma_mx_part<U>(w[r], wl.lo8, x4, i, kq, acc[r]);
+#else
+        acc[r] = mma_mx_part<U>(w[r], x4, i, kq, acc[r]);
+#endif
+      }
     }
 #else
     u32x4 x[8 * U];
