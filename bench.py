@@ -161,7 +161,9 @@ def ffn_accounting(cfg, touched):
 
     return {
         "gate_up": launch(w13 + rows * H * xb + h_elems * hb, fl_gu, kgu),
-        "down": launch(w2 + h_elems * hb + rows * H * 4.0, fl_dn, kdn),
+        # expert outputs: fp32 for bf16/fp32 banks, bf16 for the quantised formats
+        "down": launch(w2 + h_elems * hb + rows * H * (4.0 if cfg.wdt in ("bf16", "f32") else 2.0),
+                       fl_dn, kdn),
         # router weights + x read by the router (routed layers), output written by the combine
         "other_bytes": ((cfg.E * H + T * H) * ELEM_BYTES[cfg.act] if cfg.routed else 0)
         + T * H * ELEM_BYTES[cfg.out],

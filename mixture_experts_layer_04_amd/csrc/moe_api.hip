@@ -85,10 +85,15 @@ void plan_ffn(Carve& c, FfnPlan& p, moe_dtype wdt, moe_dtype act, int32_t H, int
   int64_t mt = max_tiles(rows_routed, E, p.tile_m);
   if (shared_rows) mt += (shared_rows + p.tile_m - 1) / p.tile_m;
   p.max_tiles = (int32_t)mt;
-  // Expert outputs stay fp32 until the combine rounds once: with bf16 rows here the
-  // heavy-tailed SwiGLU outputs of small layers measured up to 2.5e-2 of the output RMS.
+  // bf16 and fp32 banks: expert outputs stay fp32 until the combine rounds once (with
+  // bf16 rows here the heavy-tailed SwiGLU outputs of small layers measured up to 2.5e-2 of
+  // the output RMS, over the bf16 tolerance). fp8, INT8, MXFP4 and W4A4 banks, whose layer
+  // outputs are held to 6e-2 (their codes differ by a step where the GPU's fp32 h and the
+  // float64 one fall on either side of a rounding boundary), store them as bf16: one more
+  // rounding of at most 2^-9 of each term, and half the bytes between the down projection
+  // and the combine.
   (void)act;
-  p.y_dt = MOE_F32;
+  p.y_dt = (wdt == MOE_BF16 || wdt == MOE_F32) ? MOE_F32 : MOE_BF16;
   p.o_tiles = c.take((size_t)mt * sizeof(Tile));
   p.o_ntiles = c.take(sizeof(int32_t));
   p.o_scratch = c.take(ffn_scratch_bytes(wdt, p.rows_total, H, I_max));
