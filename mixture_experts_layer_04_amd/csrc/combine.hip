@@ -10,14 +10,31 @@
 namespace moe {
 namespace {
 
+#ifndef MOE_COMBINE_GROUP  // slots whose row loads are issued together
+#define MOE_COMBINE_GROUP 4
+#endif
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// bf16 expert rows are read with the non-temporal hint (each is read once: e384_fp8's
+// combine 0.122 -> 0.096 ms); fp32 rows with cached loads (the hint measured 2% slower on
+// r1_prefill's 2.1 GB of fp32 rows).
+template <bool kNT, typename V>
+__device__ __forceinline__ V ld16(const V* p) {
+  if (kNT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
 template <bool kYF32>
 __device__ __forceinline__ void load8f(const void* base, int64_t off, float* v) {
   if (kYF32) {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const f32x4v* p = reinterpret_cast<const f32x4v*>(reinterpret_cast<const float*>(base) + off);
+    const f32x4v a = ld16<false>(p), b = ld16<false>(p + 1);
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3]; v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
   } else {
-    uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
+    const u32x4v qv = ld16<true>(reinterpret_cast<const u32x4v*>(reinterpret_cast<const uint16_t*>(base) + off));
+    const uint4 q = make_uint4(qv[0], qv[1], qv[2], qv[3]);
     v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
     v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
   }
@@ -49,23 +66,24 @@ __global__ void __launch_bounds__(256) k_combine(const void* __restrict__ y,
   const int h = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (h >= H) return;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  // slots in groups of four: the group's row loads are all issued before the first is
-  // used; the sum still runs in slot order
-  for (int j0 = 0; j0 < k; j0 += 4) {
+  // slots in groups of G: the group's row loads are all issued before the first is used;
+  // the sum still runs in slot order
+  constexpr int G = MOE_COMBINE_GROUP;
+  for (int j0 = 0; j0 < k; j0 += G) {
     const int64_t a = (int64_t)t * k + j0;
-    const int nj = k - j0 < 4 ? k - j0 : 4;
-    int r[4];
-    float wj[4], v[4][8];
+    const int nj = k - j0 < G ? k - j0 : G;
+    int r[G];
+    float wj[G], v[G][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < G; ++j) {
       r[j] = j < nj ? inv_perm[a + j] : 0;
       wj[j] = j < nj ? w[a + j] : 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G; ++j)
       if (j < nj) load8f<kYF32>(y, (int64_t)r[j] * H + h, v[j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G; ++j)
       if (j < nj) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += wj[j] * v[j][i];

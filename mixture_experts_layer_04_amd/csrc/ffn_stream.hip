@@ -79,6 +79,9 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
 #ifndef MOE_STREAM_ROWS_DN  // 16-row weight groups per wavefront (bf16 down)
 #define MOE_STREAM_ROWS_DN 4
 #endif
+#ifndef MOE_STREAM_ROWS_DN_WIDE  // the same where H is a multiple of 16 of them: a
+#define MOE_STREAM_ROWS_DN_WIDE 8  // workgroup's h rows then serve twice the weight rows
+#endif
 #ifndef MOE_STREAM_UNROLL_DN
 #define MOE_STREAM_UNROLL_DN 8
 #endif
@@ -97,6 +100,7 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
 // end) and write h or y past the row's end.
 static_assert(64 % (16 * MOE_STREAM_ROWS_GU) == 0, "gate/up row groups must tile I % 64");
 static_assert(64 % (16 * MOE_STREAM_ROWS_DN) == 0, "down row groups must tile H % 64");
+// (the wide down variant is launched only where 16 MOE_STREAM_ROWS_DN_WIDE divides H)
 // Weight fragment: ordinary cached loads (on MI355X they measured faster than
 // non-temporal ones for this many-rows-at-once pattern).
 __device__ __forceinline__ Frag32 load_w(const void* p) { return load_c(p); }
@@ -870,7 +874,7 @@ __global__ void __launch_bounds__(256) k_down_stream_mx(FfnArgs a, int fb_per_ti
 bool ffn_stream_mx_ok(int32_t H, int32_t I) { return H % kMxStreamK == 0 && I % kMxStreamK == 0; }
 
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
-  constexpr int RG = MOE_STREAM_ROWS_GU, RD = MOE_STREAM_ROWS_DN;
+  constexpr int RG = MOE_STREAM_ROWS_GU, RD = MOE_STREAM_ROWS_DN, RDW = MOE_STREAM_ROWS_DN_WIDE;
   constexpr int KSG = MOE_STREAM_KSPLIT_GU;
   const int fb_gu = (a.I_max + kFeatPerWG / KSG * RG - 1) / (kFeatPerWG / KSG * RG);
   constexpr int KSD = MOE_STREAM_KSPLIT_DN;
@@ -904,7 +908,15 @@ hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s, hipEvent_t mid_eve
     hipLaunchKernelGGL((k_down_stream<true, true, 1>), dim3(a.max_tiles * fb_dn1), blk, 0, s, a, fb_dn1);
   else if (f32)
     hipLaunchKernelGGL((k_down_stream<true, false, 1>), dim3(a.max_tiles * fb_dn1), blk, 0, s, a, fb_dn1);
-  else if (yf32)
+  else if (a.H % (16 * RDW) == 0) {
+    // 16 RDW output features a wavefront (r1_decode: down 0.750 -> 0.728 ms against 16 RD):
+    // each workgroup loads its tile's h rows once for twice the weight rows
+    const int fb_dw = a.H / (kFeatPerWG / KSD * RDW);
+    if (yf32)
+      hipLaunchKernelGGL((k_down_stream<false, true, RDW>), dim3(a.max_tiles * fb_dw), blk, 0, s, a, fb_dw);
+    else
+      hipLaunchKernelGGL((k_down_stream<false, false, RDW>), dim3(a.max_tiles * fb_dw), blk, 0, s, a, fb_dw);
+  } else if (yf32)
     hipLaunchKernelGGL((k_down_stream<false, true, RD>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);
   else
     hipLaunchKernelGGL((k_down_stream<false, false, RD>), dim3(a.max_tiles * fb_dn), blk, 0, s, a, fb_dn);

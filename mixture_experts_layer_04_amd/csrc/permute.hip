@@ -20,6 +20,9 @@ namespace moe {
 namespace {
 
 constexpr int kScanThreads = 1024;
+#ifndef MOE_SCAN_UNROLL  // blocks whose counts one scan thread loads at once (1 -> 8:
+#define MOE_SCAN_UNROLL 8   // k_scan 19.5 -> 12 us at e384_fp8)
+#endif
 
 __global__ void __launch_bounds__(64) k_hist(const int32_t* __restrict__ topk_idx, int T, int k,
                                              int E, uint64_t* __restrict__ masks,
@@ -93,8 +96,10 @@ __global__ void __launch_bounds__(kScanThreads) k_scan(int32_t* __restrict__ cnt
   const bool worker = part < P;
   const int b0 = part * C, b1 = min(nb, b0 + C);
   int s = 0;
-  if (worker)
+  if (worker) {
+#pragma unroll MOE_SCAN_UNROLL
     for (int b = b0; b < b1; ++b) s += cnt[(int64_t)b * E + pe];
+  }
   part_sum[tid] = worker ? s : 0;
   __syncthreads();
   // per expert: exclusive prefix over its parts, and its total
@@ -116,6 +121,7 @@ __global__ void __launch_bounds__(kScanThreads) k_scan(int32_t* __restrict__ cnt
   __syncthreads();
   if (worker) {
     int run = sh[pe] + pre;
+#pragma unroll MOE_SCAN_UNROLL
     for (int b = b0; b < b1; ++b) {
       const int c = cnt[(int64_t)b * E + pe];
       cnt[(int64_t)b * E + pe] = run;
