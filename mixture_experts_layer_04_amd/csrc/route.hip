@@ -501,6 +501,7 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
   // exact dot products below)
   const uint16_t* xr = x + (int64_t)t * H;
   double nx2 = 0.0;
+#pragma unroll 7  // the row's loads in flight together (H = 7168: all 14); the sum keeps its order
   for (int h = 8 * l; h < H; h += 512) {
     const uint4 q = *reinterpret_cast<const uint4*>(xr + h);
     const double v0 = bf16_lo(q.x), v1 = bf16_hi(q.x), v2 = bf16_lo(q.y), v3 = bf16_hi(q.y);
