@@ -11,7 +11,11 @@ Besides layer tokens/s the line carries:
   roofline      the dominant kernel (grouped gate/up + SwiGLU) timed with HIP events
                 recorded by the library around it on the stream it runs on; its
                 algorithmic bytes (touched experts' gate/up weights + activation rows read
-                + h written) per launch over its average duration, against 8 TB/s HBM.
+                + h written) per launch over its average duration, against 8 TB/s HBM;
+                also against the device's measured peak of the same bound (a streaming
+                read, or a dense MFMA loop, run by the library's measurement probes in the
+                same process): measured_peak and frac_of_measured; for an MFMA-bound launch
+                also against min(MFMA peak, AI x HBM peak): attainable, frac_of_attainable.
   cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the same batch
                 (the first few tokens; routing covers all tokens), tokens/s.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
@@ -49,6 +53,8 @@ def parse():
                          "(the prefill batch timed after a decode workload always gets it)")
     ap.add_argument("--cpu-tokens", type=int, default=72,
                     help="tokens of the batch the CPU oracle leg computes (about 10 s of CPU work)")
+    ap.add_argument("--no-measured-peaks", dest="measured_peaks", action="store_false",
+                    help="skip the streaming-read and MFMA-loop probes of the device's rates")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (a known-size "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -195,6 +201,64 @@ def percentile(v, q):
     import numpy as np
 
     return float(np.percentile(np.asarray(v, np.float64), q))
+
+
+# the matrix-core product each weight format is computed with (MXFP4 weights are decoded to
+# bf16 and multiplied on the bf16 MFMA), as moe_probe_mfma names it
+PROBE_DTYPE = {"bf16": "bf16", "fp8": "fp8", "int8": "int8", "mxfp4": "bf16",
+               "mxfp4a4": "mxfp4a4"}
+
+
+def measured_peaks(dtypes, read_gib=4):
+    """The device's measured rates, for fractions against measured peaks beside the
+    datasheet ones: one non-temporal streaming read of read_gib GiB (moe_probe_hbm_read)
+    and dense MFMA loops on register operands at four wavefronts a SIMD on every CU
+    (moe_probe_mfma), each timed with events on the stream it runs on; the best of five
+    runs after a warm-up."""
+    import torch
+
+    import mixture_experts_layer_04_amd as moe
+
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_s(fn):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(5):
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b) / 1e3)
+        return min(t)
+
+    buf = torch.empty(read_gib << 30, dtype=torch.uint8, device="cuda")
+    res = {"hbm_read_GBs": buf.numel() / best_s(lambda: moe.moe_probe_hbm_read(buf, sink)) / 1e9}
+    del buf
+    for dt in sorted(set(dtypes)):
+        iters = 20000
+        flops = moe.moe_probe_mfma(dt, iters, sink)  # the same count every launch
+        res[f"{dt}_mfma_TFLOPs"] = flops / best_s(lambda: moe.moe_probe_mfma(dt, iters, sink)) / 1e12
+    log("measured peaks: " + ", ".join(f"{k}={v:.1f}" for k, v in res.items()))
+    return res
+
+
+def add_measured(roofline, peaks, wdt):
+    """Fractions of the dominant kernel against the measured peak of its bound and, for an
+    MFMA-bound launch, against the attainable min(peak, AI x HBM peak)."""
+    if roofline["bound"] == "hbm":
+        m = peaks["hbm_read_GBs"]
+    else:
+        m = peaks[f"{PROBE_DTYPE[wdt]}_mfma_TFLOPs"]
+        ai = roofline["algorithmic_flops_per_launch"] / roofline["algorithmic_bytes_per_launch"]
+        att = min(roofline["peak"], ai * HBM_PEAK_GBS / 1e3)
+        roofline["attainable"] = att
+        roofline["frac_of_attainable"] = roofline["achieved"] / att
+    roofline["measured_peak"] = m
+    roofline["frac_of_measured"] = roofline["achieved"] / m
 
 
 def run_workload(cfg, dev, args, overlap=False):
@@ -402,6 +466,15 @@ def main():
                    "down_frac": p["down_frac"],
                    "roofline": p["roofline"]}
         del pdev
+
+    # measured peaks of the device (measurement probes), for fractions of measured peaks
+    probes = [PROBE_DTYPE[c.wdt] for c in ([cfg] + ([CONFIGS[pname]] if prefill else []))
+              if c.wdt in PROBE_DTYPE]
+    if args.measured_peaks:
+        peaks = measured_peaks(probes)
+        add_measured(r["roofline"], peaks, cfg.wdt)
+        if prefill:
+            add_measured(prefill["roofline"], peaks, CONFIGS[pname].wdt)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20)

@@ -338,6 +338,28 @@ moe_status moe_bias_update(const int32_t* counts, int32_t E, float u, float* bia
 moe_status moe_quantize_mxfp4(const void* x, int32_t n, int32_t H, uint8_t* q, uint8_t* q_scale,
                               void* stream);
 
+/* ---------------------------------------------------------------- measurement probes */
+
+/* Not part of the layer: two kernels that measure the device's achievable rates, so that a
+ * benchmark can state a kernel's fraction of a measured peak beside the datasheet one.
+ *
+ * moe_probe_hbm_read reads `bytes` of device memory at `buf` once, with non-temporal 16-B
+ * loads: each wavefront streams its own contiguous chunk, 1 KB per instruction, sixteen
+ * instructions in flight, two 256-thread workgroups a CU. bytes: a positive multiple of
+ * 16; buf 16-byte aligned. `sink` (device, 4 bytes, caller-owned) is written only if the
+ * XOR of all data read equals a fixed mark, which keeps the loads from being dropped. Time
+ * the call with events on `stream`. MOE_ERR_SHAPE for bytes out of range. */
+moe_status moe_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/* moe_probe_mfma runs four wavefronts a SIMD on every CU, each issuing `iters` rounds of
+ * eight independent dense MFMAs on register operands: MOE_BF16 v_mfma_f32_16x16x32_bf16,
+ * MOE_FP8_E4M3 v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), MOE_INT8
+ * v_mfma_i32_16x16x64_i8, MOE_MXFP4_A4 the same scaled instruction with both operands E2M1.
+ * *flops (host) receives the operations the launch executes (2 per multiply-add). sink as
+ * above. MOE_ERR_DTYPE for another dtype, MOE_ERR_SHAPE for iters outside [1, 2^30]. */
+moe_status moe_probe_mfma(moe_dtype dtype, int64_t iters, uint32_t* sink, double* flops,
+                          void* stream);
+
 const char* moe_status_str(moe_status s);
 const char* moe_last_hip_error(void); /* thread-local text of the last MOE_ERR_HIP */
 

@@ -57,7 +57,7 @@ EXPORTS = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size"
            "moe_layer_forward_overlap", "moe_layer_forward_noalloc", "moe_layer_forward_split",
            "moe_rows_workspace_size",
            "moe_rows_forward", "moe_rows_forward_timed", "moe_quantize_fp8", "moe_quantize_mxfp4", "moe_quantize_int8", "moe_bias_update",
-           "moe_status_str",
+           "moe_probe_hbm_read", "moe_probe_mfma", "moe_status_str",
            "moe_last_hip_error"]
 
 
@@ -109,6 +109,10 @@ def lib():
     L.moe_quantize_mxfp4.restype = ci
     L.moe_bias_update.argtypes = [vp, i32, f32, vp, vp]
     L.moe_bias_update.restype = ci
+    L.moe_probe_hbm_read.argtypes = [vp, sz, vp, vp]
+    L.moe_probe_hbm_read.restype = ci
+    L.moe_probe_mfma.argtypes = [ci, ctypes.c_int64, vp, P(ctypes.c_double), vp]
+    L.moe_probe_mfma.restype = ci
     L.moe_status_str.argtypes = [ci]
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_last_hip_error.argtypes = []
@@ -424,6 +428,24 @@ def moe_bias_update(counts, u: float, bias, stream=None):
         raise ValueError(f"counts has {counts.numel()} experts, bias {bias.numel()}")
     st = lib().moe_bias_update(_ptr(counts), counts.numel(), float(u), _ptr(bias), _stream(stream))
     _check(st, "moe_bias_update")
+
+
+def moe_probe_hbm_read(buf, sink, stream=None):
+    """Measurement probe: one non-temporal streaming read of the whole of `buf` (a device
+    tensor of a multiple of 16 bytes); sink: a device int32/uint32 tensor of >= 1 element."""
+    st = lib().moe_probe_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                  _stream(stream))
+    _check(st, "moe_probe_hbm_read")
+
+
+def moe_probe_mfma(dtype: str, iters: int, sink, stream=None) -> float:
+    """Measurement probe: `iters` rounds of dense MFMAs ("bf16", "fp8", "int8" or "mxfp4a4",
+    the FP4 product) on every CU; returns the operations the launch executes."""
+    flops = ctypes.c_double(0.0)
+    st = lib().moe_probe_mfma(DTYPES[dtype], int(iters), _ptr(sink), ctypes.byref(flops),
+                              _stream(stream))
+    _check(st, "moe_probe_mfma")
+    return flops.value
 
 
 def moe_rows_workspace_size(experts: Experts, act_dtype, rows: int) -> int:

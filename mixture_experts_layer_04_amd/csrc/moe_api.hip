@@ -784,4 +784,24 @@ moe_status moe_quantize_mxfp4(const void* x, int32_t n, int32_t H, uint8_t* q, u
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_mxfp4");
 }
 
+// ------------------------------------------------------------- measurement probes
+
+moe_status moe_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0 || bytes % 16 || bytes > ((size_t)1 << 40)) return MOE_ERR_SHAPE;
+  if (!buf || !sink) return MOE_ERR_NULL;
+  if (!al16(buf)) return MOE_ERR_ALIGN;
+  hipError_t e = launch_probe_read(buf, (int64_t)bytes, sink, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_probe_hbm_read");
+}
+
+moe_status moe_probe_mfma(moe_dtype dtype, int64_t iters, uint32_t* sink, double* flops,
+                          void* stream) {
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3 && dtype != MOE_INT8 && dtype != MOE_MXFP4_A4)
+    return MOE_ERR_DTYPE;
+  if (iters < 1 || iters > (1 << 30)) return MOE_ERR_SHAPE;
+  if (!sink || !flops) return MOE_ERR_NULL;
+  hipError_t e = launch_probe_mfma(dtype, iters, sink, flops, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_probe_mfma");
+}
+
 }  // extern "C"

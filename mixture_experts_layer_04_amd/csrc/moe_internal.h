@@ -166,4 +166,9 @@ hipError_t launch_combine(const void* y, moe_dtype y_dt, const int32_t* inv_perm
                           const float* topk_w, int32_t T, int32_t k, int32_t H,
                           const void* shared, void* out, moe_dtype out_dt, hipStream_t s);
 
+// probe.hip (measurement probes, not part of the layer)
+hipError_t launch_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_mfma(moe_dtype dt, int64_t iters, uint32_t* sink, double* flops,
+                             hipStream_t s);
+
 }  // namespace moe

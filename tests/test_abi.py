@@ -245,3 +245,19 @@ def test_noalloc_rejects_layers_beyond_its_static_workspace():
     # and the usual argument checks come first
     d.k = 300
     assert L.moe_layer_forward_noalloc(ctypes.byref(d), P, P, None, None, None, None, None) == moe.MOE_ERR_SHAPE
+
+
+def test_probe_validation():
+    """The measurement probes check their arguments before any launch."""
+    L = moe.lib()
+    f = ctypes.c_double(0.0)
+    assert L.moe_probe_hbm_read(P, 0, P, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_probe_hbm_read(P, 1000, P, None) == moe.MOE_ERR_SHAPE   # not a multiple of 16
+    assert L.moe_probe_hbm_read(None, 1024, P, None) == moe.MOE_ERR_NULL
+    assert L.moe_probe_hbm_read(P, 1024, None, None) == moe.MOE_ERR_NULL
+    assert L.moe_probe_hbm_read(MISALIGNED, 1024, P, None) == moe.MOE_ERR_ALIGN
+    assert L.moe_probe_mfma(moe.MOE_F32, 10, P, ctypes.byref(f), None) == moe.MOE_ERR_DTYPE
+    assert L.moe_probe_mfma(moe.MOE_MXFP4, 10, P, ctypes.byref(f), None) == moe.MOE_ERR_DTYPE
+    assert L.moe_probe_mfma(moe.MOE_BF16, 0, P, ctypes.byref(f), None) == moe.MOE_ERR_SHAPE
+    assert L.moe_probe_mfma(moe.MOE_BF16, 10, None, ctypes.byref(f), None) == moe.MOE_ERR_NULL
+    assert L.moe_probe_mfma(moe.MOE_BF16, 10, P, None, None) == moe.MOE_ERR_NULL
