@@ -88,6 +88,9 @@ __device__ __forceinline__ void store4(void* base, int64_t off, f32x4 v) {
 #ifndef MOE_STREAM_UNROLL_DN_LINES  // K steps per iteration of the bf16 down kernel
 #define MOE_STREAM_UNROLL_DN_LINES 1
 #endif
+#ifndef MOE_STREAM_CACHED_MULTI  // weights of groups of several tiles read through the cache
+#define MOE_STREAM_CACHED_MULTI 1
+#endif
 #ifndef MOE_STREAM_KSPLIT_GU  // gate/up: wavefronts that share one row group, each a K range
 #define MOE_STREAM_KSPLIT_GU 4
 #endif
@@ -126,10 +129,18 @@ __device__ __forceinline__ WLane wlane(int m, int kq, uint32_t row_bytes) {
   return WLane{(uint32_t)(m & 7) * row_bytes + (uint32_t)(kq + 4 * (m >> 3)) * 16,
                (uint32_t)(8 + (m & 7)) * row_bytes + (uint32_t)(kq + 4 * (1 - (m >> 3))) * 16, m < 8};
 }
+// kNT: with the non-temporal hint (weights read once); without it for groups of more than
+// one tile, whose tiles read the same weights and share them only through the cache.
+template <bool kNT = true>
 __device__ __forceinline__ WRaw load_w_lines(const char* group, const WLane& w) {
   WRaw r;
-  r.g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(group + w.o0));
-  r.g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(group + w.o1));
+  if constexpr (kNT) {
+    r.g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(group + w.o0));
+    r.g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(group + w.o1));
+  } else {
+    r.g0 = *reinterpret_cast<const u32x4*>(group + w.o0);
+    r.g1 = *reinterpret_cast<const u32x4*>(group + w.o1);
+  }
   return r;
 }
 __device__ __forceinline__ Frag32 w_frag(const WRaw& r, bool lo8) {
@@ -234,8 +245,9 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
     const char* xq = reinterpret_cast<const char*>(a.a) + src * H * 2 + kq * 16;
     const char* g0 = w13 + (int64_t)f0 * H * 2;
     const char* u0 = w13 + (int64_t)(I + f0) * H * 2;
-    auto step = [&](int k0, auto uc) {
+    auto step = [&](int k0, auto uc, auto ntc) {
       constexpr int UU = decltype(uc)::value;
+      constexpr bool NT = decltype(ntc)::value != 0;
       WRaw rg[UU][R], ru[UU][R];
       Frag32 fx[UU];
 #pragma unroll
@@ -243,8 +255,8 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
         const int64_t o = (int64_t)(k0 + u * 64) * 2;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          rg[u][r] = load_w_lines(g0 + (int64_t)16 * r * H * 2 + o, wl);
-          ru[u][r] = load_w_lines(u0 + (int64_t)16 * r * H * 2 + o, wl);
+          rg[u][r] = load_w_lines<NT>(g0 + (int64_t)16 * r * H * 2 + o, wl);
+          ru[u][r] = load_w_lines<NT>(u0 + (int64_t)16 * r * H * 2 + o, wl);
         }
         fx[u] = load_x_perm(xq + o, xv);
       }
@@ -258,8 +270,16 @@ __global__ void __launch_bounds__(256) k_gateup_stream(FfnArgs a, int fb_per_til
     };
     constexpr int UB = MOE_STREAM_UNROLL_GU_BF16;
     const int kmb = kend - (kend - kbeg) % (64 * UB);
-    for (int k0 = kbeg; k0 < kmb; k0 += 64 * UB) step(k0, IntC<UB>{});
-    for (int k0 = kmb; k0 < kend; k0 += 64) step(k0, IntC<1>{});
+    // a group of one tile streams its weights past the cache; the tiles of a larger group
+    // (a hot expert, the shared expert) read them through it, where they meet: with the
+    // hint on every group the second tile of each 17-32-row expert fetched the weights
+    // again (r1_decode gate/up 1.328 -> 1.291 ms, down 0.726 -> 0.708 ms)
+    auto kloop = [&](auto ntc) {
+      for (int k0 = kbeg; k0 < kmb; k0 += 64 * UB) step(k0, IntC<UB>{}, ntc);
+      for (int k0 = kmb; k0 < kend; k0 += 64) step(k0, IntC<1>{}, ntc);
+    };
+    if (!MOE_STREAM_CACHED_MULTI || tl.nblk == 1) kloop(IntC<1>{});
+    else kloop(IntC<0>{});
   } else {
     // fp32: each lane's 32 contiguous bytes of its row per step (cached loads), K index
     // k0 + 8 kq + j in both operands
@@ -411,8 +431,9 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
     const char* hq = reinterpret_cast<const char*>(a.h) + hrow * a.I_max * 2 + kq * 16;
     const uint8_t* lq = a.h_lo + hrow * (a.I_max / 2) + kq * 4;
     const uint8_t* lsb = a.h_lo_s + hrow * lo_sstride(a.I_max);
-    auto step = [&](int k0, auto uc) {
+    auto step = [&](int k0, auto uc, auto ntc) {
       constexpr int UU = decltype(uc)::value;
+      constexpr bool NT = decltype(ntc)::value != 0;
       WRaw rw[UU][R];
       Frag32 fh[UU], fl[UU];
 #pragma unroll
@@ -420,7 +441,7 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
         const int64_t o = (int64_t)(k0 + u * 64) * 2;
 #pragma unroll
         for (int r = 0; r < R; ++r)
-          rw[u][r] = load_w_lines(w2 + (int64_t)(f0 + 16 * r) * I * 2 + o, wl);
+          rw[u][r] = load_w_lines<NT>(w2 + (int64_t)(f0 + 16 * r) * I * 2 + o, wl);
         fh[u] = load_x_perm(hq + o, xv);
         fl[u] = load_lo_perm(lq, lsb, k0 + u * 64, xv);
       }
@@ -435,8 +456,12 @@ __global__ void __launch_bounds__(256) k_down_stream(FfnArgs a, int fb_per_tile)
     };
     constexpr int UB = MOE_STREAM_UNROLL_DN_LINES;
     const int kmb = kend - (kend - kbeg) % (64 * UB);
-    for (int k0 = kbeg; k0 < kmb; k0 += 64 * UB) step(k0, IntC<UB>{});
-    for (int k0 = kmb; k0 < kend; k0 += 64) step(k0, IntC<1>{});
+    auto kloop = [&](auto ntc) {  // as in the gate/up launch
+      for (int k0 = kbeg; k0 < kmb; k0 += 64 * UB) step(k0, IntC<UB>{}, ntc);
+      for (int k0 = kmb; k0 < kend; k0 += 64) step(k0, IntC<1>{}, ntc);
+    };
+    if (!MOE_STREAM_CACHED_MULTI || tl.nblk == 1) kloop(IntC<1>{});
+    else kloop(IntC<0>{});
   } else {
     // fp32: each lane's 32 contiguous bytes of its row per step (cached loads), K index
     // k0 + 8 kq + j in both operands
@@ -600,6 +625,8 @@ struct MxLines {
   uint32_t sc[2 * U];
 };
 // grp: the group's first row's codes at the iteration's start; scales: this lane's row's
+// (Reading the codes of groups of several tiles through the cache, as the bf16 kernels do,
+// measured slower here: r1_decode_mxfp4 gate/up 0.425 -> 0.454 ms.)
 template <int U>
 __device__ __forceinline__ MxLines<U> load_mx_lines(const uint8_t* grp, const WLane& wl,
                                                     const uint8_t* scales) {
