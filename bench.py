@@ -107,7 +107,15 @@ def cpu_baseline(cfg, host, n_tokens):
     res = O.layer_forward(host, tokens=tokens)
     dt = time.perf_counter() - t0
     assert res["out"].shape[0] == len(tokens)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         None)
+    except OSError:  # pragma: no cover
+        pass
     return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"{len(tokens)} of {cfg.T} tokens of the same batch (routing of all {cfg.T} "
                       f"tokens, {len(used)} routed experts + shared expert FFNs in float64), "
                       f"{dt:.1f} s"}

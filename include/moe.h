@@ -79,6 +79,9 @@ typedef enum {
  *           (one scale per 128 x 128 block; value = code * scale). H, I multiples of 128.
  * MXFP4:    w13 bytes [E, 2I, H/2], w2 bytes [E, H, I/2]; w13_scale u8 [E, 2I, H/32],
  *           w2_scale u8 [E, H, I/32] (value = e2m1 * 2^(scale - 127)). H, I multiples of 128.
+ *           A scale byte of 0xFF (NaN in the OCP format) makes its block non-finite: the
+ *           batched (tiled) kernels decode it as +Inf (zero codes give NaN, others +-Inf),
+ *           the decode-sized ones as NaN.
  * MXFP4_A4: the MXFP4 layout; activations BF16 in, quantised inside. H, I multiples of 128.
  * INT8:     w13 int8 [E, 2I, H], w2 int8 [E, H, I]; w13_scale f32 [E, 2I/128, H/128],
  *           w2_scale f32 [E, H/128, I/128] (value = code * scale; the W8A8 weights of

@@ -67,6 +67,13 @@ __device__ __forceinline__ float e8m0_f32(uint32_t c) {
   bits = c == 0xFFu ? 0x7FC00000u : bits;  // NaN
   return __uint_as_float(bits);
 }
+// The same in two instructions for codes 0..254 (exact, 0 giving 2^-127); code 0xFF gives
+// +Inf instead of NaN, so that a block with a NaN scale decodes to infinities (non-zero
+// codes) and NaNs (zero codes). For the tiled MXFP4 kernel's weight scales (ep32_mxfp4
+// gate/up 0.913 -> 0.890 ms against e8m0_f32) and h's residual, whose writer emits 0..254.
+__device__ __forceinline__ float e8m0_f32_fast(uint32_t c) {
+  return __uint_as_float(max(c << 23, 0x00400000u));
+}
 
 // Eight E2M1 values (one 32-bit word, low nibble first) times their E8M0 block scale, as
 // the bf16 fragment of one MFMA k-step (v_cvt_scalef32_pk_bf16_fp4 is exact: every

@@ -192,8 +192,8 @@ __device__ __forceinline__ Frag32 load_lo_perm(const uint8_t* lr, const uint8_t*
   const uint32_t q0 = *reinterpret_cast<const uint32_t*>(lr + k0 / 2);
   const uint32_t q1 = *reinterpret_cast<const uint32_t*>(lr + k0 / 2 + 16);
   const uint32_t sc = *reinterpret_cast<const uint16_t*>(ls + k0 / 32);
-  f.lo = __builtin_bit_cast(u32x4, e2m1x8_bf16(q0, e8m0_f32(sc & 0xFFu)));
-  f.hi = __builtin_bit_cast(u32x4, e2m1x8_bf16(q1, e8m0_f32(sc >> 8)));
+  f.lo = __builtin_bit_cast(u32x4, e2m1x8_bf16(q0, e8m0_f32_fast(sc & 0xFFu)));
+  f.hi = __builtin_bit_cast(u32x4, e2m1x8_bf16(q1, e8m0_f32_fast(sc >> 8)));
   return f;
 }
 

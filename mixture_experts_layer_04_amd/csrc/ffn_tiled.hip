@@ -298,7 +298,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
           // two 32-bit reads: with one 64-bit read the compiler makes it wait for all DMA
           wq[t].x = *reinterpret_cast<const uint32_t*>(q + 512 * t);
           wq[t].y = *reinterpret_cast<const uint32_t*>(q + 512 * t + 4);
-          wsc[t] = e8m0_f32(*reinterpret_cast<const uint8_t*>(sc + 64 * t));
+          wsc[t] = e8m0_f32_fast(*reinterpret_cast<const uint8_t*>(sc + 64 * t));
         }
       }
       // bf16 down: the block scale of this lane's 16 residual elements of each A row (the
