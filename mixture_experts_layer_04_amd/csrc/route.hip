@@ -311,9 +311,11 @@ __global__ void __launch_bounds__(256) k_topk(const double* __restrict__ part, i
 // sigmoid; for softmax, in the own logit and non-increasing in the others), and takes the
 // k experts of the largest approximate keys only if every chosen interval lies strictly
 // above every other one. The exact keys then choose the same k experts, and their exact
-// fp64 dot products give the fp32 logits and the weights. A token without that
-// separation (near-ties, non-finite values) is appended to a list that the exact kernels
-// 1 and 2 then route.
+// fp64 dot products give the fp32 logits and the weights. Where the intervals overlap,
+// the same wavefront takes exact logits of the few experts that can still be chosen (at
+// most 16) and chooses among them (k_topk_fast describes how). A token that this leaves
+// undecided (more candidates, keys equal to within the bounds, non-finite values) is
+// appended to a list that the exact kernels 1 and 2 then route.
 //
 // The bound. A block sum of 64 exact products formed with fp32 additions, in whatever
 // order the matrix core adds and as long as each addition errs by at most 2^-23 of its
@@ -487,15 +489,65 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// At most this many candidate experts are refined in k_topk_fast (two passes of eight).
+constexpr int kRefineMax = 16;
+#ifndef MOE_LOGIT_UNROLL  // chunks of the exact dot products whose loads go out together
+#define MOE_LOGIT_UNROLL 1   // (2: the same speed with registers spilled at 3 workgroups a CU)
+#endif
+#ifndef MOE_TOPK_FAST_WGS  // workgroups a CU that k_topk_fast's register budget allows
+#define MOE_TOPK_FAST_WGS 2  // (3: route step 7-10 us longer at e384_fp8 and r1_prefill)
+#endif
+
+// Exact logits of token row xr against router rows ids[0..8): fp64 dot products of the
+// bf16 values (each product exact), rounded once to fp32. Lane l takes the 8-element
+// chunks l, l + 64, ... of x and of the eight rows, whose loads of one chunk are issued
+// together.
+__device__ __forceinline__ void exact_logits8(const uint16_t* __restrict__ xr,
+                                              const uint16_t* __restrict__ wr, int H,
+                                              const int* ids, int l, double* out) {
+  int64_t woff[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) woff[r] = (int64_t)ids[r] * H;
+  double dot[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) dot[r] = 0.0;
+#pragma unroll MOE_LOGIT_UNROLL  // the sums keep their order whatever the unrolling
+  for (int h = 8 * l; h < H; h += 512) {
+    const uint4 a = *reinterpret_cast<const uint4*>(xr + h);
+    uint4 b[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) b[r] = *reinterpret_cast<const uint4*>(wr + woff[r] + h);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      double d = dot[r];
+      d += (double)bf16_lo(a.x) * (double)bf16_lo(b[r].x);
+      d += (double)bf16_hi(a.x) * (double)bf16_hi(b[r].x);
+      d += (double)bf16_lo(a.y) * (double)bf16_lo(b[r].y);
+      d += (double)bf16_hi(a.y) * (double)bf16_hi(b[r].y);
+      d += (double)bf16_lo(a.z) * (double)bf16_lo(b[r].z);
+      d += (double)bf16_hi(a.z) * (double)bf16_hi(b[r].z);
+      d += (double)bf16_lo(a.w) * (double)bf16_lo(b[r].w);
+      d += (double)bf16_hi(a.w) * (double)bf16_hi(b[r].w);
+      dot[r] = d;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) out[r] = (double)(float)wave_sum_f64(dot[r]);
+}
+
 template <int NPL>  // experts per lane: E <= 64 NPL
-__global__ void __launch_bounds__(256, 3) k_topk_fast(
+__global__ void __launch_bounds__(256, MOE_TOPK_FAST_WGS) k_topk_fast(
     const double* __restrict__ part, const double* __restrict__ nw2s, int S, int T, int H, int E,
     int k, int fn, float scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ wr, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ list, int32_t* __restrict__ cnt) {
-  const int l = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // per-wavefront slots for the refinement of a token whose choice the bounds leave open
+  __shared__ int r_id[4][kRefineMax];
+  __shared__ double r_lg[4][kRefineMax], r_t[4][kRefineMax];
+  __shared__ uint64_t r_lo[4][kRefineMax], r_hi[4][kRefineMax];
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + w;
   if (t >= T) return;
   // ||x_t||^2 in fp64 from the token's row (its chunks are read again, from cache, for the
   // exact dot products below)
@@ -592,6 +644,7 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
     }
   }
   int sel[16];
+  double lg[16];  // exact logits of the chosen experts, in the order of sel
   if (certified) {
     uint32_t chosen = 0u;  // bit i: expert 64 i + l is chosen
     for (int r = 0; r < k; ++r) {
@@ -614,55 +667,192 @@ __global__ void __launch_bounds__(256, 3) k_topk_fast(
     }
     certified = wave_min_u32(min_in) > wave_max_u32(max_out);
   }
-  if (!certified) {
-    if (l == 0) list[atomicAdd(cnt, 1)] = t;
-    return;
+  if (certified) {
+    for (int a = 1; a < k; ++a) {
+      int v = sel[a], b = a - 1;
+      while (b >= 0 && sel[b] > v) { sel[b + 1] = sel[b]; --b; }
+      sel[b + 1] = v;
+    }
+    // exact logits of the chosen experts
+    for (int r0 = 0; r0 < k; r0 += 8) {
+      int ids[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) ids[r] = r0 + r < k ? sel[r0 + r] : sel[r0];
+      double v[8];
+      exact_logits8(xr, wr, H, ids, l, v);
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r0 + r < k) lg[r0 + r] = v[r];
+    }
+  } else {
+    // Not separated. The experts that can be among the k largest exact keys are those
+    // whose upper key bound reaches L, the k-th largest lower bound: k experts have exact
+    // keys >= L, so an expert whose key lies below L is beaten k times. With at most
+    // kRefineMax of them (the candidates), their exact logits are computed and the k are
+    // chosen among them on key bounds that hold the exact path's keys: exact for sigmoid;
+    // for softmax the normaliser (a sum over all experts, the others' logits known to
+    // their intervals) is known to an interval, which is all that widens them. A token
+    // whose choice these bounds do not settle goes to the list for the exact kernels.
+    bool done = false;
+    if (__all(fin)) {
+      uint64_t kk[NPL];
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int e = i * 64 + l;
+        kk[i] = e < E ? ((uint64_t)klo[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+      }
+      uint64_t kth = 0ull;
+      for (int r = 0; r < k; ++r) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) best = kk[i] > best ? kk[i] : best;
+        kth = wave_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+          if (kk[i] == kth) kk[i] = 0ull;
+      }
+      const uint32_t L = (uint32_t)(kth >> 32);
+      uint64_t cm[NPL];
+      int nc = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        cm[i] = __ballot(i * 64 + l < E && khi[i] >= L);
+        nc += __popcll(cm[i]);
+      }
+      if (nc <= kRefineMax) {
+        // the candidates' data (uniform) in this wavefront's slots, candidates in
+        // increasing id order; written by lane 0 and read back by every lane
+        int* rid = r_id[w];
+        double* rlg = r_lg[w];
+        uint64_t* rlo = r_lo[w];
+        uint64_t* rhi = r_hi[w];
+        double* rt = r_t[w];
+        {
+          uint64_t m[NPL];
+#pragma unroll
+          for (int i = 0; i < NPL; ++i) m[i] = cm[i];
+          for (int j = 0; j < nc; ++j) {
+            int id = -1;
+#pragma unroll
+            for (int i = 0; i < NPL; ++i)
+              if (id < 0 && m[i] != 0ull) {
+                id = i * 64 + __builtin_ctzll(m[i]);
+                m[i] &= m[i] - 1ull;
+              }
+            if (l == 0) rid[j] = id;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        for (int j0 = 0; j0 < nc; j0 += 8) {
+          int ids[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) ids[r] = rid[j0 + r < nc ? j0 + r : j0];
+          double v[8];
+          exact_logits8(xr, wr, H, ids, l, v);
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            if (l == 0 && j0 + r < nc) rlg[j0 + r] = v[r];
+        }
+        __builtin_amdgcn_wave_barrier();
+        // key bounds of the candidates as 64-bit (key, ~id) values
+        double shi = 1.0;
+        if (fn == MOE_SIGMOID) {
+          for (int j = 0; j < nc; ++j) {
+            float kf = (float)(1.0 / (1.0 + exp(-rlg[j])));
+            if (bias) kf = kf + bias[rid[j]];
+            const uint64_t v = ((uint64_t)key_order(kf) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)rid[j]);
+            if (l == 0) { rlo[j] = v; rhi[j] = v; }
+          }
+        } else {
+          // the exact path's max is the largest exact logit, a candidate's; its sum of
+          // exp(logit - max) over all experts lies in [slo, shi]: the candidates' terms as
+          // it computes them, the others' from their logit bounds, widened by 2^-40 for
+          // the rounding of exp and of the sums in any order
+          double mx = -INFINITY;
+          for (int j = 0; j < nc; ++j) mx = fmax(mx, rlg[j]);
+          double slo = 0.0;
+          shi = 0.0;
+          int before = 0;  // candidates in the slots before this lane's expert of slot i
+#pragma unroll
+          for (int i = 0; i < NPL; ++i) {
+            const int e = i * 64 + l;
+            const uint64_t below = l ? cm[i] & (~0ull >> (64 - l)) : 0ull;
+            if (e < E) {
+              if (cm[i] >> l & 1ull) {
+                const double tc = exp(rlg[before + __popcll(below)] - mx);
+                slo += tc;
+                shi += tc;
+              } else {
+                slo += exp((double)lo[i] - mx);
+                shi += exp((double)hi[i] - mx);
+              }
+            }
+            before += __popcll(cm[i]);
+          }
+          slo = wave_sum_f64(slo) * (1.0 - 0x1p-40);
+          shi = wave_sum_f64(shi) * (1.0 + 0x1p-40);
+          for (int j = 0; j < nc; ++j) {
+            const double tc = exp(rlg[j] - mx);
+            float a = (float)(tc / shi), b = (float)(tc / slo);
+            if (bias) { a = a + bias[rid[j]]; b = b + bias[rid[j]]; }
+            const uint64_t id = (uint64_t)(0xFFFFFFFFu - (uint32_t)rid[j]);
+            if (l == 0) {
+              rt[j] = tc;
+              rlo[j] = ((uint64_t)key_order(a) << 32) | id;
+              rhi[j] = ((uint64_t)key_order(b) << 32) | id;
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // Softmax without bias: every key is fp32(t / S) with the same S, so a candidate
+        // whose t exceeds another's by more than a factor 1 + 2^-22 (with keys above the
+        // subnormal range) has the strictly larger key whatever S is; the choice is then
+        // made by t.
+        const bool by_t = fn != MOE_SIGMOID && !bias;
+        uint32_t cho = 0u;
+        for (int r = 0; r < k; ++r) {
+          int bj = -1;
+          for (int j = 0; j < nc; ++j) {
+            if (cho >> j & 1u) continue;
+            // candidates are in increasing id order: a later one wins only if larger
+            if (bj < 0 || (by_t ? rt[j] > rt[bj] : rlo[j] > rlo[bj])) bj = j;
+          }
+          if (bj >= 0) cho |= 1u << bj;
+        }
+        // settled if the weakest chosen candidate certainly beats the strongest other
+        uint64_t min_in = ~0ull, max_out = 0ull;
+        double tmin = INFINITY, tmax = 0.0;
+        for (int j = 0; j < nc; ++j) {
+          if (cho >> j & 1u) {
+            min_in = rlo[j] < min_in ? rlo[j] : min_in;
+            if (by_t) tmin = fmin(tmin, rt[j]);
+          } else {
+            max_out = rhi[j] > max_out ? rhi[j] : max_out;
+            if (by_t) tmax = fmax(tmax, rt[j]);
+          }
+        }
+        const bool sep = __builtin_popcount(cho) == k &&
+                         (min_in > max_out ||
+                          (by_t && tmin > tmax * (1.0 + 0x1p-22) && tmax / shi >= 0x1p-100));
+        if (sep) {
+          int r = 0;
+          for (int j = 0; j < nc; ++j)
+            if (cho >> j & 1u) {
+              sel[r] = rid[j];
+              lg[r] = rlg[j];
+              ++r;
+            }
+          done = true;
+        }
+      }
+    }
+    if (!done) {
+      if (l == 0) list[atomicAdd(cnt, 1)] = t;
+      return;
+    }
   }
-  for (int a = 1; a < k; ++a) {
-    int v = sel[a], b = a - 1;
-    while (b >= 0 && sel[b] > v) { sel[b + 1] = sel[b]; --b; }
-    sel[b + 1] = v;
-  }
-  // exact logits of the chosen experts: fp64 dot products, rounded once to fp32. Lane l
-  // takes the 8-element chunks l, l + 64, ... of x and of the chosen router rows, eight
-  // experts at a time, whose loads of one chunk are issued together.
-  double lg[16];
   double mx = -INFINITY;
-  for (int r0 = 0; r0 < k; r0 += 8) {
-    int woff[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) woff[r] = (r0 + r < k ? sel[r0 + r] : sel[r0]) * H;
-    double dot[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) dot[r] = 0.0;
-    for (int h = 8 * l; h < H; h += 512) {
-      const uint4 a = *reinterpret_cast<const uint4*>(xr + h);
-      uint4 b[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) b[r] = *reinterpret_cast<const uint4*>(wr + woff[r] + h);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        double d = dot[r];
-        d += (double)bf16_lo(a.x) * (double)bf16_lo(b[r].x);
-        d += (double)bf16_hi(a.x) * (double)bf16_hi(b[r].x);
-        d += (double)bf16_lo(a.y) * (double)bf16_lo(b[r].y);
-        d += (double)bf16_hi(a.y) * (double)bf16_hi(b[r].y);
-        d += (double)bf16_lo(a.z) * (double)bf16_lo(b[r].z);
-        d += (double)bf16_hi(a.z) * (double)bf16_hi(b[r].z);
-        d += (double)bf16_lo(a.w) * (double)bf16_lo(b[r].w);
-        d += (double)bf16_hi(a.w) * (double)bf16_hi(b[r].w);
-        dot[r] = d;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const double v = (double)(float)wave_sum_f64(dot[r]);
-      if (r0 + r < k) {
-        lg[r0 + r] = v;
-        mx = fmax(mx, v);
-      }
-    }
-  }
+  for (int r = 0; r < k; ++r) mx = fmax(mx, lg[r]);
   // weights from the unbiased scores of the chosen experts (softmax: renormalised over
   // the chosen, i.e. the softmax of their logits)
   double sc[16];

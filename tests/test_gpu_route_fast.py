@@ -180,3 +180,60 @@ def test_fast_route_exact_ties_and_nan_token(score):
     np.testing.assert_allclose(got_w[ok], want["topk_w"][ok], rtol=1e-6, atol=0)
     chosen = set(got_idx[ok].ravel().tolist())
     assert 3 in chosen and 12 not in chosen
+
+
+def _route_listed(x, wr, bias, k, score, scale):
+    """moe_route on a workspace of its own; returns ids, weights and the number of tokens
+    handed to the exact kernels (the int32 count that closes the route workspace)."""
+    T, H = x.shape
+    E = wr.shape[0]
+    ws = moe.workspace(moe.lib().moe_route_workspace_size(T, H, E))
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(x, wr, bias, k, score, scale, idx, w, ws=ws)
+    torch.cuda.synchronize()
+    listed = ws[ws.numel() - 256: ws.numel() - 252].view(torch.int32).item()
+    return idx.cpu().numpy(), w.cpu().numpy(), listed
+
+
+@pytest.mark.parametrize("score", ["sigmoid", "softmax"])
+def test_fast_route_refines_grouped_ties(score):
+    """Router rows in groups of four identical rows (with equal bias inside a group): the
+    k-th key of most tokens falls inside a group of exactly tied keys, which no bound can
+    separate. The wavefront refines them from exact logits of the few candidates: with
+    sigmoid the exact keys settle every token (ties to the lower id), so none reaches the
+    exact kernels; with softmax the exact ties are left to the exact kernels. Ids equal the
+    oracle's either way."""
+    cfg = MoEConfig("fast_grouped_ties", T=640, H=256, E=64, k=6, I=64, score=score,
+                    use_bias=score == "sigmoid", scale=1.0, seed=150, weight_seed=150)
+    print("case", describe(cfg), flush=True)
+    host = host_problem(cfg)
+    x, wr = host.x, host.wr.copy()
+    for g in range(0, cfg.E, 4):
+        wr[g + 1: g + 4] = wr[g]
+    bias = None
+    if cfg.use_bias:
+        bias = host.bias.copy()
+        for g in range(0, cfg.E, 4):
+            bias[g + 1: g + 4] = bias[g]
+    got_idx, got_w, listed = _route_listed(
+        _bf16_dev(x), _bf16_dev(wr), None if bias is None else torch.from_numpy(bias).cuda(),
+        cfg.k, score, cfg.scale)
+    want = O.route(O.bf16_to_f64(x), O.bf16_to_f64(wr), bias, cfg.k, score, cfg.scale)
+    assert np.array_equal(got_idx, want["topk_idx"])
+    np.testing.assert_allclose(got_w, want["topk_w"], rtol=1e-6, atol=0)
+    if score == "sigmoid":
+        assert listed == 0, listed
+    else:
+        assert 0 < listed <= cfg.T, listed
+
+
+@pytest.mark.parametrize("name", ["r1_prefill", "e384_fp8"])
+def test_fast_route_refinement_at_size(name):
+    """At full size the bounds leave a few hundred tokens undecided (362 of e384_fp8's 4096,
+    302 of r1_prefill's 8192 before refinement); the refinement settles all of them on
+    these inputs, with ids equal to the oracle's (checked by the full-size test above)."""
+    cfg = CONFIGS[name]
+    dev = device_problem(cfg, host=host_problem(cfg))
+    _, _, listed = _route_listed(dev.x, dev.wr, dev.bias, cfg.k, cfg.score, cfg.scale)
+    assert listed <= 4, listed
