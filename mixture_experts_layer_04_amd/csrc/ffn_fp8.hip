@@ -264,24 +264,53 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
       }
       const float sw0 = *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 64);
       const float sw1 = kGateUp ? *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 68) : 0.0f;
+      if constexpr (kGateUp) {
+        // all sub-tiles' activation fragments read, then all 2 NT products issued, then
+        // scaled into the accumulators: the matrix cores run back to back instead of
+        // waiting on each product's scaling (gate/up runs two wavefronts a SIMD, so the
+        // registers are there; e384_fp8 gate/up 2.46 -> 2.41 ms, r1_prefill_int8 4.00 ->
+        // 3.84 ms)
+        i32x8 xb[NT];
+        float sx[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int r = t * 16 + m16;
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g));
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g + 1));
-        i32x8 xb;
-        xb[0] = x0[0]; xb[1] = x0[1]; xb[2] = x0[2]; xb[3] = x0[3];
-        xb[4] = x1[0]; xb[5] = x1[1]; xb[6] = x1[2]; xb[7] = x1[3];
-        const float sx = *reinterpret_cast<const float*>(st + WB + ACT + t * 128 + m16 * 4);
-        const f32x4 p0 = block_product<kI8>(wa, xb);
-        const float c0 = sw0 * sx;
+        for (int t = 0; t < NT; ++t) {
+          const int r = t * 16 + m16;
+          const u32x4 x0 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g));
+          const u32x4 x1 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g + 1));
+          xb[t][0] = x0[0]; xb[t][1] = x0[1]; xb[t][2] = x0[2]; xb[t][3] = x0[3];
+          xb[t][4] = x1[0]; xb[t][5] = x1[1]; xb[t][6] = x1[2]; xb[t][7] = x1[3];
+          sx[t] = *reinterpret_cast<const float*>(st + WB + ACT + t * 128 + m16 * 4);
+        }
+        f32x4 p0[NT], p1[NT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc0[t][i] += p0[i] * c0;
-        if (kGateUp) {
-          const f32x4 p1 = block_product<kI8>(wb, xb);
-          const float c1 = sw1 * sx;
+        for (int t = 0; t < NT; ++t) {
+          p0[t] = block_product<kI8>(wa, xb[t]);
+          p1[t] = block_product<kI8>(wb, xb[t]);
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc1[t][i] += p1[i] * c1;
+        for (int t = 0; t < NT; ++t) {
+          const float c0 = sw0 * sx[t], c1 = sw1 * sx[t];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc0[t][i] += p0[t][i] * c0;
+            acc1[t][i] += p1[t][i] * c1;
+          }
+        }
+      } else {
+        // down (two workgroups a CU, four wavefronts a SIMD): one sub-tile at a time
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int r = t * 16 + m16;
+          const u32x4 x0 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g));
+          const u32x4 x1 = *reinterpret_cast<const u32x4*>(st + WB + lds_off(r, 2 * g + 1));
+          i32x8 xb;
+          xb[0] = x0[0]; xb[1] = x0[1]; xb[2] = x0[2]; xb[3] = x0[3];
+          xb[4] = x1[0]; xb[5] = x1[1]; xb[6] = x1[2]; xb[7] = x1[3];
+          const float sx = *reinterpret_cast<const float*>(st + WB + ACT + t * 128 + m16 * 4);
+          const f32x4 p0 = block_product<kI8>(wa, xb);
+          const float c0 = sw0 * sx;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc0[t][i] += p0[i] * c0;
         }
       }
     }

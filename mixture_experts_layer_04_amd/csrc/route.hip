@@ -494,8 +494,8 @@ constexpr int kRefineMax = 16;
 #ifndef MOE_LOGIT_UNROLL  // chunks of the exact dot products whose loads go out together
 #define MOE_LOGIT_UNROLL 1   // (2: the same speed with registers spilled at 3 workgroups a CU)
 #endif
-#ifndef MOE_TOPK_FAST_WGS  // workgroups a CU that k_topk_fast's register budget allows
-#define MOE_TOPK_FAST_WGS 2  // (3: route step 7-10 us longer at e384_fp8 and r1_prefill)
+#ifndef MOE_TOPK_FAST_WPS  // wavefronts a SIMD that k_topk_fast's register budget must allow
+#define MOE_TOPK_FAST_WPS 2  // (3: route step 7-10 us longer at e384_fp8 and r1_prefill)
 #endif
 
 // Exact logits of token row xr against router rows ids[0..8): fp64 dot products of the
@@ -536,7 +536,7 @@ __device__ __forceinline__ void exact_logits8(const uint16_t* __restrict__ xr,
 }
 
 template <int NPL>  // experts per lane: E <= 64 NPL
-__global__ void __launch_bounds__(256, MOE_TOPK_FAST_WGS) k_topk_fast(
+__global__ void __launch_bounds__(256, MOE_TOPK_FAST_WPS) k_topk_fast(
     const double* __restrict__ part, const double* __restrict__ nw2s, int S, int T, int H, int E,
     int k, int fn, float scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x,
