@@ -10,7 +10,9 @@
 //    and the tile's <= 128 rows as B. Each K block of both operands and of their scales
 //    goes global -> LDS by DMA through a ring (k_fp8 describes it): 3 stages of 49 KB for
 //    gate/up (one workgroup a CU, two blocks of weights in flight while one is
-//    multiplied), 2 stages of 33 KB for down (two workgroups a CU).
+//    multiplied), 2 stages of 33 KB for down (two workgroups a CU); where groups average
+//    less than a tile, down takes 256 output features a workgroup through gate/up's ring
+//    (each h block then read from L2 half as often).
 //  - gate/up epilogue: h = SiLU(g) * u in fp32, per-token amax over the workgroup's 128
 //    features (wavefront shuffles, then LDS across wavefronts), scale = amax / 448,
 //    E4M3 codes of h / scale -- exactly one 1 x 128 quantisation block per workgroup.
@@ -34,6 +36,9 @@ namespace {
 #endif
 #ifndef MOE_F8_W_NT  // weight DMA of single-tile groups with the non-temporal hint
 #define MOE_F8_W_NT 1
+#endif
+#ifndef MOE_F8_WIDE_DN  // down over 256 features a workgroup where H allows
+#define MOE_F8_WIDE_DN 1
 #endif
 
 // fp32 -> E4M3FN code, round to nearest even, saturating at +-448 (NaN -> 0x7F).
@@ -133,15 +138,19 @@ __device__ __forceinline__ f32x4 block_product(const i32x8& w, const i32x8& x) {
 
 // kYF32 (down only): expert outputs stored as fp32, else rounded once to bf16. kI8: INT8
 // weights and activations (W8A8), else E4M3.
-template <bool kGateUp, bool kYF32, bool kI8>
+// kWide (down only): the workgroup takes two 128-feature blocks (256 weight rows), as
+// gate/up takes its gate and up blocks, so that each activation (h) block is read from L2
+// half as often.
+template <bool kGateUp, bool kYF32, bool kI8, bool kWide>
 __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
-  // Each K block of the workgroup's operands -- its 128 (down) or 256 (gate/up) weight
-  // rows, the tile's 128 activation rows (both in the full-rate layout of lds_off) and the
-  // fp32 scales of both -- goes global -> LDS by DMA through an S-stage ring, requested
-  // S-1 blocks ahead. The K loop issues no other vector-memory load and reads no other LDS
-  // object, so its only vector-memory wait is the one for the oldest stage.
-  constexpr int S = kGateUp ? MOE_F8_STAGES_GU : MOE_F8_STAGES_DN;
-  constexpr int WR = kGateUp ? 2 * kF8Feat : kF8Feat;   // weight rows per stage
+  // Each K block of the workgroup's operands -- its 128 (down) or 256 (gate/up, wide down)
+  // weight rows, the tile's 128 activation rows (both in the full-rate layout of lds_off)
+  // and the fp32 scales of both -- goes global -> LDS by DMA through an S-stage ring,
+  // requested S-1 blocks ahead. The K loop issues no other vector-memory load and reads no
+  // other LDS object, so its only vector-memory wait is the one for the oldest stage.
+  constexpr bool kTwo = kGateUp || kWide;  // two 128-row weight blocks a workgroup
+  constexpr int S = kTwo ? MOE_F8_STAGES_GU : MOE_F8_STAGES_DN;
+  constexpr int WR = kTwo ? 2 * kF8Feat : kF8Feat;      // weight rows per stage
   constexpr int WB = WR * 128;                           // weight bytes per stage
   constexpr int ACT = kF8TileM * 128;
   constexpr int SCL = 8 * 128;  // per wavefront: its 16 rows' scales, then the weight scales
@@ -163,7 +172,7 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   const int I = a.bank[bank].I;
   const int H = a.H;
   const int K = kGateUp ? H : I;
-  const int f0 = fb * kF8Feat;
+  const int f0 = fb * (kWide ? 2 * kF8Feat : kF8Feat);
   if (f0 >= (kGateUp ? I : H)) return;
   const int KB = K / kF8K;
   const int ntb = (tl.nrows + 15) >> 4;
@@ -176,7 +185,7 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   for (int i = 0; i < NWD; ++i) {
     int r, c;
     dma_slot(8 * i + wave, l, &r, &c);
-    const int wrow = r < kF8Feat ? f0 + r : I + f0 + (r - kF8Feat);
+    const int wrow = kGateUp && r >= kF8Feat ? I + f0 + (r - kF8Feat) : f0 + r;
     wp[i] = wbase + (int64_t)wrow * K + c * 16;
   }
   // activation DMA sources: block q = 8 i + wave of the activation area
@@ -210,7 +219,7 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
     sp = sb + (int64_t)((l == 16 ? f0 : I + f0) / 128) * KB;
   } else {
     const float* sb = reinterpret_cast<const float*>(a.bank[bank].w2_scale) + ge * (H / 128) * (int64_t)KB;
-    sp = sb + (int64_t)(f0 / 128) * KB;
+    sp = sb + (int64_t)((f0 + (l == 17 ? kF8Feat : 0)) / 128) * KB;
   }
   // A group that fits in one tile reads its weights once: stream them with the
   // non-temporal hint (r1_decode_fp8 gate/up 0.72 -> 0.66 ms). Where row tiles of a group
@@ -226,7 +235,7 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
     }
     dma16(ap[0] + o, st + WB + wave * 1024);
     dma16(ap[1] + o, st + WB + (8 + wave) * 1024);
-    if (l < (kGateUp ? 18 : 17)) dma4(sp + kb, st + WB + ACT + wave * 128);
+    if (l < (kTwo ? 18 : 17)) dma4(sp + kb, st + WB + ACT + wave * 128);
   };
   f32x4 acc0[8], acc1[8];
 #pragma unroll
@@ -240,6 +249,20 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   // be interleaved (a per-sub-tile branch would serialise them).
   auto kloop = [&](auto nt_c) {
     constexpr int NT = decltype(nt_c)::value;
+    // two weight blocks with up to 6 sub-tiles: the products of block kb are scaled into the
+    // accumulators during block kb + 1, after its fragment reads are issued, so that the
+    // scaling covers their latency (the same additions in the same order; with 7 or 8
+    // sub-tiles the registers for it would spill)
+    constexpr bool kDefer = kTwo && NT <= 6;
+    f32x4 q0[kTwo ? NT : 1], q1[kTwo ? NT : 1];
+    float c0q[kTwo ? NT : 1], c1q[kTwo ? NT : 1];
+    if constexpr (kDefer) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        q0[t] = q1[t] = f32x4{0, 0, 0, 0};
+        c0q[t] = c1q[t] = 0.0f;
+      }
+    }
     for (int kb = 0; kb < KB; ++kb) {
       // block kb has landed once at most (blocks issued after it) * A ops are outstanding
       if (kb + S - 2 < KB) wait_vmcnt<(S - 2) * A>();
@@ -253,23 +276,22 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
         const u32x4 p1 = *reinterpret_cast<const u32x4*>(st + lds_off(wr0, 2 * g + 1));
         wa[0] = p0[0]; wa[1] = p0[1]; wa[2] = p0[2]; wa[3] = p0[3];
         wa[4] = p1[0]; wa[5] = p1[1]; wa[6] = p1[2]; wa[7] = p1[3];
-        if (kGateUp) {
-          const u32x4 q0 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g));
-          const u32x4 q1 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g + 1));
-          wb[0] = q0[0]; wb[1] = q0[1]; wb[2] = q0[2]; wb[3] = q0[3];
-          wb[4] = q1[0]; wb[5] = q1[1]; wb[6] = q1[2]; wb[7] = q1[3];
+        if (kTwo) {
+          const u32x4 u0 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g));
+          const u32x4 u1 = *reinterpret_cast<const u32x4*>(st + lds_off(kF8Feat + wr0, 2 * g + 1));
+          wb[0] = u0[0]; wb[1] = u0[1]; wb[2] = u0[2]; wb[3] = u0[3];
+          wb[4] = u1[0]; wb[5] = u1[1]; wb[6] = u1[2]; wb[7] = u1[3];
         } else {
           wb = wa;
         }
       }
       const float sw0 = *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 64);
-      const float sw1 = kGateUp ? *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 68) : 0.0f;
-      if constexpr (kGateUp) {
-        // all sub-tiles' activation fragments read, then all 2 NT products issued, then
-        // scaled into the accumulators: the matrix cores run back to back instead of
-        // waiting on each product's scaling (gate/up runs two wavefronts a SIMD, so the
-        // registers are there; e384_fp8 gate/up 2.46 -> 2.41 ms, r1_prefill_int8 4.00 ->
-        // 3.84 ms)
+      const float sw1 = kTwo ? *reinterpret_cast<const float*>(st + WB + ACT + wave * 128 + 68) : 0.0f;
+      if constexpr (kTwo) {
+        // all sub-tiles' activation fragments read (then, deferring, the previous block's
+        // products scaled), then all 2 NT products of this block issued back to back
+        // (gate/up runs two wavefronts a SIMD, so the registers are there; issuing them
+        // together: e384_fp8 gate/up 2.46 -> 2.41 ms, r1_prefill_int8 4.00 -> 3.84 ms)
         i32x8 xb[NT];
         float sx[NT];
 #pragma unroll
@@ -281,23 +303,36 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
           xb[t][4] = x1[0]; xb[t][5] = x1[1]; xb[t][6] = x1[2]; xb[t][7] = x1[3];
           sx[t] = *reinterpret_cast<const float*>(st + WB + ACT + t * 128 + m16 * 4);
         }
-        f32x4 p0[NT], p1[NT];
+        if constexpr (kDefer) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          p0[t] = block_product<kI8>(wa, xb[t]);
-          p1[t] = block_product<kI8>(wb, xb[t]);
+          for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc0[t][i] += q0[t][i] * c0q[t];
+              acc1[t][i] += q1[t][i] * c1q[t];
+            }
+          }
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const float c0 = sw0 * sx[t], c1 = sw1 * sx[t];
+          q0[t] = block_product<kI8>(wa, xb[t]);
+          q1[t] = block_product<kI8>(wb, xb[t]);
+          c0q[t] = sw0 * sx[t];
+          c1q[t] = sw1 * sx[t];
+        }
+        if constexpr (!kDefer) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc0[t][i] += p0[t][i] * c0;
-            acc1[t][i] += p1[t][i] * c1;
+          for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc0[t][i] += q0[t][i] * c0q[t];
+              acc1[t][i] += q1[t][i] * c1q[t];
+            }
           }
         }
       } else {
-        // down (two workgroups a CU, four wavefronts a SIMD): one sub-tile at a time
+        // one weight block (down, two workgroups a CU, four wavefronts a SIMD): one
+        // sub-tile at a time
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int r = t * 16 + m16;
@@ -311,6 +346,16 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
           const float c0 = sw0 * sx;
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc0[t][i] += p0[i] * c0;
+        }
+      }
+    }
+    if constexpr (kDefer) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc0[t][i] += q0[t][i] * c0q[t];
+          acc1[t][i] += q1[t][i] * c1q[t];
         }
       }
     }
@@ -364,14 +409,18 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
       const int tok = t * 16 + m16;
       if (tok >= tl.nrows) continue;
       const int64_t o = (int64_t)(tl.row0 + tok) * H + fw + 4 * g;
-      if (kYF32) {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + o) =
-            make_float4(acc0[t][0], acc0[t][1], acc0[t][2], acc0[t][3]);
-      } else {
-        uint2 b;
-        b.x = (uint32_t)f32_to_bf16(acc0[t][0]) | ((uint32_t)f32_to_bf16(acc0[t][1]) << 16);
-        b.y = (uint32_t)f32_to_bf16(acc0[t][2]) | ((uint32_t)f32_to_bf16(acc0[t][3]) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + o) = b;
+#pragma unroll
+      for (int hb = 0; hb < (kWide ? 2 : 1); ++hb) {  // wide: the second block 128 further
+        const f32x4 v = hb ? acc1[t] : acc0[t];
+        const int64_t oh = o + hb * kF8Feat;
+        if (kYF32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + oh) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          uint2 b;
+          b.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          b.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + oh) = b;
+        }
       }
     }
   }
@@ -380,18 +429,32 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
 }  // namespace
 
 namespace {
+template <bool kI8, bool kWide>
+hipError_t launch_q8_down(const FfnArgs& a, hipStream_t s) {
+  const int nb_dn = a.H / (kWide ? 2 * kF8Feat : kF8Feat);
+  if (a.y_dt == MOE_F32)
+    hipLaunchKernelGGL((k_fp8<false, true, kI8, kWide>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
+  else
+    hipLaunchKernelGGL((k_fp8<false, false, kI8, kWide>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
+  return hipGetLastError();
+}
+
 template <bool kI8>
 hipError_t launch_q8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
-  const int nb_gu = a.I_max / kF8Feat, nb_dn = a.H / kF8Feat;
-  hipLaunchKernelGGL((k_fp8<true, true, kI8>), dim3(a.max_tiles * nb_gu), dim3(512), 0, s, a, nb_gu);
+  const int nb_gu = a.I_max / kF8Feat;
+  hipLaunchKernelGGL((k_fp8<true, true, kI8, false>), dim3(a.max_tiles * nb_gu), dim3(512), 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
-  if (a.y_dt == MOE_F32)
-    hipLaunchKernelGGL((k_fp8<false, true, kI8>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
-  else
-    hipLaunchKernelGGL((k_fp8<false, false, kI8>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
-  return hipGetLastError();
+  // Wide down where groups average less than a full 128-row tile: such tiles are light
+  // on the matrix cores and the launch waits on its loads, half of which are h (e384_fp8,
+  // 96 rows a group: down 1.387 -> 1.336 ms). Full tiles keep two workgroups a CU, whose
+  // four wavefronts a SIMD the heavier K loop needs (r1_prefill_int8, 287 rows a group:
+  // wide 2.110 ms against 1.978).
+  const int64_t groups = (int64_t)a.E + (a.has_shared ? 1 : 0);
+  if (MOE_F8_WIDE_DN && a.H % (2 * kF8Feat) == 0 && a.rows_total < (int64_t)kF8TileM * groups)
+    return launch_q8_down<kI8, true>(a, s);
+  return launch_q8_down<kI8, false>(a, s);
 }
 }  // namespace
 
