@@ -76,8 +76,8 @@ constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt to them round-robi
 #endif
 static_assert(4 * 16 * 4 == kTiledMB && 4 * 16 * 4 == kTiledNB, "tile shape of the tile list");
 // waves a SIMD that the register budget must allow: a 16-wavefront workgroup puts four on
-// each SIMD of its CU
-constexpr int waves_per_simd(int nw) { return nw >= 16 ? 4 : MOE_T2_WAVES_PER_SIMD; }
+// each SIMD of its CU, and two 8-wavefront workgroups a CU do the same
+constexpr int waves_per_simd(int nw) { return nw >= 8 ? 4 : MOE_T2_WAVES_PER_SIMD; }
 constexpr int kT2M = MOE_T2_WGM * 16 * MOE_T2_TM, kT2N = MOE_T2_WGN * 16 * MOE_T2_TN;
 static_assert(kT2M == kTiledM && kT2N == kTiledN, "tile shape of the tile list");
 
@@ -403,22 +403,27 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
 // slices are a quarter of bf16's, so the ring still leaves room for two workgroups a CU.
 constexpr int kMXN = MOE_T2_WGN * 16 * MOE_T2_MX_TN;
 
-// SB: weight-ring stages of the gate/up launch, SBD of the down launch
-template <int TM, int TN, int WGM, int WGN, int S, int SB, int SBD, bool kMX>
+// SB: weight-ring stages of the gate/up launch, SBD of the down launch; TND x WGND: the
+// down launch's column tiles a wavefront and wavefronts along the weight rows (the same
+// 16 TN WGN weight rows a workgroup, the same row tiles)
+template <int TM, int TN, int WGM, int WGN, int S, int SB, int SBD, bool kMX, int TND = TN,
+          int WGND = WGN>
 hipError_t launch_tiled_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
   constexpr int BN = WGN * 16 * TN;
+  static_assert(WGND * 16 * TND == BN, "both launches take the same weight block");
   const int nb_gu = a.I_max / (BN / 2), nb_dn = a.H / BN;
   // whole rounds of kXcds workgroups, so that every chunk's last item has a workgroup
   const dim3 gu((a.max_tiles * nb_gu + kXcds - 1) / kXcds * kXcds),
-      dn((a.max_tiles * nb_dn + kXcds - 1) / kXcds * kXcds), blk(64 * WGM * WGN);
+      dn((a.max_tiles * nb_dn + kXcds - 1) / kXcds * kXcds), blk(64 * WGM * WGN),
+      blkd(64 * WGM * WGND);
   hipLaunchKernelGGL((k_tiled2<TM, TN, WGM, WGN, S, SB, true, false, kMX>), gu, blk, 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
   if (a.y_dt == MOE_F32)
-    hipLaunchKernelGGL((k_tiled2<TM, TN, WGM, WGN, S, SBD, false, true, kMX>), dn, blk, 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_tiled2<TM, TND, WGM, WGND, S, SBD, false, true, kMX>), dn, blkd, 0, s, a, nb_dn);
   else
-    hipLaunchKernelGGL((k_tiled2<TM, TN, WGM, WGN, S, SBD, false, false, kMX>), dn, blk, 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_tiled2<TM, TND, WGM, WGND, S, SBD, false, false, kMX>), dn, blkd, 0, s, a, nb_dn);
   return hipGetLastError();
 }
 
@@ -435,9 +440,13 @@ hipError_t launch_ffn_tiled(const FfnArgs& a, hipStream_t s, hipEvent_t mid_even
   if (a.wdt != MOE_MXFP4)
     return launch_tiled_pair<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_STAGES,
                              MOE_T2_STAGES_B_GU, MOE_T2_STAGES_B_DN, false>(a, s, mid_event);
+  // MXFP4 down on 8 wavefronts of 64 x 64 (two workgroups a CU, four wavefronts a SIMD):
+  // ep32_mxfp4 down 0.464 -> 0.451 ms; the same tiles for gate/up measured slower (0.905
+  // -> 0.950 ms), which keeps 4 wavefronts of 64 x 128
   if (kMXN != kT2N && fits(kMXN))
     return launch_tiled_pair<MOE_T2_TM, MOE_T2_MX_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES,
-                             MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, true>(a, s, mid_event);
+                             MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, true, MOE_T2_MX_TN / 2,
+                             MOE_T2_WGN * 2>(a, s, mid_event);
   return launch_tiled_pair<MOE_T2_TM, MOE_T2_TN, MOE_T2_WGM, MOE_T2_WGN, MOE_T2_MX_STAGES,
                            MOE_T2_MX_STAGES, MOE_T2_MX_STAGES, true>(a, s, mid_event);
 }
