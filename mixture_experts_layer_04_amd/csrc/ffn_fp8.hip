@@ -40,6 +40,9 @@ namespace {
 #ifndef MOE_F8_WIDE_DN  // down over 256 features a workgroup where H allows
 #define MOE_F8_WIDE_DN 1
 #endif
+#ifndef MOE_F8_DEFER  // sub-tiles whose scaling two-block launches defer to the next K block
+#define MOE_F8_DEFER 6
+#endif
 
 // fp32 -> E4M3FN code, round to nearest even, saturating at +-448 (NaN -> 0x7F).
 // Written from the format: magnitudes below 2^-6 lie on the subnormal grid m * 2^-9;
@@ -249,16 +252,17 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   // be interleaved (a per-sub-tile branch would serialise them).
   auto kloop = [&](auto nt_c) {
     constexpr int NT = decltype(nt_c)::value;
-    // two weight blocks with up to 6 sub-tiles: the products of block kb are scaled into the
-    // accumulators during block kb + 1, after its fragment reads are issued, so that the
-    // scaling covers their latency (the same additions in the same order; with 7 or 8
-    // sub-tiles the registers for it would spill)
-    constexpr bool kDefer = kTwo && NT <= 6;
+    // two weight blocks with up to MOE_F8_DEFER sub-tiles: the products of block kb are
+    // scaled into the accumulators during block kb + 1, after its fragment reads are
+    // issued, so that the scaling covers their latency (the same additions in the same
+    // order); with more sub-tiles they are scaled at once (deferring any of 7 or 8 spills
+    // registers)
+    constexpr int ND = kTwo && NT <= MOE_F8_DEFER ? NT : 0;
     f32x4 q0[kTwo ? NT : 1], q1[kTwo ? NT : 1];
     float c0q[kTwo ? NT : 1], c1q[kTwo ? NT : 1];
-    if constexpr (kDefer) {
+    if constexpr (ND > 0) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+      for (int t = 0; t < ND; ++t) {
         q0[t] = q1[t] = f32x4{0, 0, 0, 0};
         c0q[t] = c1q[t] = 0.0f;
       }
@@ -303,14 +307,12 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
           xb[t][4] = x1[0]; xb[t][5] = x1[1]; xb[t][6] = x1[2]; xb[t][7] = x1[3];
           sx[t] = *reinterpret_cast<const float*>(st + WB + ACT + t * 128 + m16 * 4);
         }
-        if constexpr (kDefer) {
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < ND; ++t) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              acc0[t][i] += q0[t][i] * c0q[t];
-              acc1[t][i] += q1[t][i] * c1q[t];
-            }
+          for (int i = 0; i < 4; ++i) {
+            acc0[t][i] += q0[t][i] * c0q[t];
+            acc1[t][i] += q1[t][i] * c1q[t];
           }
         }
 #pragma unroll
@@ -320,14 +322,12 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
           c0q[t] = sw0 * sx[t];
           c1q[t] = sw1 * sx[t];
         }
-        if constexpr (!kDefer) {
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
+        for (int t = ND; t < NT; ++t) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              acc0[t][i] += q0[t][i] * c0q[t];
-              acc1[t][i] += q1[t][i] * c1q[t];
-            }
+          for (int i = 0; i < 4; ++i) {
+            acc0[t][i] += q0[t][i] * c0q[t];
+            acc1[t][i] += q1[t][i] * c1q[t];
           }
         }
       } else {
@@ -349,14 +349,12 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
         }
       }
     }
-    if constexpr (kDefer) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < ND; ++t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc0[t][i] += q0[t][i] * c0q[t];
-          acc1[t][i] += q1[t][i] * c1q[t];
-        }
+      for (int i = 0; i < 4; ++i) {
+        acc0[t][i] += q0[t][i] * c0q[t];
+        acc1[t][i] += q1[t][i] * c1q[t];
       }
     }
   };
