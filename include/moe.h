@@ -169,6 +169,24 @@ moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype a
                            const int32_t* offsets, int32_t rows, void* y_perm, moe_dtype y_dt,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* moe_grouped_ffn on rows that the caller has already quantised, for FP8_E4M3, INT8 and
+ * MXFP4_A4 banks (the low-precision grouped GEMM of GC-MoE, key_changes, fourth item, takes
+ * its activations as codes plus block scales). Codes and scales are in the layout that
+ * moe_quantize_fp8, moe_quantize_int8 and moe_quantize_mxfp4 write:
+ *   FP8_E4M3  x_codes [rows, H] E4M3 bytes,      x_scales [rows, H/128] f32;
+ *   INT8      x_codes [rows, H] int8,            x_scales [rows, H/128] f32;
+ *   MXFP4_A4  x_codes [rows, H/2] E2M1 pairs,    x_scales [rows, H/32] E8M0 bytes.
+ * Both 16-byte aligned. offsets, y_perm, y_dt and the limits are moe_grouped_ffn's; the
+ * workspace is moe_grouped_ffn_workspace_size(w, MOE_BF16, rows) bytes. h is re-quantised
+ * inside exactly as in moe_grouped_ffn, so with the codes and scales of the matching
+ * moe_quantize_* call on bf16 rows x the output is bit-identical to
+ * moe_grouped_ffn(w, x, MOE_BF16, ...). Scales are used as given (not checked on the
+ * device). MOE_ERR_DTYPE for any other bank format. */
+moe_status moe_grouped_ffn_prequant(const moe_experts* w, const void* x_codes,
+                                    const void* x_scales, const int32_t* offsets, int32_t rows,
+                                    void* y_perm, moe_dtype y_dt, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* ------------------------------------------------------------------------------ combine */
 
 /* out[t] = sum_j topk_w[t,j] * y_perm[inv_perm[t*k+j]] + shared_out[t]   (moe_ffn's

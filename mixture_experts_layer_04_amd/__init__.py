@@ -52,7 +52,8 @@ class moe_layer_desc(ctypes.Structure):
 
 _lib = None
 EXPORTS = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
-           "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
+           "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_prequant",
+           "moe_combine",
            "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_layer_forward_overlap", "moe_layer_forward_noalloc", "moe_layer_forward_split",
            "moe_rows_workspace_size",
@@ -80,6 +81,7 @@ def lib():
     L.moe_grouped_ffn_workspace_size.argtypes = [P(moe_experts), ci, i32]
     L.moe_grouped_ffn_workspace_size.restype = sz
     L.moe_grouped_ffn.argtypes = [P(moe_experts), vp, ci, vp, i32, vp, ci, vp, sz, vp]
+    L.moe_grouped_ffn_prequant.argtypes = [P(moe_experts), vp, vp, vp, i32, vp, ci, vp, sz, vp]
     L.moe_combine.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, ci, vp]
     L.moe_layer_workspace_size.argtypes = [P(moe_layer_desc), P(sz)]
     L.moe_layer_forward.argtypes = [P(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -95,7 +97,7 @@ def lib():
     L.moe_rows_forward.argtypes = [P(moe_experts), vp, ci, vp, vp, i32, vp, ci, vp, sz, vp]
     L.moe_rows_forward_timed.argtypes = [P(moe_experts), vp, ci, vp, vp, i32, vp, ci, vp, sz, vp,
                                          P(vp)]
-    for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
+    for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_prequant", "moe_combine", "moe_layer_workspace_size",
               "moe_layer_forward", "moe_layer_forward_timed", "moe_layer_forward_overlap",
               "moe_layer_forward_noalloc", "moe_layer_forward_split",
               "moe_rows_forward",
@@ -210,6 +212,21 @@ def moe_grouped_ffn(experts: Experts, x_perm, offsets, y_perm, ws=None, stream=N
     st = lib().moe_grouped_ffn(ctypes.byref(cw), _ptr(x_perm), act, _ptr(offsets), rows, _ptr(y_perm),
                                _act_dt(y_perm), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_grouped_ffn")
+
+
+def moe_grouped_ffn_prequant(experts: Experts, x_codes, x_scales, offsets, y_perm, ws=None,
+                             stream=None):
+    """moe_grouped_ffn on rows given as the codes and block scales of moe_quantize_fp8,
+    moe_quantize_int8 or moe_quantize_mxfp4 (FP8_E4M3, INT8 and MXFP4_A4 banks)."""
+    rows = x_codes.shape[0]
+    cw = experts.c()
+    if ws is None:
+        ws = workspace(lib().moe_grouped_ffn_workspace_size(ctypes.byref(cw), DTYPES["bf16"], rows),
+                       x_codes.device)
+    st = lib().moe_grouped_ffn_prequant(ctypes.byref(cw), _ptr(x_codes), _ptr(x_scales), _ptr(offsets),
+                                        rows, _ptr(y_perm), _act_dt(y_perm), _ptr(ws), ws.numel(),
+                                        _stream(stream))
+    _check(st, "moe_grouped_ffn_prequant")
 
 
 def moe_combine(y_perm, inv_perm, topk_w, out, shared_out=None, stream=None):

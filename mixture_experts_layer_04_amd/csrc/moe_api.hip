@@ -367,6 +367,41 @@ moe_status moe_grouped_ffn(const moe_experts* w, const void* x_perm, moe_dtype a
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_ffn");
 }
 
+moe_status moe_grouped_ffn_prequant(const moe_experts* w, const void* x_codes,
+                                    const void* x_scales, const int32_t* offsets, int32_t rows,
+                                    void* y_perm, moe_dtype y_dt, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (!w) return MOE_ERR_NULL;
+  if (rows < 0 || (int64_t)rows * 8 >= ((int64_t)1 << 31) || w->E > 1024) return MOE_ERR_SHAPE;
+  moe_status st = check_bank(w, w->H, true);
+  if (st != MOE_OK) return st;
+  const bool q8 = w->dtype == MOE_FP8_E4M3 || w->dtype == MOE_INT8;
+  if (!(q8 || w->dtype == MOE_MXFP4_A4) || !io_dt_ok(y_dt)) return MOE_ERR_DTYPE;
+  if (!offsets || !ws) return MOE_ERR_NULL;
+  if (rows > 0 && (!x_codes || !x_scales || !y_perm)) return MOE_ERR_NULL;
+  if ((x_codes && !al16(x_codes)) || (x_scales && !al16(x_scales)) || (y_perm && !al16(y_perm)) ||
+      !al256(ws))
+    return MOE_ERR_ALIGN;
+  FfnPlan p;
+  QPlan q;
+  size_t total;
+  plan_grouped(w, MOE_BF16, rows, &p, &q, &total);
+  if (ws_bytes < total) return MOE_ERR_WORKSPACE;
+  char* base = reinterpret_cast<char*>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_tiles_from_offsets(offsets, w->E, reinterpret_cast<Tile*>(base + p.o_tiles),
+                                           reinterpret_cast<int32_t*>(base + p.o_ntiles), p.tile_m, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn_prequant tiles");
+  // the kernels of these formats read only the codes and scales of the rows
+  FfnArgs f = ffn_args(p, base, *w, nullptr, MOE_BF16, w->H, nullptr, nullptr, y_perm);
+  f.y_dt = y_dt;
+  f.a_q = reinterpret_cast<const uint8_t*>(x_codes);
+  if (q8) f.a_qscale = reinterpret_cast<const float*>(x_scales);
+  else f.a_xs = reinterpret_cast<const uint8_t*>(x_scales);
+  e = launch_grouped_ffn(f, base + p.o_scratch, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_ffn_prequant");
+}
+
 // ----------------------------------------------------------------------- combine
 
 moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* inv_perm,

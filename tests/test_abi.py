@@ -188,6 +188,30 @@ def test_other_entry_point_validation():
                                   1 << 30, None) == moe.MOE_ERR_SHAPE
 
 
+def test_grouped_ffn_prequant_validation():
+    """moe_grouped_ffn_prequant takes FP8_E4M3, INT8 and MXFP4_A4 banks only, and checks its
+    pointers, alignment and workspace before any launch."""
+    L = moe.lib()
+    f = L.moe_grouped_ffn_prequant
+    for fmt in ("bf16", "mxfp4"):                          # formats without quantised rows
+        b = bank(fmt, H=256, I=128, scales=fmt == "mxfp4")
+        assert f(ctypes.byref(b), P, P, P, 64, P, moe.MOE_BF16, P, 1 << 30, None) == moe.MOE_ERR_DTYPE
+    for fmt in ("fp8", "int8", "mxfp4a4"):
+        b = bank(fmt, H=256, I=128, scales=True)
+        need = L.moe_grouped_ffn_workspace_size(ctypes.byref(b), moe.MOE_BF16, 64)
+        assert need > 0
+        assert f(ctypes.byref(b), P, P, P, 64, P, moe.MOE_FP8_E4M3, P, need, None) == moe.MOE_ERR_DTYPE
+        assert f(ctypes.byref(b), P, None, P, 64, P, moe.MOE_BF16, P, need, None) == moe.MOE_ERR_NULL
+        assert f(ctypes.byref(b), None, P, P, 64, P, moe.MOE_BF16, P, need, None) == moe.MOE_ERR_NULL
+        assert f(ctypes.byref(b), P, P, None, 64, P, moe.MOE_BF16, P, need, None) == moe.MOE_ERR_NULL
+        assert f(ctypes.byref(b), P, MISALIGNED, P, 64, P, moe.MOE_BF16, P, need, None) == \
+            moe.MOE_ERR_ALIGN
+        assert f(ctypes.byref(b), P, P, P, 64, P, moe.MOE_BF16, P, need - 1, None) == \
+            moe.MOE_ERR_WORKSPACE
+        assert f(ctypes.byref(b), P, P, P, -1, P, moe.MOE_BF16, P, need, None) == moe.MOE_ERR_SHAPE
+    assert f(None, P, P, P, 64, P, moe.MOE_BF16, P, 1 << 30, None) == moe.MOE_ERR_NULL
+
+
 def test_bias_update_validation():
     L = moe.lib()
     for E in (0, 1025, -3):

@@ -6,7 +6,10 @@
   * moe_grouped_ffn on its own for every expert format and kernel family (streaming,
     LDS-staged streaming down, 128- and 256-row tiles, fp8, MXFP4 streaming and tiled, W4A4,
     fp32), each with fp32 and bf16 output rows, row by row against oracle.expert_ffn on the
-    same (quantised) activations.
+    same (quantised) activations;
+  * moe_grouped_ffn_prequant (fp8, INT8, W4A4) on the oracle's own codes and scales against
+    oracle.expert_ffn, and on the library quantisers' codes bit-identical to
+    moe_grouped_ffn on the bf16 rows.
 The expert ids fed to moe_permute come from the oracle's routing (or the workload's
 pre-routed ids), never from the library.
 """
@@ -113,6 +116,65 @@ def test_grouped_ffn_alone(case, y_dt):
     tol = TOL[wdt] if not (wdt == "f32" and y_dt == "bf16") else TOL["bf16"]
     print(name, y_dt, "rel err", err, flush=True)
     assert err <= tol, (name, y_dt, err)
+
+
+PREQUANT = {"fp8": (O.quantise_rows_e4m3, moe.moe_quantize_fp8, 1, 128, torch.uint8, torch.float32),
+            "int8": (O.quantise_rows_int8, moe.moe_quantize_int8, 1, 128, torch.int8, torch.float32),
+            "mxfp4a4": (O.quantise_rows_mxfp4, moe.moe_quantize_mxfp4, 2, 32, torch.uint8,
+                        torch.uint8)}
+
+
+@pytest.mark.parametrize("y_dt", ["f32", "bf16"])
+@pytest.mark.parametrize("case", [c for c in FFN_CASES if c[1] in PREQUANT], ids=lambda c: c[0])
+def test_grouped_ffn_prequant(case, y_dt):
+    """Rows handed over already quantised. The oracle's codes and scales, uploaded as they
+    are, give oracle.expert_ffn's rows within the format's tolerance; the codes and scales of
+    the library's moe_quantize_* on the bf16 rows give exactly moe_grouped_ffn's bits."""
+    name, wdt, H, I, E, rows = case
+    quantise, lib_quantise, per_byte, blk, code_dt, scale_dt = PREQUANT[wdt]
+    cfg = MoEConfig(f"ffn_{name}", T=rows, H=H, E=E, k=1, I=I, score="none", act="bf16", wdt=wdt,
+                    out=y_dt, seed=150 + len(name), weight_seed=150 + len(name),
+                    dirichlet_alpha=0.7)
+    print("case", describe(cfg), flush=True)
+    host = host_problem(cfg)
+    dev = device_problem(cfg, host=host)
+    counts = np.bincount(host.topk_idx[:, 0], minlength=E)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    codes, scales, a = quantise(O.decode_act("bf16", host.x).astype(np.float32))
+    if per_byte == 2:  # E2M1 nibbles, element 2i in the low nibble of byte i
+        codes = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    requant = {"fp8": True, "int8": "int8", "mxfp4a4": "mxfp4"}[wdt]
+    want = np.zeros((rows, H))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            w13, w2 = O.expert_weights(host.routed, e)
+            want[r0:r1] = O.expert_ffn(a[r0:r1], w13, w2, requant_h=requant)
+    experts = moe.Experts.from_bank(dev.routed)
+    d_off = torch.from_numpy(offsets).cuda()
+    ydt = torch.float32 if y_dt == "f32" else torch.bfloat16
+    y = torch.full((rows + 8, H), float("nan"), dtype=ydt, device="cuda")  # 8 guard rows
+    d_codes = torch.from_numpy(np.ascontiguousarray(codes).view(np.uint8)).cuda().view(code_dt)
+    d_scales = torch.from_numpy(np.ascontiguousarray(scales)).cuda()
+    moe.moe_grouped_ffn_prequant(experts, d_codes, d_scales, d_off, y[:rows])
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    assert np.isnan(got[rows:]).all()                # nothing written past the last row
+    err = O.rel_err(got[:rows], want)
+    print(name, y_dt, "rel err", err, flush=True)
+    assert err <= TOL[wdt], (name, y_dt, err)
+    # the library's quantiser, then the pre-quantised call: the bits of moe_grouped_ffn
+    q = torch.empty((rows, H // per_byte), dtype=code_dt, device="cuda")
+    qs = torch.empty((rows, H // blk), dtype=scale_dt, device="cuda")
+    lib_quantise(dev.x, q, qs)
+    y_pre = torch.empty((rows, H), dtype=ydt, device="cuda")
+    y_ref = torch.empty((rows, H), dtype=ydt, device="cuda")
+    moe.moe_grouped_ffn_prequant(experts, q, qs, d_off, y_pre)
+    moe.moe_grouped_ffn(experts, dev.x, d_off, y_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(y_pre.view(torch.int16 if y_dt == "bf16" else torch.int32),
+                       y_ref.view(torch.int16 if y_dt == "bf16" else torch.int32))
 
 
 def _split_h(h64):
