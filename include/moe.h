@@ -88,7 +88,8 @@ typedef enum {
  *           section 3.1 of "Trillion-Parameter LLM Architecture Explained and
  *           Cost-Efficient Inference in Practice"). Activations BF16 in, quantised inside.
  *           H, I multiples of 128.
- * F32/BF16: no scales (NULL). H, I multiples of 64.
+ * F32/BF16: no scales (NULL). H, I multiples of 8 (multiples of 64 run on the matrix cores;
+ *           other multiples of 8 on plain fp32 dot products with h kept in fp32).
  * The fp8 and MXFP4 expert formats are the FP8/FP4 grouped GEMM inputs of "GC-MoE:
  * Overlapping Expert-Parallel Token Dispatch with FP8/FP4 Grouped GEMM via CUDA Green
  * Contexts" (key_changes, fourth item); block shapes are this library's choice. */

@@ -7,7 +7,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 
 SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "ffn_stream.hip",
-           "ffn_tiled.hip", "ffn_fp8.hip", "combine.hip", "balance.hip", "ffn_w4a4.hip", "probe.hip"]
+           "ffn_tiled.hip", "ffn_fp8.hip", "combine.hip", "balance.hip", "ffn_w4a4.hip", "ffn_generic.hip",
+           "probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -11,16 +11,18 @@
 // workgroups exit at once, so no host synchronisation is needed.
 //
 // Kernel families, chosen per call: streaming kernels (ffn_stream.hip), the LDS-tiled bf16 /
-// MXFP4 kernel (ffn_tiled.hip), the fp8 / INT8 kernel (ffn_fp8.hip) and the W4A4 kernel
-// (ffn_w4a4.hip).
+// MXFP4 kernel (ffn_tiled.hip), the fp8 / INT8 kernel (ffn_fp8.hip), the W4A4 kernel
+// (ffn_w4a4.hip), and plain dot products for bf16 / fp32 shapes that are multiples of 8 but
+// not of 64 (ffn_generic.hip).
 #include "ffn_common.h"
 
 namespace moe {
 
 bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I) {
   switch (wdt) {
+    // multiples of 64 go to the MFMA kernels, other multiples of 8 to ffn_generic.hip
     case MOE_F32:
-    case MOE_BF16: return H % 64 == 0 && I % 64 == 0;
+    case MOE_BF16: return H % 8 == 0 && I % 8 == 0;
     case MOE_FP8_E4M3:
     case MOE_INT8: return H % kF8Feat == 0 && I % kF8Feat == 0;
     // the tiled kernel's weight-row blocks, and dword-aligned scale bytes of every row
@@ -56,8 +58,11 @@ int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32
 
 int32_t ffn_stream_tile_rows() { return kStreamTileM; }
 
-size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_max) {
-  (void)H;
+size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_routed,
+                         int32_t I_shared) {
+  const int32_t I_max = I_shared > I_routed ? I_shared : I_routed;
+  if (ffn_generic(wdt, H, I_routed, I_shared))  // h kept fp32
+    return ((size_t)rows_total * I_max * 4 + 255) / 256 * 256;
   if (wdt == MOE_FP8_E4M3 || wdt == MOE_INT8) {
     const size_t q = ((size_t)rows_total * I_max + 255) / 256 * 256;
     return q + ((size_t)rows_total * (I_max / kF8K) * sizeof(float) + 255) / 256 * 256;
@@ -80,6 +85,8 @@ hipError_t launch_grouped_ffn(FfnArgs a, void* scratch, hipStream_t s, hipEvent_
     return mid_event ? hipEventRecord(mid_event, s) : hipSuccess;
   }
   a.h = scratch;
+  if (ffn_generic(a.wdt, a.H, a.bank[0].I, a.has_shared ? a.bank[1].I : 0))
+    return launch_ffn_generic(a, s, mid_event);
   if (a.wdt == MOE_FP8_E4M3 || a.wdt == MOE_INT8) {
     a.h_scale = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) +
                                          ((size_t)a.rows_total * a.I_max + 255) / 256 * 256);

@@ -96,7 +96,7 @@ void plan_ffn(Carve& c, FfnPlan& p, moe_dtype wdt, moe_dtype act, int32_t H, int
   p.y_dt = (wdt == MOE_BF16 || wdt == MOE_F32) ? MOE_F32 : MOE_BF16;
   p.o_tiles = c.take((size_t)mt * sizeof(Tile));
   p.o_ntiles = c.take(sizeof(int32_t));
-  p.o_scratch = c.take(ffn_scratch_bytes(wdt, p.rows_total, H, I_max));
+  p.o_scratch = c.take(ffn_scratch_bytes(wdt, p.rows_total, H, I_routed, I_shared));
   if (need_y) p.o_y = c.take((size_t)p.rows_total * H * dt_bytes(p.y_dt));
 }
 

@@ -139,7 +139,11 @@ bool ffn_shape_ok(moe_dtype wdt, int32_t H, int32_t I);
 // Rows per tile for a call: streaming (16) or tiled; I_shared = 0 when there is none.
 int32_t ffn_tile_m(moe_dtype wdt, int32_t rows, int32_t groups, int32_t H, int32_t I_routed,
                    int32_t I_shared);
-size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_max);
+size_t ffn_scratch_bytes(moe_dtype wdt, int32_t rows_total, int32_t H, int32_t I_routed,
+                         int32_t I_shared);
+// Whether a bf16 / fp32 layer takes the plain dot-product kernels (H or an I not a
+// multiple of 64; I_shared 0 without a shared expert).
+bool ffn_generic(moe_dtype wdt, int32_t H, int32_t I_routed, int32_t I_shared);
 // Rows per tile of the streaming kernels (the tile_m that selects them).
 int32_t ffn_stream_tile_rows();
 // Runs gate/up + SwiGLU and down for all tiles. `scratch` holds h (and fp8 staging).

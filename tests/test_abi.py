@@ -115,8 +115,8 @@ def ws_size(d):
     (dict(E=1024, routed=bank(E=1024), shared=bank(E=1)), moe.MOE_ERR_SHAPE),  # E + shared > 1024
     (dict(routed=bank(E=7)), moe.MOE_ERR_SHAPE),                               # bank E != E
     (dict(routed=bank(H=128)), moe.MOE_ERR_SHAPE),                             # bank H != H
-    (dict(H=200, routed=bank(H=200)), moe.MOE_ERR_SHAPE),                      # H % 64
-    (dict(routed=bank(I=100)), moe.MOE_ERR_SHAPE),                             # I % 64
+    (dict(H=204, routed=bank(H=204)), moe.MOE_ERR_SHAPE),                      # H % 8
+    (dict(routed=bank(I=100)), moe.MOE_ERR_SHAPE),                             # I % 8
     (dict(act=moe.MOE_F32), moe.MOE_ERR_DTYPE),                                # f32 act, bf16 weights
     (dict(out=moe.MOE_FP8_E4M3), moe.MOE_ERR_DTYPE),
     (dict(shared=bank("f32", E=1)), moe.MOE_ERR_DTYPE),                        # shared dtype differs
@@ -135,6 +135,17 @@ def test_layer_validation(kw, status):
     assert st == status
     assert moe.lib().moe_layer_forward(ctypes.byref(d), P, P, None, None, None, None, P, 1 << 40,
                                        None) == status
+
+
+@pytest.mark.parametrize("kw", [dict(H=200, routed=bank(H=200)),              # H % 8, not % 64
+                                dict(routed=bank(I=136), shared=bank(E=1, I=72)),
+                                dict(H=136, act=moe.MOE_F32, out=moe.MOE_F32,
+                                     routed=bank("f32", H=136, I=200))])
+def test_layer_accepts_multiples_of_8(kw):
+    """bf16 and fp32 layers whose H or I is a multiple of 8 but not of 64 are accepted (they
+    run on the plain dot-product kernels), and their workspace holds h in fp32."""
+    st, n = ws_size(desc(**kw))
+    assert st == moe.MOE_OK and n > 0
 
 
 def test_layer_workspace_and_call_errors():

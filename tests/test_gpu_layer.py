@@ -51,6 +51,11 @@ SMALL = [
               use_bias=True, scale=2.5, shared_I=512, seed=22, weight_seed=22),
     MoEConfig("bf16_stream_lds_f32out", T=6, H=192, E=5, k=2, I=512, score="softmax",
               out="f32", seed=23, weight_seed=23),
+    # H or I a multiple of 8 but not of 64: the plain dot-product kernels (h kept in fp32)
+    MoEConfig("bf16_h200_i136_shared72", T=90, H=200, E=12, k=4, I=136, score="sigmoid",
+              use_bias=True, scale=2.5, shared_I=72, seed=24, weight_seed=24),
+    MoEConfig("f32_h136_i200", T=50, H=136, E=6, k=2, I=200, score="softmax", act="f32",
+              wdt="f32", out="f32", seed=25, weight_seed=25),
     # a group of more tiles than one tile block (the shared expert's 2100 rows: nine tiles)
     MoEConfig("bf16_tile_blocks", T=2100, H=512, E=3, k=1, I=128, score="sigmoid",
               use_bias=True, scale=2.5, shared_I=128, out="f32", seed=21, weight_seed=21),
