@@ -55,6 +55,11 @@ def parse():
                     help="tokens of the batch the CPU oracle leg computes (about 10 s of CPU work)")
     ap.add_argument("--no-measured-peaks", dest="measured_peaks", action="store_false",
                     help="skip the streaming-read and MFMA-loop probes of the device's rates")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="pre-routed workloads (weights under 1 GB, not many times the 256 MB "
+                         "Infinity Cache): before each timed step write this many MiB of "
+                         "device memory, outside the timing, so that no weights stay cached "
+                         "from the step before; 0 times the steps back to back")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (a known-size "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -312,21 +317,45 @@ def run_workload(cfg, dev, args, overlap=False):
     torch.cuda.synchronize()
     log(f"{cfg.name}: warmup done ({args.warmup} steps)")
 
-    # timed region: K plain steps
+    # the routed workloads' weights (17-23 GB) are far beyond the 256 MB Infinity Cache; a
+    # pre-routed share's (0.7 GB) is not, so each of its steps starts after a large write
+    flush = None
+    if not cfg.routed and args.flush_mib > 0:
+        flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
+
+    def evict():
+        if flush is not None:
+            flush.fill_(1)
+            torch.cuda.synchronize()
+
+    # timed region: K plain steps (back to back, or each after the flush, outside its events)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    log(f"{cfg.name}: timed {args.steps} steps: {ms:.4f} ms/step")
+    if flush is None:
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / args.steps
+    else:
+        tot = 0.0
+        for _ in range(args.steps):
+            evict()
+            start.record(stream)
+            step()
+            stop.record(stream)
+            torch.cuda.synchronize()
+            tot += start.elapsed_time(stop)
+        ms = tot / args.steps
+    log(f"{cfg.name}: timed {args.steps} steps: {ms:.4f} ms/step"
+        + (f" (each after a {args.flush_mib} MiB cache flush)" if flush is not None else ""))
 
     # per-stage times of the same launches, from events the library records on its stream
     stage = {s_: [] for s_ in moe.STAGES}
     per_step = []
     for _ in range(args.steps):
+        evict()
         timed_step()
         torch.cuda.synchronize()
         st = ev.elapsed_ms()
@@ -366,6 +395,7 @@ def run_workload(cfg, dev, args, overlap=False):
     ffn_flops = acct["gate_up"]["flops"] + acct["down"]["flops"]
     return {
         "ms": ms, "stage_ms": stage_ms, "touched": touched, "counts": counts,
+        "cache_flush_mib": args.flush_mib if flush is not None else 0,
         "step_ms_p10_p50_p90": [percentile(per_step, q) for q in (10, 50, 90)],
         "ovl_ms": ovl_ms,
         "layer_bytes": layer_bytes, "layer_flops": layer_flops,
@@ -517,6 +547,7 @@ def main():
                    "tokens": T, "experts_touched": r["touched"],
                    "stage_ms": {s_: round(v, 5) for s_, v in r["stage_ms"].items()},
                    "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
+                   "cache_flush_mib_before_each_step": r["cache_flush_mib"],
                    "layer_algorithmic_bytes": r["layer_bytes"], "layer_flops": r["layer_flops"],
                    "layer_hbm_frac": r["layer_bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                    "down_frac": r["down_frac"],
