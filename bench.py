@@ -139,8 +139,9 @@ def ffn_accounting(cfg, touched):
     """Algorithmic HBM bytes and flops of the grouped gate/up (+SwiGLU) and down launches:
     every touched expert's weights read once, every routed/shared row's input read once and
     its output written once; which of HBM or MFMA bounds each launch; the kernel the library
-    picks for it (fp8: k_fp8; bf16 and MXFP4 with more than 32 routed rows per expert on
-    average: k_tiled2; otherwise the streaming kernels)."""
+    picks for it (fp8: k_fp8; bf16 and fp32 with H or I not a multiple of 64: the plain
+    dot-product kernels; bf16 and MXFP4 with more than 32 routed rows per expert on average:
+    k_tiled2; otherwise the streaming kernels)."""
     T, H, I, Is, k = cfg.T, cfg.H, cfg.I, cfg.shared_I, cfg.k
     rows_r = T * k if cfg.routed else T
     rows = rows_r + (T if Is else 0)
@@ -165,6 +166,8 @@ def ffn_accounting(cfg, touched):
         kgu, kdn = "k_tiled2<gate/up, MXFP4>", "k_tiled2<down, MXFP4>"
     elif cfg.wdt == "mxfp4a4":
         kgu, kdn = "k_w4a4<gate/up>", "k_w4a4<down>"
+    elif cfg.wdt in ("bf16", "f32") and (H % 64 or I % 64 or Is % 64):
+        kgu, kdn = "k_gateup_generic", "k_down_generic"
     elif cfg.wdt == "bf16" and rows_r > 32 * cfg.E:
         kgu, kdn = "k_tiled2<gate/up>", "k_tiled2<down>"
     else:
