@@ -40,6 +40,13 @@ namespace {
 #ifndef MOE_F8_WIDE_DN  // down over 256 features a workgroup where H allows
 #define MOE_F8_WIDE_DN 1
 #endif
+#ifndef MOE_F8_XCD_CHUNKS  // wide down: work items dealt to the XCDs in contiguous chunks
+#define MOE_F8_XCD_CHUNKS 1
+#endif
+constexpr int kF8Xcds = 8;  // MI355X: 8 XCDs, workgroups dealt to them round-robin
+// the launches whose items go to the XCDs in chunks (k_fp8's wide down)
+template <bool kGateUp, bool kWide>
+constexpr bool kChunkedOrder() { return MOE_F8_XCD_CHUNKS && !kGateUp && kWide; }
 #ifndef MOE_F8_DEFER  // sub-tiles whose scaling two-block launches defer to the next K block
 #define MOE_F8_DEFER 6
 #endif
@@ -166,10 +173,31 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   __shared__ __attribute__((aligned(1024))) char ring[S * STG];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int m16 = l & 15, g = l >> 4;
-  const int tile_id = blockIdx.x / fb_per_tile;
-  const int fb = blockIdx.x - tile_id * fb_per_tile;
-  if (tile_id >= *a.ntiles) return;
-  const Tile tl = a.tiles[tile_id];
+  // Wide down: work items (tile, feature block) dealt to the 8 XCDs in contiguous chunks
+  // (workgroup b runs on XCD b mod 8), inside a chunk the row tiles of one tile block side
+  // by side per feature block (the order of the LDS-tiled kernel): r1_decode_fp8 down
+  // 0.347-0.349 -> 0.339-0.341 ms and r1_decode_int8 0.345 -> 0.339 ms on two boxes,
+  // e384_fp8 within 1% either way. The same order made gate/up slower
+  // (e384_fp8 2.360 -> 2.395 ms, r1_prefill_int8 3.89 -> 4.29 ms) and the one-block down
+  // of the prefill-sized INT8 layer too (2.01 -> 2.12 ms), which keep tile-major order.
+  int fb;
+  Tile tl;
+  if constexpr (kChunkedOrder<kGateUp, kWide>()) {
+    const int nitems = *a.ntiles * fb_per_tile;
+    const int chunk = (nitems + kF8Xcds - 1) / kF8Xcds;
+    const int slot = blockIdx.x / kF8Xcds;
+    const int item = (blockIdx.x % kF8Xcds) * chunk + slot;
+    if (slot >= chunk || item >= nitems) return;
+    const Tile tb = a.tiles[item / fb_per_tile];
+    const int o = item - tb.blk0 * fb_per_tile;
+    fb = o / tb.nblk;
+    tl = a.tiles[tb.blk0 + (o - fb * tb.nblk)];
+  } else {
+    const int tile_id = blockIdx.x / fb_per_tile;
+    fb = blockIdx.x - tile_id * fb_per_tile;
+    if (tile_id >= *a.ntiles) return;
+    tl = a.tiles[tile_id];
+  }
   const int bank = tl.group < a.E ? 0 : 1;
   const int64_t ge = tl.group < a.E ? tl.group : 0;
   const int I = a.bank[bank].I;
@@ -427,20 +455,27 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
 }  // namespace
 
 namespace {
+// workgroups for the items of max_tiles tiles: whole rounds of the XCD count when items
+// are dealt to XCDs in chunks, so that every chunk's last item has a workgroup
+inline int q8_grid(int max_tiles, int fb_per_tile, bool chunked) {
+  const int n = max_tiles * fb_per_tile;
+  return chunked ? (n + kF8Xcds - 1) / kF8Xcds * kF8Xcds : n;
+}
+
 template <bool kI8, bool kWide>
 hipError_t launch_q8_down(const FfnArgs& a, hipStream_t s) {
   const int nb_dn = a.H / (kWide ? 2 * kF8Feat : kF8Feat);
   if (a.y_dt == MOE_F32)
-    hipLaunchKernelGGL((k_fp8<false, true, kI8, kWide>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_fp8<false, true, kI8, kWide>), dim3(q8_grid(a.max_tiles, nb_dn, kChunkedOrder<false, kWide>())), dim3(512), 0, s, a, nb_dn);
   else
-    hipLaunchKernelGGL((k_fp8<false, false, kI8, kWide>), dim3(a.max_tiles * nb_dn), dim3(512), 0, s, a, nb_dn);
+    hipLaunchKernelGGL((k_fp8<false, false, kI8, kWide>), dim3(q8_grid(a.max_tiles, nb_dn, kChunkedOrder<false, kWide>())), dim3(512), 0, s, a, nb_dn);
   return hipGetLastError();
 }
 
 template <bool kI8>
 hipError_t launch_q8(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
   const int nb_gu = a.I_max / kF8Feat;
-  hipLaunchKernelGGL((k_fp8<true, true, kI8, false>), dim3(a.max_tiles * nb_gu), dim3(512), 0, s, a, nb_gu);
+  hipLaunchKernelGGL((k_fp8<true, true, kI8, false>), dim3(q8_grid(a.max_tiles, nb_gu, kChunkedOrder<true, false>())), dim3(512), 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = hipEventRecord(mid_event, s)) != hipSuccess) return err;
