@@ -131,6 +131,31 @@ __device__ __forceinline__ uint16_t split_bf16(float h, float* lo) {
   return b;
 }
 
+// The work item (tile, feature block) of this workgroup when a launch's items are dealt to
+// the 8 XCDs in contiguous chunks (workgroup b runs on XCD b mod 8): chunk x goes to XCD
+// x, and inside a chunk the tiles of one tile block run side by side per feature block,
+// so that the items sharing a tile's rows (or a group's weights) meet in one L2. The grid
+// must be a whole number of rounds of 8 covering ntiles * fb_per_tile items (xcd_grid).
+// Returns false for a workgroup without an item.
+constexpr int kXcdCount = 8;  // MI355X
+__device__ __forceinline__ bool xcd_chunked_item(const FfnArgs& a, int fb_per_tile, int* fb,
+                                                 Tile* tl) {
+  const int nitems = *a.ntiles * fb_per_tile;
+  const int chunk = (nitems + kXcdCount - 1) / kXcdCount;
+  const int slot = blockIdx.x / kXcdCount;
+  const int item = (blockIdx.x % kXcdCount) * chunk + slot;
+  if (slot >= chunk || item >= nitems) return false;
+  const Tile tb = a.tiles[item / fb_per_tile];
+  const int o = item - tb.blk0 * fb_per_tile;
+  *fb = o / tb.nblk;
+  *tl = a.tiles[tb.blk0 + (o - *fb * tb.nblk)];
+  return true;
+}
+// Workgroups for max_tiles * fb_per_tile items, in whole rounds of the XCD count.
+inline int xcd_grid(int max_tiles, int fb_per_tile) {
+  return (max_tiles * fb_per_tile + kXcdCount - 1) / kXcdCount * kXcdCount;
+}
+
 // A compile-time int as a value, so that a generic lambda can be instantiated per count.
 template <int N>
 struct IntC {
