@@ -43,7 +43,6 @@ namespace {
 #ifndef MOE_F8_XCD_CHUNKS  // wide down: work items dealt to the XCDs in contiguous chunks
 #define MOE_F8_XCD_CHUNKS 1
 #endif
-constexpr int kF8Xcds = 8;  // MI355X: 8 XCDs, workgroups dealt to them round-robin
 // the launches whose items go to the XCDs in chunks (k_fp8's wide down)
 template <bool kGateUp, bool kWide>
 constexpr bool kChunkedOrder() { return MOE_F8_XCD_CHUNKS && !kGateUp && kWide; }
@@ -183,15 +182,7 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
   int fb;
   Tile tl;
   if constexpr (kChunkedOrder<kGateUp, kWide>()) {
-    const int nitems = *a.ntiles * fb_per_tile;
-    const int chunk = (nitems + kF8Xcds - 1) / kF8Xcds;
-    const int slot = blockIdx.x / kF8Xcds;
-    const int item = (blockIdx.x % kF8Xcds) * chunk + slot;
-    if (slot >= chunk || item >= nitems) return;
-    const Tile tb = a.tiles[item / fb_per_tile];
-    const int o = item - tb.blk0 * fb_per_tile;
-    fb = o / tb.nblk;
-    tl = a.tiles[tb.blk0 + (o - fb * tb.nblk)];
+    if (!xcd_chunked_item(a, fb_per_tile, &fb, &tl)) return;
   } else {
     const int tile_id = blockIdx.x / fb_per_tile;
     fb = blockIdx.x - tile_id * fb_per_tile;
@@ -455,11 +446,10 @@ __global__ void __launch_bounds__(512, 2) k_fp8(FfnArgs a, int fb_per_tile) {
 }  // namespace
 
 namespace {
-// workgroups for the items of max_tiles tiles: whole rounds of the XCD count when items
-// are dealt to XCDs in chunks, so that every chunk's last item has a workgroup
+// workgroups for the items of max_tiles tiles (whole rounds of the XCD count when the
+// items are dealt to the XCDs in chunks)
 inline int q8_grid(int max_tiles, int fb_per_tile, bool chunked) {
-  const int n = max_tiles * fb_per_tile;
-  return chunked ? (n + kF8Xcds - 1) / kF8Xcds * kF8Xcds : n;
+  return chunked ? xcd_grid(max_tiles, fb_per_tile) : max_tiles * fb_per_tile;
 }
 
 template <bool kI8, bool kWide>

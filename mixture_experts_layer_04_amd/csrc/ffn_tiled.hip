@@ -61,7 +61,6 @@ namespace {
 #ifndef MOE_T2_MX_TN
 #define MOE_T2_MX_TN 8
 #endif
-constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt to them round-robin
 #ifndef MOE_T2_WAVES_PER_SIMD
 #define MOE_T2_WAVES_PER_SIMD 2
 #endif
@@ -124,22 +123,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN, waves_per_simd(WGM * WGN)) k_t
   __shared__ __attribute__((aligned(1024))) char smem[S * ASTAGE + SB * BSTAGE];
   // the wavefront index as a uniform (scalar) value: the DMA destinations derive from it
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  // Work items (tile, weight block) are cut into kXcds equal contiguous chunks, chunk x run
-  // by the workgroups that the dispatcher deals to XCD x (blockIdx = x mod kXcds), so that
-  // each XCD's L2 serves the items that share data. Inside a chunk the items of a block
+  // Work items (tile, weight block) are cut into 8 equal contiguous chunks, chunk x run by
+  // the workgroups that the dispatcher deals to XCD x (blockIdx = x mod 8; xcd_chunked_item),
+  // so that each XCD's L2 serves the items that share data. Inside a chunk the items of a block
   // of up to kTileBlock row tiles of one group run weight block by weight block, the
   // block's row tiles side by side: they read the same weight rows at the same time, and
   // the items that read one activation tile are at most kTileBlock apart.
-  const int nitems = *a.ntiles * nb_per_tile;
-  const int chunk = (nitems + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int item = (blockIdx.x % kXcds) * chunk + slot;
-  if (slot >= chunk || item >= nitems) return;
-  const Tile tb = a.tiles[item / nb_per_tile];
-  const int o = item - tb.blk0 * nb_per_tile;
-  const int nb = o / tb.nblk;
-  const int tidx = tb.blk0 + (o - nb * tb.nblk);
-  const Tile tl = a.tiles[tidx];
+  int nb;
+  Tile tl;
+  if (!xcd_chunked_item(a, nb_per_tile, &nb, &tl)) return;
   const int bank = tl.group < a.E ? 0 : 1;
   const int64_t ge = tl.group < a.E ? tl.group : 0;
   const int I = a.bank[bank].I;
@@ -412,9 +404,8 @@ hipError_t launch_tiled_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid_eve
   constexpr int BN = WGN * 16 * TN;
   static_assert(WGND * 16 * TND == BN, "both launches take the same weight block");
   const int nb_gu = a.I_max / (BN / 2), nb_dn = a.H / BN;
-  // whole rounds of kXcds workgroups, so that every chunk's last item has a workgroup
-  const dim3 gu((a.max_tiles * nb_gu + kXcds - 1) / kXcds * kXcds),
-      dn((a.max_tiles * nb_dn + kXcds - 1) / kXcds * kXcds), blk(64 * WGM * WGN),
+  // whole rounds of 8 workgroups, so that every chunk's last item has a workgroup
+  const dim3 gu(xcd_grid(a.max_tiles, nb_gu)), dn(xcd_grid(a.max_tiles, nb_dn)), blk(64 * WGM * WGN),
       blkd(64 * WGM * WGND);
   hipLaunchKernelGGL((k_tiled2<TM, TN, WGM, WGN, S, SB, true, false, kMX>), gu, blk, 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
