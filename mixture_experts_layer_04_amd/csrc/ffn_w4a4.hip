@@ -32,7 +32,6 @@ namespace {
 #ifndef MOE_A4_WGN  // 4: 128 x 256 tiles where the shapes allow; 2: always 128 x 128
 #define MOE_A4_WGN 4
 #endif
-constexpr int kA4Xcds = 8;
 
 // One thread per 32-element block of a bf16 row: codes [n, H/2] bytes, scales [n, H/32].
 __global__ void __launch_bounds__(256) k_quant_rows_mxfp4(const uint16_t* __restrict__ x, int n,
@@ -83,15 +82,9 @@ __global__ void __launch_bounds__(128 * WGN, 2) k_w4a4(FfnArgs a, int nb_per_til
   static_assert(S >= 2 && (S - 2) * OPS < 64, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[S * STG];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  const int nitems = *a.ntiles * nb_per_tile;
-  const int chunk = (nitems + kA4Xcds - 1) / kA4Xcds;
-  const int slot = blockIdx.x / kA4Xcds;
-  const int item = (blockIdx.x % kA4Xcds) * chunk + slot;
-  if (slot >= chunk || item >= nitems) return;
-  const Tile tb = a.tiles[item / nb_per_tile];
-  const int o = item - tb.blk0 * nb_per_tile;
-  const int nb = o / tb.nblk;
-  const Tile tl = a.tiles[tb.blk0 + (o - nb * tb.nblk)];
+  int nb;
+  Tile tl;
+  if (!xcd_chunked_item(a, nb_per_tile, &nb, &tl)) return;
   const int bank = tl.group < a.E ? 0 : 1;
   const int64_t ge = tl.group < a.E ? tl.group : 0;
   const int I = a.bank[bank].I;
@@ -251,8 +244,7 @@ __global__ void __launch_bounds__(128 * WGN, 2) k_w4a4(FfnArgs a, int nb_per_til
 template <int WGN>
 hipError_t launch_w4a4_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid_event) {
   const int nb_gu = a.I_max / (32 * WGN), nb_dn = a.H / (64 * WGN);
-  const dim3 gu((a.max_tiles * nb_gu + kA4Xcds - 1) / kA4Xcds * kA4Xcds),
-      dn((a.max_tiles * nb_dn + kA4Xcds - 1) / kA4Xcds * kA4Xcds), blk(128 * WGN);
+  const dim3 gu(xcd_grid(a.max_tiles, nb_gu)), dn(xcd_grid(a.max_tiles, nb_dn)), blk(128 * WGN);
   hipLaunchKernelGGL((k_w4a4<WGN, true, false>), gu, blk, 0, s, a, nb_gu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
